@@ -1,0 +1,141 @@
+"""Pins for the oracle's dense float64 attention (CPU only).
+
+The oracle is checked against things other than itself: a pure-Python loop
+with math.exp on tiny inputs, scipy's softmax/logsumexp, and closed forms
+(K = 0 gives the mean of V; constant V; a single key; a dominant key).
+"""
+import math
+
+import numpy as np
+import pytest
+from scipy.special import logsumexp, softmax
+
+from memory_bounded_streaming_amd.inputs import gen_qkv, round_to_bf16_bits
+from oracle.attention import attention_fp64, to_f64
+
+
+def _loop_attention(q, k, v, scale):
+    """Softmax attention written element by element (no numpy linear algebra)."""
+    n, h_count, d = q.shape
+    out = [[[0.0] * d for _ in range(h_count)] for _ in range(n)]
+    lse = [[0.0] * n for _ in range(h_count)]
+    for h in range(h_count):
+        for i in range(n):
+            s = []
+            for j in range(n):
+                acc = 0.0
+                for t in range(d):
+                    acc += float(q[i, h, t]) * float(k[j, h, t])
+                s.append(acc * scale)
+            mx = max(s)
+            w = [math.exp(x - mx) for x in s]
+            tot = sum(w)
+            for t in range(d):
+                out[i][h][t] = sum(w[j] * float(v[j, h, t]) for j in range(n)) / tot
+            lse[h][i] = mx + math.log(tot)
+    return np.array(out), np.array(lse)
+
+
+def test_matches_python_loop_on_tiny_input():
+    rng = np.random.default_rng(3)
+    q, k, v = (rng.standard_normal((5, 2, 3)).astype(np.float32) for _ in range(3))
+    o, lse = attention_fp64(q, k, v, dtype="f32", scale=0.7)
+    o_ref, lse_ref = _loop_attention(q, k, v, 0.7)
+    np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse, lse_ref, rtol=0, atol=1e-13)
+
+
+def test_matches_scipy_softmax_and_logsumexp():
+    rng = np.random.default_rng(4)
+    n, h_count, d = 50, 3, 16
+    q, k, v = (rng.standard_normal((n, h_count, d)).astype(np.float32) for _ in range(3))
+    rows = np.array([0, 7, 49])
+    o, lse = attention_fp64(q, k, v, rows=rows, dtype="f32", key_block=7, row_block=2)
+    for h in range(h_count):
+        s = q[rows, h, :].astype(np.float64) @ k[:, h, :].astype(np.float64).T / math.sqrt(d)
+        np.testing.assert_allclose(o[:, h, :], softmax(s, axis=1) @ v[:, h, :].astype(np.float64),
+                                   rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(lse[h], logsumexp(s, axis=1), rtol=1e-13)
+
+
+def test_zero_keys_give_mean_of_values():
+    rng = np.random.default_rng(5)
+    n, d = 37, 8
+    q = rng.standard_normal((n, 2, d)).astype(np.float32)
+    k = np.zeros((n, 2, d), np.float32)
+    v = rng.standard_normal((n, 2, d)).astype(np.float32)
+    o, lse = attention_fp64(q, k, v, dtype="f32")
+    mean = v.astype(np.float64).mean(axis=0)
+    np.testing.assert_allclose(o, np.broadcast_to(mean, o.shape), rtol=0, atol=1e-15)
+    np.testing.assert_allclose(lse, math.log(n), rtol=1e-15)
+
+
+def test_constant_values_give_constant_output():
+    rng = np.random.default_rng(6)
+    q, k = (rng.standard_normal((20, 1, 4)).astype(np.float32) for _ in range(2))
+    v = np.full((20, 1, 4), 1.25, np.float32)
+    o, _ = attention_fp64(q, k, v, dtype="f32")
+    np.testing.assert_allclose(o, 1.25, rtol=0, atol=1e-15)
+
+
+def test_single_token():
+    q = np.array([[[0.5, -1.0]]], np.float32)
+    k = np.array([[[2.0, 1.0]]], np.float32)
+    v = np.array([[[3.0, -4.0]]], np.float32)
+    o, lse = attention_fp64(q, k, v, dtype="f32")
+    np.testing.assert_array_equal(o, v.astype(np.float64))
+    assert lse[0, 0] == pytest.approx((0.5 * 2.0 - 1.0 * 1.0) / math.sqrt(2.0))
+
+
+def test_dominant_key_and_large_scores_do_not_overflow():
+    n, d = 16, 4
+    q = np.zeros((n, 1, d), np.float32)
+    q[:, 0, 0] = 3000.0
+    k = np.zeros((n, 1, d), np.float32)
+    k[9, 0, 0] = 1.0
+    v = np.arange(n * d, dtype=np.float32).reshape(n, 1, d)
+    o, lse = attention_fp64(q, k, v, dtype="f32")
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    np.testing.assert_allclose(o[:, 0, :], np.broadcast_to(v[9, 0, :], (n, d)), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, 3000.0 / 2.0, rtol=1e-15)
+
+
+def test_asymmetric_roles_of_q_and_k():
+    # swapping Q and K (a transposed score matrix) must change the answer
+    rng = np.random.default_rng(8)
+    q, k, v = (rng.standard_normal((6, 1, 3)).astype(np.float32) for _ in range(3))
+    o, _ = attention_fp64(q, k, v, dtype="f32")
+    o_swapped, _ = attention_fp64(k, q, v, dtype="f32")
+    o_ref, _ = _loop_attention(q, k, v, 1 / math.sqrt(3))
+    np.testing.assert_allclose(o, o_ref, atol=1e-14)
+    assert np.abs(o_swapped - o_ref).max() > 1e-3
+
+
+def test_bf16_inputs_are_widened_exactly():
+    bits = np.array([0x3F80, 0xC000, 0x3F81, 0x0000, 0x8000, 0x7F7F], np.uint16)
+    want = [1.0, -2.0, 1.0078125, 0.0, -0.0, 3.3895313892515355e38]
+    np.testing.assert_array_equal(to_f64(bits, "bf16"), want)
+    q, k, v = gen_qkv(11, 40, 2, 8, dtype="bf16")
+    o_bits, _ = attention_fp64(q, k, v, dtype="bf16")
+    o_f32, _ = attention_fp64(to_f64(q, "bf16").astype(np.float32), to_f64(k, "bf16").astype(np.float32),
+                              to_f64(v, "bf16").astype(np.float32), dtype="f32")
+    np.testing.assert_array_equal(o_bits, o_f32)
+
+
+def test_blocking_does_not_change_the_result():
+    q, k, v = gen_qkv(12, 300, 2, 16, dtype="f32")
+    o1, l1 = attention_fp64(q, k, v, dtype="f32", key_block=300, row_block=300)
+    o2, l2 = attention_fp64(q, k, v, dtype="f32", key_block=17, row_block=11)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(l1, l2, rtol=1e-15)
+
+
+def test_input_generator_rounding_and_determinism():
+    # ties go to even; the stream does not depend on the block split
+    x = np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -1.0 - 2 ** -9], np.float32)
+    assert list(round_to_bf16_bits(x)) == [0x3F80, 0x3F82, 0xBF80]
+    a = gen_qkv(0, 70000, 1, 4, dtype="bf16")
+    b = gen_qkv(0, 70000, 1, 4, dtype="bf16")
+    for x1, x2 in zip(a, b):
+        np.testing.assert_array_equal(x1, x2)
+    assert not np.array_equal(a[0], a[1])
