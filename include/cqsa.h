@@ -1,0 +1,225 @@
+/*
+ * cqsa.h -- C ABI of the Stream-CQSA forward library (libcqsa.so, MI355X / gfx950).
+ *
+ * The method (sources are the pages describing it):
+ *   - "Stream-CQSA: Exact Out-of-Memory Recovery for Attention" (arXiv 2604.20819),
+ *     abstract: an infeasible attention call is partitioned recursively into
+ *     independent subsequence tasks; each runs an inner attention kernel and the
+ *     local statistics are recomposed into the exact full output.
+ *   - "Stream-CQSA: Breaking the Billion-Token Barrier on a Single GPU" (wispaper
+ *     explainer), section "The 'CQS Divide': Attention as a Steiner System":
+ *     N tokens -> c = l(l-1)+1 chunks -> c subsequences of l chunks, every chunk
+ *     pair exactly once; section "The Recursive Benefit": divide again until a
+ *     task fits the memory budget; section "Implementation: From High-Level Logic
+ *     to GPU Kernels": CQS Mask, stream Q_i/K_i/V_i to the GPU, local numerators
+ *     and denominators, aggregation in host memory.
+ *   - Lattice summary of arXiv:2604.20819: subproblems that fit arbitrary memory
+ *     budgets; recomposition equals full-sequence attention.
+ *
+ * Conventions for every call
+ *   - Tensors are token-major [N, H, d] (batch 1), row stride H*d elements.
+ *     dtype CQSA_BF16 = bfloat16 (2 bytes), CQSA_F32 = float32.
+ *   - Attention is non-causal over all N keys with softmax scale 1/sqrt(d).
+ *   - Every call returns a cqsa_status; 0 is success.  On failure nothing is
+ *     guaranteed about outputs, and cqsa_last_error() returns a thread-local
+ *     message.  No C++ exception crosses this boundary.
+ *   - "stream" is a hipStream_t passed as void* (NULL = the null stream).
+ *   - Device pointers must be on the current HIP device.
+ */
+#ifndef CQSA_H
+#define CQSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CQSA_OK = 0,
+  CQSA_EINVAL = -1,   /* bad argument (null pointer, size, unsupported d/dtype/flag) */
+  CQSA_ENOSET = -2,   /* no perfect difference set for this l (l = 7) */
+  CQSA_EDIVIDE = -3,  /* N is not a multiple of prod(c_k) over the levels */
+  CQSA_EBUDGET = -4,  /* no staging mode fits the memory budget */
+  CQSA_EHIP = -5,     /* a HIP runtime call failed */
+  CQSA_ENOMEM = -6,   /* a host or device allocation failed */
+  CQSA_ESMALL = -7    /* a caller buffer or workspace is smaller than required */
+} cqsa_status;
+
+typedef enum { CQSA_BF16 = 0, CQSA_F32 = 1 } cqsa_dtype;
+
+/* Where q, k, v, o and lse live for cqsa_forward. */
+typedef enum { CQSA_RES_DEVICE = 0, CQSA_RES_HOST_PINNED = 1 } cqsa_residency;
+
+/* Staging mode of the host-pinned path, chosen by the footprint model. */
+typedef enum {
+  CQSA_MODE_DEVICE_ACC_KV2 = 1, /* K/V of two tasks staged (double buffer), accumulator on device */
+  CQSA_MODE_HOST_ACC_KV2 = 2,   /* K/V double buffer, accumulator in pinned host memory */
+  CQSA_MODE_DEVICE_ACC_KV1 = 3, /* one task's K/V resident at a time, accumulator on device */
+  CQSA_MODE_HOST_ACC_KV1 = 4    /* one task's K/V resident at a time, accumulator on host */
+} cqsa_mode;
+
+/* plan_create flags (all optional; 0 = let the footprint model choose). */
+#define CQSA_FLAG_HOST_ACC 0x1u  /* only consider modes with the accumulator on the host */
+#define CQSA_FLAG_KV_SINGLE 0x2u /* only consider single-buffered K/V staging */
+
+#define CQSA_MAX_LEVELS 8
+#define CQSA_MAX_L 10
+
+typedef struct cqsa_plan cqsa_plan; /* opaque; immutable once created */
+
+typedef struct {
+  int64_t n_tokens;
+  int32_t heads, head_dim, dtype;
+  int32_t levels;               /* itr: number of CQS Divide levels */
+  int32_t c[CQSA_MAX_LEVELS];   /* chunks per level, c = l(l-1)+1 */
+  int32_t l[CQSA_MAX_LEVELS];   /* chunks per subsequence per level */
+  int64_t n_tasks;              /* prod(c_k) innermost tasks */
+  int64_t unit_tokens;          /* N / prod(c_k): the ownership grid */
+  int64_t n_units;              /* prod(c_k) */
+  int64_t visits;               /* prod(l_k): tasks that visit each query row */
+  int64_t task_tokens;          /* tokens per innermost task */
+  int64_t budget_bytes;         /* 0 = unlimited */
+  int32_t stream_mode;          /* cqsa_mode chosen for CQSA_RES_HOST_PINNED */
+  int32_t kv_buffers;           /* 1 or 2 */
+  int64_t stream_workspace_bytes; /* device bytes the host-pinned path needs (<= budget) */
+  int64_t device_workspace_bytes; /* device bytes the device-resident path needs */
+  int64_t host_acc_bytes;       /* pinned host accumulator the host-pinned path allocates (0 if on device) */
+  double useful_flop;           /* 4 * N^2 * d * H */
+} cqsa_plan_info;
+
+typedef struct {
+  double t_total_ms;            /* wall time of the call (host clock) */
+  double t_h2d_ms, t_attn_ms, t_merge_ms, t_d2h_ms; /* summed event-timed durations per phase */
+  int64_t bytes_h2d, bytes_d2h;
+  int64_t peak_device_bytes;    /* workspace bytes used by the call */
+  int64_t n_attn_launches, n_merge_launches, n_h2d_copies, n_d2h_copies;
+  double useful_flop;
+} cqsa_stats;
+
+/* Library version string. */
+const char* cqsa_version(void);
+
+/*
+ * Perfect difference set of size l (the cyclic quorum behind CQS Divide; "Stream-CQSA:
+ * Exact Out-of-Memory Recovery for Attention", abstract: "derived from the theory of
+ * cyclic quorum sets").  Writes the lexicographically smallest sorted set D of l
+ * residues mod c = l(l-1)+1 with {0,1} in D whose nonzero differences cover 1..c-1
+ * exactly once (l = 1 gives {0}).  out: host array of >= l int32 (cap = its length).
+ * Errors: EINVAL (l outside 1..CQSA_MAX_L, out NULL, cap < l), ENOSET (l = 7).
+ */
+cqsa_status cqsa_difference_set(int32_t l, int32_t* out, int32_t cap);
+
+/*
+ * Build the CQS plan for an N-token attention ("The 'CQS Divide'" and "The Recursive
+ * Benefit" sections of the wispaper explainer; the Lattice summary's memory budget).
+ *   l_levels[0..n_levels): l per level, outer level first.  n_levels = 0 means
+ *     "auto": repeat l_levels[0] (one value read) until the host-pinned path fits
+ *     budget_bytes (at most CQSA_MAX_LEVELS levels).
+ *   Task t (mixed radix over levels, outer first) holds the chunks
+ *     sorted{(t_k + d) mod c_k : d in D_k} of its parent at each level; inside a task,
+ *     query unit i and key unit j are admitted iff at every level they lie in
+ *     different chunks or both in chunk t_k (the CQS Mask: one owner per pair).
+ *   budget_bytes: device-memory budget of the host-pinned path (0 = unlimited); the
+ *     footprint model picks the first fitting mode in the order of cqsa_mode.
+ *   flags: CQSA_FLAG_* above.
+ * Host-only (no HIP call).  *out receives a plan owned by the caller (free with
+ * cqsa_plan_destroy) or NULL on error.  Errors: EINVAL, ENOSET, EDIVIDE, EBUDGET.
+ * Supported: dtype BF16 with head_dim 64 or 128, dtype F32 with head_dim 64 or 128.
+ */
+cqsa_status cqsa_plan_create(int64_t n, int32_t heads, int32_t head_dim, cqsa_dtype dtype,
+                             const int32_t* l_levels, int32_t n_levels, int64_t budget_bytes,
+                             uint32_t flags, cqsa_plan** out);
+
+/* Copy the plan's summary into *out (host). Errors: EINVAL. */
+cqsa_status cqsa_plan_info_get(const cqsa_plan* plan, cqsa_plan_info* out);
+
+/*
+ * Canonical schedule record (int64, host).  Layout:
+ *   n_levels, (c_k, l_k) per level, n_tasks, unit_tokens, n_units, then per task in
+ *   ascending id: tid, t_1..t_L, n_segments, (global_start, length, local_offset) per
+ *   segment in tokens, n_query_units, and per local query unit: global_unit, n_runs,
+ *   (key_local_unit_start, key_unit_count) per run.
+ * Size query: cap = 0 (buf may be NULL) sets *needed.  Errors: EINVAL, ESMALL.
+ */
+cqsa_status cqsa_plan_schedule(const cqsa_plan* plan, int64_t* buf, int64_t cap, int64_t* needed);
+
+/*
+ * Coverage table: int32 [U][U], entry [p][q] = id of the task that owns the pair
+ * (query unit p, key unit q).  Each pair has exactly one owner (the Steiner system
+ * S(2,l,c) of the "CQS Divide" section).  Size query with cap = 0.  Errors: EINVAL, ESMALL.
+ */
+cqsa_status cqsa_plan_coverage(const cqsa_plan* plan, int32_t* table, int64_t cap, int64_t* needed);
+
+/* Free a plan and any device descriptor tables it cached.  NULL is ignored. */
+void cqsa_plan_destroy(cqsa_plan* plan);
+
+/*
+ * Device workspace the call needs for residency res (bytes).  Pass a buffer of at
+ * least this size to cqsa_forward to keep the call free of device allocation.
+ */
+cqsa_status cqsa_workspace_size(const cqsa_plan* plan, cqsa_residency res, int64_t* bytes);
+
+/*
+ * Masked attention partials of every task, device-resident ("Implementation" section
+ * of the wispaper explainer: compute the local numerators and denominators; the CQS
+ * Mask selects the keys).  For every task t and every query row i of t:
+ *     s_ij = (1/sqrt(d)) <q_i, k_j> over the keys j that t admits for i,
+ *     m = log2(e) * max_j s_ij,  l = sum_j 2^(log2(e) s_ij - m),
+ *     n = sum_j 2^(log2(e) s_ij - m) v_j            (unnormalised, float32)
+ * q, k, v: device [N, H, d] in the plan's dtype (read only).
+ * n_out: device float32 [V][N][H][d]; ml_out: device float32 [V][N][H][2] holding (m, l);
+ *   V = visits; slot s of row i holds the s-th task (ascending id) that visits row i.
+ * Enqueued on stream; returns before the kernels finish.  The plan uploads its
+ * descriptor table to the device once (kept until cqsa_plan_destroy).
+ * Errors: EINVAL, EHIP, ENOMEM.
+ */
+cqsa_status cqsa_partials(const cqsa_plan* plan, const void* q, const void* k, const void* v,
+                          float* n_out, float* ml_out, void* stream);
+
+/*
+ * Recompose partials into the output ("recomposes the local statistics", abstract of
+ * arXiv 2604.20819).  Folds the V slots of each (row, head) in ascending slot order:
+ *     m = max(m_a, m_b), l = l_a 2^(m_a-m) + l_b 2^(m_b-m), n likewise,
+ * then O = n / l in the plan's dtype (round to nearest even for bf16) and
+ * LSE = ln(2) * (m + log2 l).
+ * n_in, ml_in: device, layout of cqsa_partials.  o: device [N, H, d] dtype.
+ * lse: device float32 [H, N] or NULL.  Enqueued on stream.  Errors: EINVAL, EHIP.
+ */
+cqsa_status cqsa_merge(const cqsa_plan* plan, const float* n_in, const float* ml_in,
+                       void* o, float* lse, void* stream);
+
+/*
+ * Full CQS forward: O = softmax(Q K^T / sqrt(d)) V and LSE, exact up to rounding.
+ *   CQSA_RES_DEVICE: q, k, v, o, lse are device pointers; runs cqsa_partials then
+ *     cqsa_merge on stream using `workspace` (>= cqsa_workspace_size bytes) for the
+ *     partial slots.  Stream-ordered: returns after enqueuing unless the library had
+ *     to allocate the workspace itself (workspace == NULL), or stats != NULL.
+ *   CQSA_RES_HOST_PINNED: q, k, v, o, lse are pinned host pointers (lse may be NULL).
+ *     Tasks run in ascending id; each task's K/V segments are gathered into device
+ *     staging with hipMemcpyAsync on copy streams, double-buffered when the mode says
+ *     so, query units are streamed in blocks, partials are merged into the
+ *     accumulator (device, or pinned host memory with H2D/D2H round trips), and the
+ *     finished O/LSE blocks are copied back.  Device memory used is the workspace
+ *     (<= budget).  Synchronous: returns after all work is complete.
+ * workspace: device buffer or NULL (then the library allocates exactly the size
+ *   needed and frees it before returning).  lse may be NULL.
+ * stats: optional; when given, phases are timed with HIP events.
+ * Errors: EINVAL, ESMALL, EBUDGET (device path over budget), EHIP, ENOMEM.
+ */
+cqsa_status cqsa_forward(const cqsa_plan* plan, const void* q, const void* k, const void* v,
+                         void* o, float* lse, cqsa_residency res, void* workspace,
+                         int64_t workspace_bytes, void* stream, cqsa_stats* stats);
+
+/* Static text for a status code. */
+const char* cqsa_status_string(cqsa_status status);
+
+/* Thread-local detail of the last failure on this thread ("" if none). */
+const char* cqsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CQSA_H */

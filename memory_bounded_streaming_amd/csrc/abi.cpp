@@ -1,0 +1,220 @@
+// extern "C" entry points of libcqsa.so (declared and documented in include/cqsa.h).
+// Every call validates its arguments, converts failures into a cqsa_status and keeps a
+// thread-local message; no exception crosses the boundary.
+#include <hip/hip_runtime_api.h>
+
+#include <cstring>
+#include <exception>
+#include <new>
+#include <string>
+
+#include "../../include/cqsa.h"
+#include "engine.hpp"
+#include "plan.hpp"
+
+struct cqsa_plan {
+  cqsa::Plan p;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+cqsa_status fail(cqsa_status s, const std::string& why) {
+  g_last_error = why;
+  return s;
+}
+
+cqsa_status ok() {
+  g_last_error.clear();
+  return CQSA_OK;
+}
+
+template <typename F>
+cqsa_status guarded(F&& f) {
+  try {
+    return f();
+  } catch (const std::bad_alloc&) {
+    return fail(CQSA_ENOMEM, "host allocation failed");
+  } catch (const std::exception& e) {
+    return fail(CQSA_EINVAL, std::string("internal error: ") + e.what());
+  } catch (...) {
+    return fail(CQSA_EINVAL, "internal error");
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* cqsa_version(void) { return "cqsa 0.1.0 (gfx950)"; }
+
+const char* cqsa_status_string(cqsa_status s) {
+  switch (s) {
+    case CQSA_OK: return "CQSA_OK";
+    case CQSA_EINVAL: return "CQSA_EINVAL: invalid argument";
+    case CQSA_ENOSET: return "CQSA_ENOSET: no perfect difference set for this l";
+    case CQSA_EDIVIDE: return "CQSA_EDIVIDE: N does not divide into the unit grid";
+    case CQSA_EBUDGET: return "CQSA_EBUDGET: no staging mode fits the memory budget";
+    case CQSA_EHIP: return "CQSA_EHIP: HIP runtime error";
+    case CQSA_ENOMEM: return "CQSA_ENOMEM: allocation failed";
+    case CQSA_ESMALL: return "CQSA_ESMALL: buffer too small";
+  }
+  return "unknown cqsa_status";
+}
+
+const char* cqsa_last_error(void) { return g_last_error.c_str(); }
+
+cqsa_status cqsa_difference_set(int32_t l, int32_t* out, int32_t cap) {
+  return guarded([&]() -> cqsa_status {
+    if (out == nullptr || cap < l) return fail(CQSA_EINVAL, "out must hold at least l values");
+    std::vector<int> d;
+    std::string why;
+    const cqsa_status s = cqsa::difference_set(l, d, why);
+    if (s != CQSA_OK) return fail(s, why);
+    for (size_t i = 0; i < d.size(); ++i) out[i] = d[i];
+    return ok();
+  });
+}
+
+cqsa_status cqsa_plan_create(int64_t n, int32_t heads, int32_t head_dim, cqsa_dtype dtype, const int32_t* l_levels,
+                             int32_t n_levels, int64_t budget_bytes, uint32_t flags, cqsa_plan** out) {
+  return guarded([&]() -> cqsa_status {
+    if (out == nullptr) return fail(CQSA_EINVAL, "out is NULL");
+    *out = nullptr;
+    auto* plan = new cqsa_plan();
+    std::string why;
+    const cqsa_status s = cqsa::build_plan(n, heads, head_dim, dtype, l_levels, n_levels, budget_bytes, flags,
+                                           plan->p, why);
+    if (s != CQSA_OK) {
+      delete plan;
+      return fail(s, why);
+    }
+    *out = plan;
+    return ok();
+  });
+}
+
+cqsa_status cqsa_plan_info_get(const cqsa_plan* plan, cqsa_plan_info* out) {
+  return guarded([&]() -> cqsa_status {
+    if (plan == nullptr || out == nullptr) return fail(CQSA_EINVAL, "NULL argument");
+    const cqsa::Plan& p = plan->p;
+    std::memset(out, 0, sizeof(*out));
+    out->n_tokens = p.n;
+    out->heads = p.heads;
+    out->head_dim = p.d;
+    out->dtype = p.dtype;
+    out->levels = static_cast<int32_t>(p.ls.size());
+    for (size_t k = 0; k < p.ls.size(); ++k) {
+      out->c[k] = p.cs[k];
+      out->l[k] = p.ls[k];
+    }
+    out->n_tasks = static_cast<int64_t>(p.tasks.size());
+    out->unit_tokens = p.unit;
+    out->n_units = p.n_units;
+    out->visits = p.visits;
+    out->task_tokens = p.task_tokens();
+    out->budget_bytes = p.budget;
+    out->stream_mode = p.stream_fp.acc_on_device ? (p.stream_fp.kv_buffers == 2 ? CQSA_MODE_DEVICE_ACC_KV2 : CQSA_MODE_DEVICE_ACC_KV1)
+                                                 : (p.stream_fp.kv_buffers == 2 ? CQSA_MODE_HOST_ACC_KV2 : CQSA_MODE_HOST_ACC_KV1);
+    out->kv_buffers = p.stream_fp.kv_buffers;
+    out->stream_workspace_bytes = p.stream_fp.bytes;
+    out->device_workspace_bytes = p.device_ws;
+    out->host_acc_bytes = p.host_acc_bytes;
+    out->useful_flop = 4.0 * double(p.n) * double(p.n) * p.d * p.heads;
+    return ok();
+  });
+}
+
+cqsa_status cqsa_plan_schedule(const cqsa_plan* plan, int64_t* buf, int64_t cap, int64_t* needed) {
+  return guarded([&]() -> cqsa_status {
+    if (plan == nullptr || needed == nullptr) return fail(CQSA_EINVAL, "NULL argument");
+    const auto& s = plan->p.schedule;
+    *needed = static_cast<int64_t>(s.size());
+    if (cap == 0) return ok();
+    if (buf == nullptr || cap < *needed) return fail(CQSA_ESMALL, "schedule buffer too small");
+    std::memcpy(buf, s.data(), s.size() * sizeof(int64_t));
+    return ok();
+  });
+}
+
+cqsa_status cqsa_plan_coverage(const cqsa_plan* plan, int32_t* table, int64_t cap, int64_t* needed) {
+  return guarded([&]() -> cqsa_status {
+    if (plan == nullptr || needed == nullptr) return fail(CQSA_EINVAL, "NULL argument");
+    const cqsa::Plan& p = plan->p;
+    const int64_t u = p.n_units;
+    *needed = u * u;
+    if (cap == 0) return ok();
+    if (table == nullptr || cap < *needed) return fail(CQSA_ESMALL, "coverage buffer too small");
+    for (int64_t i = 0; i < u * u; ++i) table[i] = -1;
+    for (const cqsa::Task& t : p.tasks)
+      for (size_t a = 0; a < t.units.size(); ++a)
+        for (const cqsa::UnitRun& r : t.runs[a])
+          for (int32_t b = r.start; b < r.start + r.count; ++b) {
+            int32_t& cell = table[t.units[a] * u + t.units[b]];
+            cell = cell == -1 ? static_cast<int32_t>(t.tid) : -2;  // -2 would mark a doubly owned pair
+          }
+    return ok();
+  });
+}
+
+void cqsa_plan_destroy(cqsa_plan* plan) {
+  if (plan == nullptr) return;
+  try {
+    cqsa::free_device_tables(plan->p);
+  } catch (...) {
+  }
+  delete plan;
+}
+
+cqsa_status cqsa_workspace_size(const cqsa_plan* plan, cqsa_residency res, int64_t* bytes) {
+  return guarded([&]() -> cqsa_status {
+    if (plan == nullptr || bytes == nullptr) return fail(CQSA_EINVAL, "NULL argument");
+    if (res == CQSA_RES_DEVICE)
+      *bytes = plan->p.device_ws;
+    else if (res == CQSA_RES_HOST_PINNED)
+      *bytes = plan->p.stream_fp.bytes;
+    else
+      return fail(CQSA_EINVAL, "unknown residency");
+    return ok();
+  });
+}
+
+cqsa_status cqsa_partials(const cqsa_plan* plan, const void* q, const void* k, const void* v, float* n_out,
+                          float* ml_out, void* stream) {
+  return guarded([&]() -> cqsa_status {
+    if (plan == nullptr || q == nullptr || k == nullptr || v == nullptr || n_out == nullptr || ml_out == nullptr)
+      return fail(CQSA_EINVAL, "NULL argument");
+    std::string why;
+    const cqsa_status s = cqsa::run_partials(plan->p, q, k, v, n_out, ml_out, static_cast<hipStream_t>(stream), why);
+    return s == CQSA_OK ? ok() : fail(s, why);
+  });
+}
+
+cqsa_status cqsa_merge(const cqsa_plan* plan, const float* n_in, const float* ml_in, void* o, float* lse,
+                       void* stream) {
+  return guarded([&]() -> cqsa_status {
+    if (plan == nullptr || n_in == nullptr || ml_in == nullptr || o == nullptr)
+      return fail(CQSA_EINVAL, "NULL argument");
+    std::string why;
+    const cqsa_status s = cqsa::run_merge(plan->p, n_in, ml_in, o, lse, static_cast<hipStream_t>(stream), why);
+    return s == CQSA_OK ? ok() : fail(s, why);
+  });
+}
+
+cqsa_status cqsa_forward(const cqsa_plan* plan, const void* q, const void* k, const void* v, void* o, float* lse,
+                         cqsa_residency res, void* workspace, int64_t workspace_bytes, void* stream,
+                         cqsa_stats* stats) {
+  return guarded([&]() -> cqsa_status {
+    if (plan == nullptr || q == nullptr || k == nullptr || v == nullptr || o == nullptr)
+      return fail(CQSA_EINVAL, "NULL argument");
+    if (res != CQSA_RES_DEVICE && res != CQSA_RES_HOST_PINNED) return fail(CQSA_EINVAL, "unknown residency");
+    if (workspace != nullptr && workspace_bytes <= 0) return fail(CQSA_EINVAL, "workspace size must be positive");
+    std::string why;
+    const cqsa_status s = cqsa::run_forward(plan->p, q, k, v, o, lse, res, workspace, workspace_bytes,
+                                            static_cast<hipStream_t>(stream), stats, why);
+    return s == CQSA_OK ? ok() : fail(s, why);
+  });
+}
+
+}  // extern "C"

@@ -1,0 +1,29 @@
+// Descriptor records shared by the host planner and the HIP kernels.
+// Plain structs with fixed layout; no HIP or host-only types.
+#pragma once
+
+#include <cstdint>
+
+namespace cqsa {
+
+// A contiguous run of admitted keys, in token rows of the K/V base the kernel reads.
+struct KeyRun {
+  int64_t start;  // first key row
+  int32_t len;    // number of keys (may be any positive count)
+  int32_t pad;
+};
+
+// One query block and its admitted keys.
+struct WorkItem {
+  int64_t q_row0;    // first query row in the Q base
+  int64_t out_row0;  // first row of the block in the (n, ml) output arrays
+  int32_t q_len;     // query rows in the block
+  int32_t run0;      // first KeyRun of this item
+  int32_t nrun;      // number of KeyRuns
+  int32_t keys;      // total admitted keys (for ordering only)
+};
+
+static_assert(sizeof(KeyRun) == 16, "KeyRun layout");
+static_assert(sizeof(WorkItem) == 32, "WorkItem layout");
+
+}  // namespace cqsa

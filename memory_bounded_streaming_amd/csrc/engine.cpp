@@ -1,0 +1,529 @@
+// Execution of a CQS plan on one GPU.
+//
+// Device-resident path: one launch of the partial kernel over every (task, query unit)
+// of the plan, each writing its visit slot, then one merge launch folding the slots of
+// every row in ascending task order.
+//
+// Host-pinned path (the stream engine): "Stream-CQSA: Breaking the Billion-Token
+// Barrier on a Single GPU" (wispaper explainer), section "Implementation: From
+// High-Level Logic to GPU Kernels": decompose, stream Q_i/K_i/V_i to the GPU, compute
+// the local numerators and denominators, aggregate (in host memory when the device
+// cannot hold the accumulator).  Tasks run in ascending id.  For each task the K/V
+// segments are gathered into a staging buffer on the K/V copy stream; query units are
+// streamed through a two-slot ring (Q block, partial block, accumulator block, output
+// block) on the Q copy stream; the compute stream runs the partial kernel and the merge;
+// the D2H stream returns accumulator or output blocks.  Events order every reuse of a
+// staging buffer or ring slot.
+#include "engine.hpp"
+
+#include <chrono>
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "kernels.hpp"
+
+namespace cqsa {
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+#define HIP_TRY(expr)                                                                      \
+  do {                                                                                     \
+    hipError_t e_ = (expr);                                                                \
+    if (e_ != hipSuccess) {                                                                \
+      why = std::string(#expr) + ": " + hipGetErrorString(e_);                             \
+      return e_ == hipErrorOutOfMemory ? CQSA_ENOMEM : CQSA_EHIP;                          \
+    }                                                                                      \
+  } while (0)
+
+float scale_log2(const Plan& p) { return static_cast<float>(1.0 / std::sqrt(double(p.d))) * kLog2e; }
+
+// Timing of one phase: pairs of events, summed after the final synchronisation.
+struct PhaseTimer {
+  bool on = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> spans[4];  // h2d, attn, merge, d2h
+  hipError_t begin(int phase, hipStream_t s, hipEvent_t& ev) {
+    ev = nullptr;
+    if (!on) return hipSuccess;
+    hipError_t e = hipEventCreate(&ev);
+    if (e != hipSuccess) return e;
+    spans[phase].push_back({ev, nullptr});
+    return hipEventRecord(ev, s);
+  }
+  hipError_t end(int phase, hipStream_t s) {
+    if (!on) return hipSuccess;
+    hipEvent_t ev;
+    hipError_t e = hipEventCreate(&ev);
+    if (e != hipSuccess) return e;
+    spans[phase].back().second = ev;
+    return hipEventRecord(ev, s);
+  }
+  double total(int phase) const {
+    double ms = 0;
+    for (auto& sp : spans[phase]) {
+      float t = 0;
+      if (sp.first && sp.second && hipEventElapsedTime(&t, sp.first, sp.second) == hipSuccess) ms += t;
+    }
+    return ms;
+  }
+  ~PhaseTimer() {
+    for (auto& v : spans)
+      for (auto& sp : v) {
+        if (sp.first) (void)hipEventDestroy(sp.first);
+        if (sp.second) (void)hipEventDestroy(sp.second);
+      }
+  }
+};
+
+enum { PH_H2D = 0, PH_ATTN = 1, PH_MERGE = 2, PH_D2H = 3 };
+
+}  // namespace
+
+// ----------------------------------------------------------------------------------
+// descriptor tables
+// ----------------------------------------------------------------------------------
+cqsa_status device_tables(const Plan& p, DeviceTables& out, std::string& why) {
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  const int64_t b0 = align_up(int64_t(p.dev_items.size()) * sizeof(WorkItem));
+  const int64_t b1 = align_up(int64_t(p.dev_runs.size()) * sizeof(KeyRun));
+  const int64_t b2 = align_up(int64_t(p.stream_items.size()) * sizeof(WorkItem));
+  const int64_t b3 = align_up(int64_t(p.stream_runs.size()) * sizeof(KeyRun));
+  std::lock_guard<std::mutex> lock(p.dev_mu);
+  char* base = nullptr;
+  for (auto& e : p.dev_tables)
+    if (e.first == dev) base = static_cast<char*>(e.second);
+  if (base == nullptr) {
+    std::vector<char> host(b0 + b1 + b2 + b3, 0);
+    std::memcpy(host.data(), p.dev_items.data(), p.dev_items.size() * sizeof(WorkItem));
+    std::memcpy(host.data() + b0, p.dev_runs.data(), p.dev_runs.size() * sizeof(KeyRun));
+    std::memcpy(host.data() + b0 + b1, p.stream_items.data(), p.stream_items.size() * sizeof(WorkItem));
+    std::memcpy(host.data() + b0 + b1 + b2, p.stream_runs.data(), p.stream_runs.size() * sizeof(KeyRun));
+    void* mem = nullptr;
+    HIP_TRY(hipMalloc(&mem, host.size()));
+    hipError_t e = hipMemcpy(mem, host.data(), host.size(), hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      (void)hipFree(mem);
+      why = std::string("hipMemcpy(descriptor tables): ") + hipGetErrorString(e);
+      return CQSA_EHIP;
+    }
+    p.dev_tables.push_back({dev, mem});
+    base = static_cast<char*>(mem);
+  }
+  out.dev_items = reinterpret_cast<const WorkItem*>(base);
+  out.dev_runs = reinterpret_cast<const KeyRun*>(base + b0);
+  out.stream_items = reinterpret_cast<const WorkItem*>(base + b0 + b1);
+  out.stream_runs = reinterpret_cast<const KeyRun*>(base + b0 + b1 + b2);
+  out.bytes = b0 + b1 + b2 + b3;
+  return CQSA_OK;
+}
+
+void free_device_tables(const Plan& p) {
+  std::lock_guard<std::mutex> lock(p.dev_mu);
+  int cur = 0;
+  const bool have = hipGetDevice(&cur) == hipSuccess;
+  for (auto& e : p.dev_tables) {
+    if (have) (void)hipSetDevice(e.first);
+    (void)hipFree(e.second);
+  }
+  if (have) (void)hipSetDevice(cur);
+  p.dev_tables.clear();
+}
+
+// ----------------------------------------------------------------------------------
+// device-resident path
+// ----------------------------------------------------------------------------------
+cqsa_status run_partials(const Plan& p, const void* q, const void* k, const void* v, float* n_out,
+                         float* ml_out, hipStream_t stream, std::string& why) {
+  DeviceTables t{};
+  cqsa_status st = device_tables(p, t, why);
+  if (st != CQSA_OK) return st;
+  AttnLaunch a{};
+  a.dtype = p.dtype;
+  a.d = p.d;
+  a.heads = p.heads;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.n_out = n_out;
+  a.ml_out = ml_out;
+  a.items = t.dev_items;
+  a.runs = t.dev_runs;
+  a.n_items = static_cast<int>(p.dev_items.size());
+  a.q_len = static_cast<int>(p.unit);
+  a.scale_log2 = scale_log2(p);
+  HIP_TRY(launch_attn(a, stream));
+  return CQSA_OK;
+}
+
+cqsa_status run_merge(const Plan& p, const float* n_in, const float* ml_in, void* o, float* lse,
+                      hipStream_t stream, std::string& why) {
+  MergeLaunch m{};
+  m.dtype = p.dtype;
+  m.d = p.d;
+  m.heads = p.heads;
+  m.rows = p.n;
+  m.n_a = n_in;
+  m.ml_a = ml_in;
+  m.b_stride_n = p.n * p.heads * int64_t(p.d);
+  m.b_stride_ml = p.n * p.heads * int64_t(2);
+  m.n_b = n_in + m.b_stride_n;
+  m.ml_b = ml_in + m.b_stride_ml;
+  m.nb = static_cast<int>(p.visits - 1);
+  m.final_out = true;
+  m.o_out = o;
+  m.lse_out = lse;
+  m.lse_stride = p.n;
+  m.lse_row0 = 0;
+  HIP_TRY(launch_merge(m, stream));
+  return CQSA_OK;
+}
+
+namespace {
+
+cqsa_status forward_device(const Plan& p, const void* q, const void* k, const void* v, void* o, float* lse,
+                           void* ws, int64_t ws_bytes, hipStream_t stream, cqsa_stats* stats, std::string& why) {
+  if (p.budget > 0 && p.device_ws > p.budget) {
+    why = "device-resident path needs " + std::to_string(p.device_ws) + " workspace bytes, over the budget";
+    return CQSA_EBUDGET;
+  }
+  bool owned = false;
+  if (ws == nullptr) {
+    HIP_TRY(hipMalloc(&ws, p.device_ws));
+    owned = true;
+  } else if (ws_bytes < p.device_ws) {
+    why = "workspace of " + std::to_string(ws_bytes) + " bytes, need " + std::to_string(p.device_ws);
+    return CQSA_ESMALL;
+  }
+  float* n_slots = static_cast<float*>(ws);
+  float* ml_slots = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(p.visits * p.n * p.heads * int64_t(p.d) * 4));
+  PhaseTimer tm;
+  tm.on = stats != nullptr;
+  const auto t0 = std::chrono::steady_clock::now();
+  hipEvent_t ev;
+  cqsa_status st = CQSA_OK;
+  auto fail = [&](cqsa_status s) {
+    if (owned) {
+      (void)hipStreamSynchronize(stream);
+      (void)hipFree(ws);
+    }
+    return s;
+  };
+  if (tm.begin(PH_ATTN, stream, ev) != hipSuccess) return fail(CQSA_EHIP);
+  st = run_partials(p, q, k, v, n_slots, ml_slots, stream, why);
+  if (st != CQSA_OK) return fail(st);
+  if (tm.end(PH_ATTN, stream) != hipSuccess || tm.begin(PH_MERGE, stream, ev) != hipSuccess) return fail(CQSA_EHIP);
+  st = run_merge(p, n_slots, ml_slots, o, lse, stream, why);
+  if (st != CQSA_OK) return fail(st);
+  if (tm.end(PH_MERGE, stream) != hipSuccess) return fail(CQSA_EHIP);
+  if (owned || stats) {
+    hipError_t e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) {
+      why = std::string("hipStreamSynchronize: ") + hipGetErrorString(e);
+      return fail(CQSA_EHIP);
+    }
+  }
+  if (owned) (void)hipFree(ws);
+  if (stats) {
+    DeviceTables t{};
+    (void)device_tables(p, t, why);
+    std::memset(stats, 0, sizeof(*stats));
+    stats->t_total_ms = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+    stats->t_attn_ms = tm.total(PH_ATTN);
+    stats->t_merge_ms = tm.total(PH_MERGE);
+    stats->peak_device_bytes = p.device_ws + t.bytes;
+    stats->n_attn_launches = 1;
+    stats->n_merge_launches = 1;
+    stats->useful_flop = 4.0 * double(p.n) * double(p.n) * p.d * p.heads;
+  }
+  return CQSA_OK;
+}
+
+// RAII holder of the stream engine's HIP objects.
+struct StreamRes {
+  hipStream_t s[4] = {nullptr, nullptr, nullptr, nullptr};  // kv, q, compute, d2h
+  std::vector<hipEvent_t> events;
+  void* ws = nullptr;
+  bool own_ws = false;
+  float* host_acc = nullptr;
+  ~StreamRes() {
+    for (hipStream_t x : s)
+      if (x) (void)hipStreamSynchronize(x);
+    for (hipEvent_t e : events) (void)hipEventDestroy(e);
+    for (hipStream_t x : s)
+      if (x) (void)hipStreamDestroy(x);
+    if (own_ws && ws) (void)hipFree(ws);
+    if (host_acc) (void)hipHostFree(host_acc);
+  }
+  hipError_t event(hipEvent_t& e) {
+    hipError_t r = hipEventCreateWithFlags(&e, hipEventDisableTiming);
+    if (r == hipSuccess) events.push_back(e);
+    return r;
+  }
+};
+
+cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const char* v, char* o, float* lse,
+                           void* ws, int64_t ws_bytes, hipStream_t caller, cqsa_stats* stats, std::string& why) {
+  const auto t0 = std::chrono::steady_clock::now();
+  const Footprint fp = p.stream_fp;
+  const StreamLayout L = stream_layout(p, fp.acc_on_device, fp.kv_buffers);
+  DeviceTables tabs{};
+  cqsa_status st = device_tables(p, tabs, why);
+  if (st != CQSA_OK) return st;
+
+  StreamRes R;
+  if (ws == nullptr) {
+    HIP_TRY(hipMalloc(&R.ws, L.total));
+    R.own_ws = true;
+  } else {
+    if (ws_bytes < L.total) {
+      why = "workspace of " + std::to_string(ws_bytes) + " bytes, need " + std::to_string(L.total);
+      return CQSA_ESMALL;
+    }
+    R.ws = ws;
+  }
+  // carve the workspace
+  char* cur = static_cast<char*>(R.ws);
+  auto take = [&](int64_t bytes) {
+    char* r = cur;
+    cur += bytes;
+    return r;
+  };
+  char* kst[2] = {nullptr, nullptr};
+  char* vst[2] = {nullptr, nullptr};
+  for (int b = 0; b < fp.kv_buffers; ++b) {
+    kst[b] = take(L.kv_stage);
+    vst[b] = take(L.kv_stage);
+  }
+  struct Slot {
+    char* q;
+    float* n;
+    float* ml;
+    float* an;
+    float* aml;
+    char* o;
+    float* lse;
+  } slot[2];
+  for (auto& s : slot) {
+    s.q = take(L.q_blk);
+    s.n = reinterpret_cast<float*>(take(L.n_blk));
+    s.ml = reinterpret_cast<float*>(take(L.ml_blk));
+    s.an = fp.acc_on_device ? nullptr : reinterpret_cast<float*>(take(L.n_blk));
+    s.aml = fp.acc_on_device ? nullptr : reinterpret_cast<float*>(take(L.ml_blk));
+    s.o = take(L.o_blk);
+    s.lse = reinterpret_cast<float*>(take(L.lse_blk));
+  }
+  float* acc_n = fp.acc_on_device ? reinterpret_cast<float*>(take(L.acc_n)) : nullptr;
+  float* acc_ml = fp.acc_on_device ? reinterpret_cast<float*>(take(L.acc_ml)) : nullptr;
+
+  const int64_t H = p.heads, D = p.d, U = p.unit, N = p.n;
+  const int64_t row_in = p.row_in_bytes();
+  const int64_t nrow_f = H * D;  // floats of n per token row
+  const int64_t mlrow_f = H * 2;
+  float* host_n = nullptr;
+  float* host_ml = nullptr;
+  if (!fp.acc_on_device) {
+    HIP_TRY(hipHostMalloc(reinterpret_cast<void**>(&R.host_acc), N * (nrow_f + mlrow_f) * sizeof(float),
+                          hipHostMallocDefault));
+    host_n = R.host_acc;
+    host_ml = R.host_acc + N * nrow_f;
+  }
+  for (auto& s : R.s) HIP_TRY(hipStreamCreateWithFlags(&s, hipStreamNonBlocking));
+  hipStream_t s_kv = R.s[0], s_q = R.s[1], s_c = R.s[2], s_d = R.s[3];
+  hipEvent_t start, kv_ready[2], kv_free[2], q_ready[2], c_done[2], slot_free[2];
+  HIP_TRY(R.event(start));
+  for (int i = 0; i < 2; ++i) {
+    HIP_TRY(R.event(kv_ready[i]));
+    HIP_TRY(R.event(kv_free[i]));
+    HIP_TRY(R.event(q_ready[i]));
+    HIP_TRY(R.event(c_done[i]));
+    HIP_TRY(R.event(slot_free[i]));
+  }
+  HIP_TRY(hipEventRecord(start, caller));
+  for (hipStream_t s : R.s) HIP_TRY(hipStreamWaitEvent(s, start, 0));
+
+  PhaseTimer tm;
+  tm.on = stats != nullptr;
+  hipEvent_t tev;
+  int64_t bytes_h2d = 0, bytes_d2h = 0, n_attn = 0, n_merge = 0, n_h2d = 0, n_d2h = 0;
+  const int64_t tu = p.task_units;
+  const float c2 = scale_log2(p);
+  const int64_t e = p.elem_bytes();
+  std::vector<int64_t> last_block(p.n_units, -4);  // ring block that last wrote a unit's host accumulator
+  int64_t blk = 0;
+
+  for (size_t ti = 0; ti < p.tasks.size(); ++ti) {
+    const Task& task = p.tasks[ti];
+    const int b = static_cast<int>(ti % fp.kv_buffers);
+    if (static_cast<int64_t>(ti) >= fp.kv_buffers) HIP_TRY(hipStreamWaitEvent(s_kv, kv_free[b], 0));
+    HIP_TRY(tm.begin(PH_H2D, s_kv, tev));
+    for (const Segment& g : task.segments) {
+      HIP_TRY(hipMemcpyAsync(kst[b] + g.local_offset * row_in, k + g.global_start * row_in, g.length * row_in,
+                             hipMemcpyHostToDevice, s_kv));
+      HIP_TRY(hipMemcpyAsync(vst[b] + g.local_offset * row_in, v + g.global_start * row_in, g.length * row_in,
+                             hipMemcpyHostToDevice, s_kv));
+      bytes_h2d += 2 * g.length * row_in;
+      n_h2d += 2;
+    }
+    HIP_TRY(tm.end(PH_H2D, s_kv));
+    HIP_TRY(hipEventRecord(kv_ready[b], s_kv));
+    HIP_TRY(hipStreamWaitEvent(s_c, kv_ready[b], 0));
+
+    for (int64_t a = 0; a < tu; ++a, ++blk) {
+      const int j = static_cast<int>(blk % 2);
+      Slot& S = slot[j];
+      const int64_t pu = task.units[a];
+      const int visit = task.slot[a];
+      const bool first = visit == 0, last = visit == p.visits - 1;
+      if (blk >= 2) HIP_TRY(hipStreamWaitEvent(s_q, slot_free[j], 0));
+      if (!fp.acc_on_device && !first && last_block[pu] == blk - 1)
+        HIP_TRY(hipStreamWaitEvent(s_q, slot_free[(blk - 1) % 2], 0));
+      // H2D: Q block (+ accumulator block)
+      HIP_TRY(tm.begin(PH_H2D, s_q, tev));
+      HIP_TRY(hipMemcpyAsync(S.q, q + pu * U * row_in, U * row_in, hipMemcpyHostToDevice, s_q));
+      bytes_h2d += U * row_in;
+      ++n_h2d;
+      if (!fp.acc_on_device && !first) {
+        HIP_TRY(hipMemcpyAsync(S.an, host_n + pu * U * nrow_f, U * nrow_f * 4, hipMemcpyHostToDevice, s_q));
+        HIP_TRY(hipMemcpyAsync(S.aml, host_ml + pu * U * mlrow_f, U * mlrow_f * 4, hipMemcpyHostToDevice, s_q));
+        bytes_h2d += U * (nrow_f + mlrow_f) * 4;
+        n_h2d += 2;
+      }
+      HIP_TRY(tm.end(PH_H2D, s_q));
+      HIP_TRY(hipEventRecord(q_ready[j], s_q));
+      HIP_TRY(hipStreamWaitEvent(s_c, q_ready[j], 0));
+
+      // partials of (task, unit)
+      float* pn = S.n;
+      float* pml = S.ml;
+      if (fp.acc_on_device && first) {
+        pn = acc_n + pu * U * nrow_f;
+        pml = acc_ml + pu * U * mlrow_f;
+      }
+      AttnLaunch at{};
+      at.dtype = p.dtype;
+      at.d = p.d;
+      at.heads = p.heads;
+      at.q = S.q;
+      at.k = kst[b];
+      at.v = vst[b];
+      at.n_out = pn;
+      at.ml_out = pml;
+      at.items = tabs.stream_items + (int64_t(ti) * tu + a);
+      at.runs = tabs.stream_runs;
+      at.n_items = 1;
+      at.q_len = static_cast<int>(U);
+      at.scale_log2 = c2;
+      HIP_TRY(tm.begin(PH_ATTN, s_c, tev));
+      HIP_TRY(launch_attn(at, s_c));
+      HIP_TRY(tm.end(PH_ATTN, s_c));
+      ++n_attn;
+
+      // merge into the accumulator (ascending task order per row)
+      MergeLaunch m{};
+      m.dtype = p.dtype;
+      m.d = p.d;
+      m.heads = p.heads;
+      m.rows = U;
+      m.final_out = last;
+      m.o_out = S.o;
+      m.lse_out = S.lse;
+      m.lse_stride = U;
+      m.lse_row0 = 0;
+      bool do_merge = true;
+      if (fp.acc_on_device) {
+        float* an = acc_n + pu * U * nrow_f;
+        float* aml = acc_ml + pu * U * mlrow_f;
+        m.n_a = an;
+        m.ml_a = aml;
+        m.n_b = S.n;
+        m.ml_b = S.ml;
+        m.nb = first ? 0 : 1;
+        m.n_out = an;
+        m.ml_out = aml;
+        do_merge = !first || last;
+      } else {
+        if (first) {
+          m.n_a = S.n;
+          m.ml_a = S.ml;
+          m.nb = 0;
+          do_merge = last;
+        } else {
+          m.n_a = S.an;
+          m.ml_a = S.aml;
+          m.n_b = S.n;
+          m.ml_b = S.ml;
+          m.nb = 1;
+          m.n_out = S.an;
+          m.ml_out = S.aml;
+        }
+      }
+      if (do_merge) {
+        HIP_TRY(tm.begin(PH_MERGE, s_c, tev));
+        HIP_TRY(launch_merge(m, s_c));
+        HIP_TRY(tm.end(PH_MERGE, s_c));
+        ++n_merge;
+      }
+      HIP_TRY(hipEventRecord(c_done[j], s_c));
+      if (a == tu - 1) HIP_TRY(hipEventRecord(kv_free[b], s_c));
+
+      // D2H: finished output block, or the accumulator block back to host memory
+      HIP_TRY(hipStreamWaitEvent(s_d, c_done[j], 0));
+      HIP_TRY(tm.begin(PH_D2H, s_d, tev));
+      if (last) {
+        HIP_TRY(hipMemcpyAsync(o + pu * U * H * D * e, S.o, U * H * D * e, hipMemcpyDeviceToHost, s_d));
+        bytes_d2h += U * H * D * e;
+        ++n_d2h;
+        if (lse != nullptr) {
+          HIP_TRY(hipMemcpy2DAsync(lse + pu * U, N * sizeof(float), S.lse, U * sizeof(float), U * sizeof(float), H,
+                                   hipMemcpyDeviceToHost, s_d));
+          bytes_d2h += H * U * 4;
+          ++n_d2h;
+        }
+      } else if (!fp.acc_on_device) {
+        const float* sn = first ? S.n : S.an;
+        const float* sml = first ? S.ml : S.aml;
+        HIP_TRY(hipMemcpyAsync(host_n + pu * U * nrow_f, sn, U * nrow_f * 4, hipMemcpyDeviceToHost, s_d));
+        HIP_TRY(hipMemcpyAsync(host_ml + pu * U * mlrow_f, sml, U * mlrow_f * 4, hipMemcpyDeviceToHost, s_d));
+        bytes_d2h += U * (nrow_f + mlrow_f) * 4;
+        n_d2h += 2;
+        last_block[pu] = blk;
+      }
+      HIP_TRY(tm.end(PH_D2H, s_d));
+      HIP_TRY(hipEventRecord(slot_free[j], s_d));
+    }
+  }
+  for (hipStream_t s : R.s) HIP_TRY(hipStreamSynchronize(s));
+  HIP_TRY(hipGetLastError());
+  if (stats) {
+    std::memset(stats, 0, sizeof(*stats));
+    stats->t_h2d_ms = tm.total(PH_H2D);
+    stats->t_attn_ms = tm.total(PH_ATTN);
+    stats->t_merge_ms = tm.total(PH_MERGE);
+    stats->t_d2h_ms = tm.total(PH_D2H);
+    stats->bytes_h2d = bytes_h2d;
+    stats->bytes_d2h = bytes_d2h;
+    stats->peak_device_bytes = L.total + tabs.bytes;
+    stats->n_attn_launches = n_attn;
+    stats->n_merge_launches = n_merge;
+    stats->n_h2d_copies = n_h2d;
+    stats->n_d2h_copies = n_d2h;
+    stats->useful_flop = 4.0 * double(p.n) * double(p.n) * p.d * p.heads;
+    stats->t_total_ms = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+  }
+  return CQSA_OK;
+}
+
+}  // namespace
+
+cqsa_status run_forward(const Plan& p, const void* q, const void* k, const void* v, void* o, float* lse,
+                        cqsa_residency res, void* ws, int64_t ws_bytes, hipStream_t stream, cqsa_stats* stats,
+                        std::string& why) {
+  if (res == CQSA_RES_DEVICE) return forward_device(p, q, k, v, o, lse, ws, ws_bytes, stream, stats, why);
+  return forward_stream(p, static_cast<const char*>(q), static_cast<const char*>(k), static_cast<const char*>(v),
+                        static_cast<char*>(o), lse, ws, ws_bytes, stream, stats, why);
+}
+
+}  // namespace cqsa

@@ -1,0 +1,33 @@
+// Device-resident execution and the stream engine behind cqsa_partials / cqsa_merge /
+// cqsa_forward.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include <string>
+
+#include "plan.hpp"
+
+namespace cqsa {
+
+struct DeviceTables {
+  const WorkItem* dev_items;
+  const KeyRun* dev_runs;
+  const WorkItem* stream_items;
+  const KeyRun* stream_runs;
+  int64_t bytes;
+};
+
+// Descriptor tables of the plan on the current device (uploaded on first use).
+cqsa_status device_tables(const Plan& p, DeviceTables& out, std::string& why);
+void free_device_tables(const Plan& p);
+
+cqsa_status run_partials(const Plan& p, const void* q, const void* k, const void* v, float* n_out,
+                         float* ml_out, hipStream_t stream, std::string& why);
+cqsa_status run_merge(const Plan& p, const float* n_in, const float* ml_in, void* o, float* lse,
+                      hipStream_t stream, std::string& why);
+cqsa_status run_forward(const Plan& p, const void* q, const void* k, const void* v, void* o, float* lse,
+                        cqsa_residency res, void* ws, int64_t ws_bytes, hipStream_t stream,
+                        cqsa_stats* stats, std::string& why);
+
+}  // namespace cqsa

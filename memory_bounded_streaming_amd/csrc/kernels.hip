@@ -1,0 +1,471 @@
+// HIP kernels for gfx950 (MI355X, CDNA4): masked attention partials and the merge of
+// (max, denominator, numerator) statistics.
+//
+// What they compute follows "Stream-CQSA: Breaking the Billion-Token Barrier on a
+// Single GPU" (wispaper explainer), section "Implementation: From High-Level Logic to
+// GPU Kernels" (local numerators and denominators of the softmax per task, the CQS Mask
+// selecting the keys) and the abstract of arXiv 2604.20819 (recompose the local
+// statistics).  The running-max form of the partials is the online normaliser of
+// "Online normalizer calculation for softmax" (cited by title on the arXiv page).
+//
+// Partial of one task for query row i:   (log2 units throughout)
+//   m = log2(e) * max_j s_ij,  l = sum_j 2^(log2(e) s_ij - m),  n = sum_j 2^(...) v_j
+// over the keys admitted for i.  The kernel design (tiles, LDS layout, MFMA shapes) is
+// this library's own for CDNA4 wave64 hardware.
+#include <hip/hip_runtime.h>
+
+#include "kernels.hpp"
+
+namespace cqsa {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned short u16;
+typedef unsigned int u32;
+
+struct AttnParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* n_out;
+  float* ml_out;
+  const WorkItem* items;
+  const KeyRun* runs;
+  int tiles_per_item;
+  int heads;
+  float scale_log2;
+};
+
+// Workgroups are dealt round-robin to the 8 XCDs; renumber them so that each XCD
+// receives one contiguous range of tiles (tiles of one query block and head share
+// their K/V stream, which then stays in that XCD's L2).
+__device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t grid) {
+  const int64_t q = grid / 8, r = grid % 8;
+  const int64_t x = b % 8, k = b / 8;
+  return x * q + (x < r ? x : r) + k;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+// ---------------------------------------------------------------------------------
+// bf16 partials on MFMA.  Workgroup = 4 wave64 = 128 query rows (32 per wave); the
+// key loop walks the item's admitted runs in tiles of 64 keys staged in LDS.
+//
+// S^T (keys x queries) = K_tile * Q^T with v_mfma_f32_32x32x16_bf16: A = 32 key rows
+// read from LDS, B = this lane's query slice held in registers.  Each lane then owns
+// one query column and 16 key rows of every 32x32 score tile, so the softmax row
+// statistics are lane-local plus one exchange with lane^32.  The K rows of an MFMA
+// tile are read in an order that swaps bits 2 and 3 of the row index; with that order
+// the 16 accumulator values a lane holds are exactly the B operand (8 consecutive
+// keys per half-wave) of O^T += V^T * P^T, so P never leaves registers.  V is
+// transposed on its way into LDS (dim-major) so the A operand of that product is one
+// 16-byte LDS read per lane.
+// ---------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void attn_partial_bf16(AttnParams P) {
+  constexpr int QT = 128;
+  constexpr int KT = 64;
+  constexpr int KSTR = D + 8;   // u16 per K row in LDS (16-byte pad)
+  constexpr int VSTR = KT + 8;  // u16 per V^T row in LDS
+  constexpr int NKK = D / 16;   // k-steps of Q K^T
+  constexpr int NDT = D / 32;   // 32-dim output tiles
+  constexpr int DCH = D / 8;    // 16-byte chunks per row
+  __shared__ __attribute__((aligned(16))) u16 ks[KT * KSTR];
+  __shared__ __attribute__((aligned(16))) u16 vt[D * VSTR];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int hl = lane >> 5, col = lane & 31;
+  const int64_t b = xcd_remap(blockIdx.x, gridDim.x);
+  const int tile = static_cast<int>(b % P.tiles_per_item);
+  const int64_t rest = b / P.tiles_per_item;
+  const int head = static_cast<int>(rest % P.heads);
+  const WorkItem it = P.items[rest / P.heads];
+  const int64_t rs = static_cast<int64_t>(P.heads) * D;
+  const u16* __restrict__ Q = static_cast<const u16*>(P.q);
+  const u16* __restrict__ K = static_cast<const u16*>(P.k);
+  const u16* __restrict__ V = static_cast<const u16*>(P.v);
+
+  const int qi = tile * QT + wave * 32 + col;
+  const bool qok = qi < it.q_len;
+  bf16x8 qf[NKK];
+  {
+    const u16* qp = Q + (it.q_row0 + (qok ? qi : 0)) * rs + head * D + 8 * hl;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (qok) u = *reinterpret_cast<const uint4*>(qp + 16 * kk);
+      qf[kk] = as_bf16x8(u);
+    }
+  }
+
+  f32x16 o[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const float c2 = P.scale_log2;
+  const int prow = (col & ~12) | ((col & 4) << 1) | ((col & 8) >> 1);
+
+  for (int ri = 0; ri < it.nrun; ++ri) {
+    const KeyRun run = P.runs[it.run0 + ri];
+    for (int k0 = 0; k0 < run.len; k0 += KT) {
+      const int nv = min(KT, run.len - k0);
+      const int64_t kbase = (run.start + k0) * rs + head * D;
+      __syncthreads();
+      // K tile, row-major [key][dim]
+      for (int c = tid; c < KT * DCH; c += 256) {
+        const int kr = c / DCH, kc = c % DCH;
+        uint4 val = make_uint4(0, 0, 0, 0);
+        if (kr < nv) val = *reinterpret_cast<const uint4*>(K + kbase + kr * rs + kc * 8);
+        *reinterpret_cast<uint4*>(ks + kr * KSTR + kc * 8) = val;
+      }
+      // V tile, transposed to [dim][key]: each thread moves a 4-key x 8-dim block
+      for (int c = tid; c < (KT / 4) * DCH; c += 256) {
+        const int kg = c / DCH, db = c % DCH;
+        uint4 rw[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          rw[j] = make_uint4(0, 0, 0, 0);
+          if (4 * kg + j < nv) rw[j] = *reinterpret_cast<const uint4*>(V + kbase + (4 * kg + j) * rs + db * 8);
+        }
+        const u32* w0 = reinterpret_cast<const u32*>(&rw[0]);
+        const u32* w1 = reinterpret_cast<const u32*>(&rw[1]);
+        const u32* w2 = reinterpret_cast<const u32*>(&rw[2]);
+        const u32* w3 = reinterpret_cast<const u32*>(&rw[3]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int wd = e >> 1;
+          u32 lo, hi;
+          if (e & 1) {
+            lo = (w0[wd] >> 16) | (w1[wd] & 0xFFFF0000u);
+            hi = (w2[wd] >> 16) | (w3[wd] & 0xFFFF0000u);
+          } else {
+            lo = (w0[wd] & 0xFFFFu) | (w1[wd] << 16);
+            hi = (w2[wd] & 0xFFFFu) | (w3[wd] << 16);
+          }
+          *reinterpret_cast<uint2*>(vt + (db * 8 + e) * VSTR + 4 * kg) = make_uint2(lo, hi);
+        }
+      }
+      __syncthreads();
+
+      // scores S^T for keys [0,32) and [32,64)
+      f32x16 s[2];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[st][i] = 0.f;
+        const u16* kp = ks + (32 * st + prow) * KSTR + 8 * hl;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(kp + 16 * kk));
+          s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[st], 0, 0, 0);
+        }
+      }
+      // accumulator element i of tile st holds key 32*st + 16*(i/8) + 8*hl + i%8
+      float mx = -INFINITY;
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = 32 * st + 16 * (i >> 3) + 8 * hl + (i & 7);
+          const float x = key < nv ? s[st][i] * c2 : -INFINITY;
+          s[st][i] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      float ps = 0.f;
+      bf16x8 pf[4];
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float pv = __builtin_amdgcn_exp2f(s[st][i] - m_use);
+          ps += pv;
+          pf[2 * st + (i >> 3)][i & 7] = static_cast<__bf16>(pv);
+        }
+      l_run = l_run * alpha + ps;
+      m_run = m_new;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+      // O^T (dims x queries) += V^T * P^T, 16 keys per step
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const u16* vp = vt + (32 * dt + col) * VSTR + 8 * hl;
+#pragma unroll
+        for (int kp4 = 0; kp4 < 4; ++kp4) {
+          const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(vp + 16 * kp4));
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kp4], o[dt], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (qok) {
+    const int64_t orow = it.out_row0 + qi;
+    float* np = P.n_out + (orow * P.heads + head) * D;
+    // accumulator element i of tile dt holds dim 32*dt + 8*(i/4) + 4*hl + i%4
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 val = make_float4(o[dt][4 * g], o[dt][4 * g + 1], o[dt][4 * g + 2], o[dt][4 * g + 3]);
+        *reinterpret_cast<float4*>(np + 32 * dt + 8 * g + 4 * hl) = val;
+      }
+    if (hl == 0) *reinterpret_cast<float2*>(P.ml_out + (orow * P.heads + head) * 2) = make_float2(m_run, l_tot);
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// float32 partials (correctness path for float32 inputs): one wave of 64 query rows,
+// one row per lane, K/V tiles of 32 keys in LDS read by broadcast, fp32 FMA.
+// ---------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(64) void attn_partial_f32(AttnParams P) {
+  constexpr int QT = 64;
+  constexpr int KT = 32;
+  __shared__ __attribute__((aligned(16))) float kf[KT * D];
+  __shared__ __attribute__((aligned(16))) float vf[KT * D];
+  const int lane = threadIdx.x;
+  const int64_t b = xcd_remap(blockIdx.x, gridDim.x);
+  const int tile = static_cast<int>(b % P.tiles_per_item);
+  const int64_t rest = b / P.tiles_per_item;
+  const int head = static_cast<int>(rest % P.heads);
+  const WorkItem it = P.items[rest / P.heads];
+  const int64_t rs = static_cast<int64_t>(P.heads) * D;
+  const float* __restrict__ Q = static_cast<const float*>(P.q);
+  const float* __restrict__ K = static_cast<const float*>(P.k);
+  const float* __restrict__ V = static_cast<const float*>(P.v);
+
+  const int qi = tile * QT + lane;
+  const bool qok = qi < it.q_len;
+  float q[D], o[D];
+  {
+    const float* qp = Q + (it.q_row0 + (qok ? qi : 0)) * rs + head * D;
+#pragma unroll
+    for (int t = 0; t < D; t += 4) {
+      float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (qok) u = *reinterpret_cast<const float4*>(qp + t);
+      q[t] = u.x;
+      q[t + 1] = u.y;
+      q[t + 2] = u.z;
+      q[t + 3] = u.w;
+      o[t] = o[t + 1] = o[t + 2] = o[t + 3] = 0.f;
+    }
+  }
+  float m_run = -INFINITY, l_run = 0.f;
+  const float c2 = P.scale_log2;
+  for (int ri = 0; ri < it.nrun; ++ri) {
+    const KeyRun run = P.runs[it.run0 + ri];
+    for (int k0 = 0; k0 < run.len; k0 += KT) {
+      const int nv = min(KT, run.len - k0);
+      const int64_t kbase = (run.start + k0) * rs + head * D;
+      __syncthreads();
+      for (int c = lane; c < KT * D / 4; c += 64) {
+        const int kr = c / (D / 4), kc = c % (D / 4);
+        float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
+        if (kr < nv) {
+          kv = *reinterpret_cast<const float4*>(K + kbase + kr * rs + kc * 4);
+          vv = *reinterpret_cast<const float4*>(V + kbase + kr * rs + kc * 4);
+        }
+        *reinterpret_cast<float4*>(kf + kr * D + kc * 4) = kv;
+        *reinterpret_cast<float4*>(vf + kr * D + kc * 4) = vv;
+      }
+      __syncthreads();
+      float sc[KT];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < KT; ++j) {
+        float acc = 0.f;
+#pragma unroll
+        for (int t = 0; t < D; ++t) acc = fmaf(q[t], kf[j * D + t], acc);
+        sc[j] = j < nv ? acc * c2 : -INFINITY;
+        mx = fmaxf(mx, sc[j]);
+      }
+      const float m_new = fmaxf(m_run, mx);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < D; ++t) o[t] *= alpha;
+#pragma unroll
+      for (int j = 0; j < KT; ++j) {
+        const float pv = __builtin_amdgcn_exp2f(sc[j] - m_use);
+        l_run += pv;
+#pragma unroll
+        for (int t = 0; t < D; ++t) o[t] = fmaf(pv, vf[j * D + t], o[t]);
+      }
+      m_run = m_new;
+    }
+  }
+  if (qok) {
+    const int64_t orow = it.out_row0 + qi;
+    float* np = P.n_out + (orow * P.heads + head) * D;
+#pragma unroll
+    for (int t = 0; t < D; t += 4) *reinterpret_cast<float4*>(np + t) = make_float4(o[t], o[t + 1], o[t + 2], o[t + 3]);
+    *reinterpret_cast<float2*>(P.ml_out + (orow * P.heads + head) * 2) = make_float2(m_run, l_run);
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Merge: D/4 lanes per (row, head), one float4 of n each; fold inputs in order.
+// ---------------------------------------------------------------------------------
+struct MergeParams {
+  const float* n_a;
+  const float* ml_a;
+  const float* n_b;
+  const float* ml_b;
+  int64_t b_stride_n, b_stride_ml;
+  int nb;
+  int heads;
+  int64_t pairs;
+  int final_out;
+  float* n_out;
+  float* ml_out;
+  void* o_out;
+  float* lse_out;
+  int64_t lse_stride, lse_row0;
+};
+
+__device__ __forceinline__ void store_out(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
+
+__device__ __forceinline__ u32 bf16_rne(float x) {
+  const u32 u = __builtin_bit_cast(u32, x);
+  if ((u & 0x7F800000u) == 0x7F800000u) return (u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u);  // inf / nan
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ void store_out(u16* p, float4 v) {
+  const u32 a = bf16_rne(v.x) | (bf16_rne(v.y) << 16);
+  const u32 b = bf16_rne(v.z) | (bf16_rne(v.w) << 16);
+  *reinterpret_cast<uint2*>(p) = make_uint2(a, b);
+}
+
+template <int D, typename OutT>
+__global__ __launch_bounds__(256) void merge_partials(MergeParams P) {
+  constexpr int TPR = D / 4;
+  constexpr int PPB = 256 / TPR;
+  const int64_t pair = static_cast<int64_t>(blockIdx.x) * PPB + threadIdx.x / TPR;
+  const int t = threadIdx.x % TPR;
+  if (pair >= P.pairs) return;
+  const float2 mla = *reinterpret_cast<const float2*>(P.ml_a + 2 * pair);
+  float4 n = *reinterpret_cast<const float4*>(P.n_a + pair * D + 4 * t);
+  float m = mla.x, l = mla.y;
+  for (int s = 0; s < P.nb; ++s) {
+    const float2 mlb = *reinterpret_cast<const float2*>(P.ml_b + s * P.b_stride_ml + 2 * pair);
+    const float4 nb = *reinterpret_cast<const float4*>(P.n_b + s * P.b_stride_n + pair * D + 4 * t);
+    const float mn = fmaxf(m, mlb.x);
+    const float mu = mn == -INFINITY ? 0.f : mn;
+    const float wa = __builtin_amdgcn_exp2f(m - mu);
+    const float wb = __builtin_amdgcn_exp2f(mlb.x - mu);
+    l = fmaf(l, wa, mlb.y * wb);
+    n.x = fmaf(n.x, wa, nb.x * wb);
+    n.y = fmaf(n.y, wa, nb.y * wb);
+    n.z = fmaf(n.z, wa, nb.z * wb);
+    n.w = fmaf(n.w, wa, nb.w * wb);
+    m = mn;
+  }
+  if (!P.final_out) {
+    *reinterpret_cast<float4*>(P.n_out + pair * D + 4 * t) = n;
+    if (t == 0) *reinterpret_cast<float2*>(P.ml_out + 2 * pair) = make_float2(m, l);
+    return;
+  }
+  float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (l > 0.f) y = make_float4(n.x / l, n.y / l, n.z / l, n.w / l);
+  store_out(static_cast<OutT*>(P.o_out) + pair * D + 4 * t, y);
+  if (t == 0 && P.lse_out != nullptr) {
+    const int64_t row = pair / P.heads;
+    const int head = static_cast<int>(pair % P.heads);
+    const float lse = l > 0.f ? (m + log2f(l)) * 0.69314718055994531f : -INFINITY;
+    P.lse_out[head * P.lse_stride + P.lse_row0 + row] = lse;
+  }
+}
+
+}  // namespace
+
+int attn_query_tile(cqsa_dtype dtype) { return dtype == CQSA_BF16 ? 128 : 64; }
+
+hipError_t launch_attn(const AttnLaunch& a, hipStream_t stream) {
+  if (a.n_items <= 0 || a.q_len <= 0) return hipSuccess;
+  AttnParams p;
+  p.q = a.q;
+  p.k = a.k;
+  p.v = a.v;
+  p.n_out = a.n_out;
+  p.ml_out = a.ml_out;
+  p.items = a.items;
+  p.runs = a.runs;
+  p.heads = a.heads;
+  p.scale_log2 = a.scale_log2;
+  const int qt = attn_query_tile(a.dtype);
+  p.tiles_per_item = (a.q_len + qt - 1) / qt;
+  const int64_t blocks = int64_t(a.n_items) * p.tiles_per_item * a.heads;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  const dim3 grid(static_cast<unsigned>(blocks));
+  if (a.dtype == CQSA_BF16) {
+    if (a.d == 128)
+      hipLaunchKernelGGL(attn_partial_bf16<128>, grid, dim3(256), 0, stream, p);
+    else if (a.d == 64)
+      hipLaunchKernelGGL(attn_partial_bf16<64>, grid, dim3(256), 0, stream, p);
+    else
+      return hipErrorInvalidValue;
+  } else {
+    if (a.d == 128)
+      hipLaunchKernelGGL(attn_partial_f32<128>, grid, dim3(64), 0, stream, p);
+    else if (a.d == 64)
+      hipLaunchKernelGGL(attn_partial_f32<64>, grid, dim3(64), 0, stream, p);
+    else
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const MergeLaunch& m, hipStream_t stream) {
+  if (m.rows <= 0) return hipSuccess;
+  MergeParams p;
+  p.n_a = m.n_a;
+  p.ml_a = m.ml_a;
+  p.n_b = m.n_b;
+  p.ml_b = m.ml_b;
+  p.b_stride_n = m.b_stride_n;
+  p.b_stride_ml = m.b_stride_ml;
+  p.nb = m.nb;
+  p.heads = m.heads;
+  p.pairs = m.rows * m.heads;
+  p.final_out = m.final_out ? 1 : 0;
+  p.n_out = m.n_out;
+  p.ml_out = m.ml_out;
+  p.o_out = m.o_out;
+  p.lse_out = m.lse_out;
+  p.lse_stride = m.lse_stride;
+  p.lse_row0 = m.lse_row0;
+  const int tpr = m.d / 4;
+  const int64_t ppb = 256 / tpr;
+  const int64_t blocks = (p.pairs + ppb - 1) / ppb;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  const dim3 grid(static_cast<unsigned>(blocks));
+  const bool bf = m.dtype == CQSA_BF16;
+  if (m.d == 128) {
+    if (bf)
+      hipLaunchKernelGGL((merge_partials<128, u16>), grid, dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((merge_partials<128, float>), grid, dim3(256), 0, stream, p);
+  } else if (m.d == 64) {
+    if (bf)
+      hipLaunchKernelGGL((merge_partials<64, u16>), grid, dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((merge_partials<64, float>), grid, dim3(256), 0, stream, p);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace cqsa

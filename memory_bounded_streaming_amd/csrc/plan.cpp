@@ -1,0 +1,367 @@
+// Host CQS planner.
+//
+// Combinatorics follow "Stream-CQSA: Breaking the Billion-Token Barrier on a Single
+// GPU" (wispaper explainer): section "The 'CQS Divide': Attention as a Steiner System"
+// (c = l(l-1)+1 chunks, c subsequences of l chunks, every chunk pair exactly once),
+// section "The Recursive Benefit" (divide a task again), and section "Implementation:
+// From High-Level Logic to GPU Kernels" (a CQS Mask removes the redundant overlapping
+// regions).  The construction rule of the quorum ("derived from the theory of cyclic
+// quorum sets", abstract of arXiv 2604.20819) and the owner of each diagonal block are
+// readings: the smallest perfect difference set containing {0,1}, and "chunk x owns its
+// diagonal block in task t = x".
+#include "plan.hpp"
+
+#include <algorithm>
+#include <cmath>
+#include <numeric>
+
+namespace cqsa {
+
+namespace {
+
+bool dfs_extend(int l, int c, std::vector<int>& chosen, std::vector<char>& used, int start) {
+  if (static_cast<int>(chosen.size()) == l) return true;
+  for (int x = start; x < c; ++x) {
+    // both differences against every chosen residue must be unused so far
+    std::vector<int> fresh;
+    bool ok = true;
+    for (int a : chosen) {
+      const int d1 = (x - a + c) % c, d2 = (a - x + c) % c;
+      if (used[d1] || used[d2] || d1 == d2 ||
+          std::find(fresh.begin(), fresh.end(), d1) != fresh.end() ||
+          std::find(fresh.begin(), fresh.end(), d2) != fresh.end()) {
+        ok = false;
+        break;
+      }
+      fresh.push_back(d1);
+      fresh.push_back(d2);
+    }
+    if (!ok) continue;
+    chosen.push_back(x);
+    for (int f : fresh) used[f] = 1;
+    if (dfs_extend(l, c, chosen, used, x + 1)) return true;
+    for (int f : fresh) used[f] = 0;
+    chosen.pop_back();
+  }
+  return false;
+}
+
+}  // namespace
+
+cqsa_status difference_set(int l, std::vector<int>& out, std::string& why) {
+  out.clear();
+  if (l < 1 || l > CQSA_MAX_L) {
+    why = "l must be in 1.." + std::to_string(CQSA_MAX_L);
+    return CQSA_EINVAL;
+  }
+  if (l == 1) {
+    out.push_back(0);
+    return CQSA_OK;
+  }
+  const int c = l * (l - 1) + 1;
+  std::vector<char> used(c, 0);
+  std::vector<int> chosen{0, 1};
+  used[1] = used[c - 1] = 1;
+  if (!dfs_extend(l, c, chosen, used, 2)) {
+    why = "no perfect difference set exists for l=" + std::to_string(l) + " (c=" + std::to_string(c) + ")";
+    return CQSA_ENOSET;
+  }
+  out = chosen;
+  return CQSA_OK;
+}
+
+StreamLayout stream_layout(const Plan& p, bool acc_on_device, int kv_buffers) {
+  StreamLayout s{};
+  const int64_t u = p.unit, h = p.heads, d = p.d, e = p.elem_bytes();
+  s.kv_stage = align_up(p.task_tokens() * p.row_in_bytes());
+  s.q_blk = align_up(u * p.row_in_bytes());
+  s.n_blk = align_up(u * h * d * 4);
+  s.ml_blk = align_up(u * h * 2 * 4);
+  s.o_blk = align_up(u * h * d * e);
+  s.lse_blk = align_up(h * u * 4);
+  s.acc_n = acc_on_device ? align_up(p.n * h * d * 4) : 0;
+  s.acc_ml = acc_on_device ? align_up(p.n * h * 2 * 4) : 0;
+  const int64_t slot = s.q_blk + s.n_blk + s.ml_blk + (acc_on_device ? 0 : s.n_blk + s.ml_blk) + s.o_blk + s.lse_blk;
+  s.total = 2 * kv_buffers * s.kv_stage + 2 * slot + s.acc_n + s.acc_ml;
+  return s;
+}
+
+namespace {
+
+// Every innermost task with its units, per-level chunk of each local unit, admitted
+// runs and segments.  With several levels a (task, query unit) may admit no key at all
+// (its keys all belong to other tasks); its partial is then the empty triple.
+cqsa_status build_tasks(Plan& p, std::string& why) {
+  (void)why;
+  const int levels = static_cast<int>(p.ls.size());
+  std::vector<int64_t> parent_len(levels + 1), chunk_len(levels);
+  parent_len[0] = p.n_units;
+  for (int k = 0; k < levels; ++k) {
+    chunk_len[k] = parent_len[k] / p.cs[k];
+    parent_len[k + 1] = chunk_len[k] * p.ls[k];
+  }
+  p.task_units = parent_len[levels];
+  // sorted member chunks of every subsequence, per level
+  std::vector<std::vector<std::vector<int>>> members(levels);
+  for (int k = 0; k < levels; ++k) {
+    members[k].resize(p.cs[k]);
+    for (int t = 0; t < p.cs[k]; ++t) {
+      for (int dd : p.sets[k]) members[k][t].push_back((t + dd) % p.cs[k]);
+      std::sort(members[k][t].begin(), members[k][t].end());
+    }
+  }
+  const int64_t n_tasks = p.n_units;  // prod(c)
+  p.tasks.assign(n_tasks, Task{});
+  std::vector<int32_t> seen(p.n_units, 0);
+  const int64_t tu = p.task_units;
+  std::vector<int32_t> chunk_of(static_cast<size_t>(levels) * tu);
+  for (int64_t tid = 0; tid < n_tasks; ++tid) {
+    Task& task = p.tasks[tid];
+    task.tid = tid;
+    task.ids.assign(levels, 0);
+    int64_t rem = tid;
+    for (int k = levels - 1; k >= 0; --k) {
+      task.ids[k] = static_cast<int>(rem % p.cs[k]);
+      rem /= p.cs[k];
+    }
+    task.units.resize(tu);
+    for (int64_t a = 0; a < tu; ++a) {
+      int64_t x = a;  // index in the level-k task list, walking outward
+      for (int k = levels - 1; k >= 0; --k) {
+        const int chunk = members[k][task.ids[k]][x / chunk_len[k]];
+        chunk_of[static_cast<size_t>(k) * tu + a] = chunk;
+        x = chunk * chunk_len[k] + x % chunk_len[k];
+      }
+      task.units[a] = x;
+    }
+    // CQS Mask: admitted iff at every level the chunks differ or equal the task's own index
+    task.runs.assign(tu, {});
+    for (int64_t a = 0; a < tu; ++a) {
+      auto& runs = task.runs[a];
+      for (int64_t b = 0; b < tu; ++b) {
+        bool ok = true;
+        for (int k = 0; k < levels && ok; ++k) {
+          const int ca = chunk_of[static_cast<size_t>(k) * tu + a];
+          const int cb = chunk_of[static_cast<size_t>(k) * tu + b];
+          ok = (ca != cb) || (ca == task.ids[k]);
+        }
+        if (!ok) continue;
+        ++task.admitted_units;
+        if (!runs.empty() && runs.back().start + runs.back().count == b)
+          ++runs.back().count;
+        else
+          runs.push_back({static_cast<int32_t>(b), 1});
+      }
+    }
+    for (int64_t a = 0; a < tu; ++a) {
+      const int64_t g = task.units[a];
+      if (!task.segments.empty() &&
+          task.segments.back().global_start + task.segments.back().length == g * p.unit)
+        task.segments.back().length += p.unit;
+      else
+        task.segments.push_back({g * p.unit, p.unit, a * p.unit});
+    }
+    task.slot.resize(tu);
+    for (int64_t a = 0; a < tu; ++a) task.slot[a] = seen[task.units[a]]++;
+  }
+  return CQSA_OK;
+}
+
+void build_schedule(Plan& p) {
+  auto& s = p.schedule;
+  s.clear();
+  s.push_back(static_cast<int64_t>(p.ls.size()));
+  for (size_t k = 0; k < p.ls.size(); ++k) {
+    s.push_back(p.cs[k]);
+    s.push_back(p.ls[k]);
+  }
+  s.push_back(static_cast<int64_t>(p.tasks.size()));
+  s.push_back(p.unit);
+  s.push_back(p.n_units);
+  for (const Task& t : p.tasks) {
+    s.push_back(t.tid);
+    for (int id : t.ids) s.push_back(id);
+    s.push_back(static_cast<int64_t>(t.segments.size()));
+    for (const Segment& g : t.segments) {
+      s.push_back(g.global_start);
+      s.push_back(g.length);
+      s.push_back(g.local_offset);
+    }
+    s.push_back(static_cast<int64_t>(t.units.size()));
+    for (size_t a = 0; a < t.units.size(); ++a) {
+      s.push_back(t.units[a]);
+      s.push_back(static_cast<int64_t>(t.runs[a].size()));
+      for (const UnitRun& r : t.runs[a]) {
+        s.push_back(r.start);
+        s.push_back(r.count);
+      }
+    }
+  }
+}
+
+// Kernel descriptor tables.  Key runs are split wherever the task's local order is not
+// globally contiguous, in both tables, so device-resident and streamed execution walk
+// identical key tiles and give identical bits.
+void build_descriptors(Plan& p) {
+  p.dev_items.clear();
+  p.dev_runs.clear();
+  p.stream_items.clear();
+  p.stream_runs.clear();
+  for (const Task& t : p.tasks) {
+    for (size_t a = 0; a < t.units.size(); ++a) {
+      WorkItem di{}, si{};
+      di.q_row0 = t.units[a] * p.unit;
+      di.out_row0 = int64_t(t.slot[a]) * p.n + t.units[a] * p.unit;
+      di.q_len = si.q_len = static_cast<int32_t>(p.unit);
+      di.run0 = static_cast<int32_t>(p.dev_runs.size());
+      si.run0 = static_cast<int32_t>(p.stream_runs.size());
+      int64_t keys = 0;
+      for (const UnitRun& r : t.runs[a]) {
+        int64_t b = r.start;
+        const int64_t end = r.start + r.count;
+        while (b < end) {
+          int64_t e = b + 1;
+          while (e < end && t.units[e] == t.units[e - 1] + 1) ++e;
+          const int64_t len = (e - b) * p.unit;
+          p.dev_runs.push_back({t.units[b] * p.unit, static_cast<int32_t>(len), 0});
+          p.stream_runs.push_back({b * p.unit, static_cast<int32_t>(len), 0});
+          keys += len;
+          b = e;
+        }
+      }
+      di.nrun = si.nrun = static_cast<int32_t>(p.dev_runs.size()) - di.run0;
+      di.keys = si.keys = static_cast<int32_t>(std::min<int64_t>(keys, INT32_MAX));
+      p.dev_items.push_back(di);
+      p.stream_items.push_back(si);
+    }
+  }
+  // heaviest query blocks first in the one-launch device path (load balance only)
+  std::stable_sort(p.dev_items.begin(), p.dev_items.end(),
+                   [](const WorkItem& x, const WorkItem& y) { return x.keys > y.keys; });
+}
+
+int64_t descriptor_bytes(const Plan& p) {
+  return align_up(int64_t(p.dev_items.size()) * sizeof(WorkItem)) +
+         align_up(int64_t(p.dev_runs.size()) * sizeof(KeyRun)) +
+         align_up(int64_t(p.stream_items.size()) * sizeof(WorkItem)) +
+         align_up(int64_t(p.stream_runs.size()) * sizeof(KeyRun));
+}
+
+cqsa_status choose_mode(Plan& p, std::string& why) {
+  struct Cand {
+    bool dev;
+    int kv;
+  };
+  const Cand order[4] = {{true, 2}, {false, 2}, {true, 1}, {false, 1}};
+  const int64_t desc = descriptor_bytes(p);
+  int64_t smallest = -1;
+  for (const Cand& c : order) {
+    if ((p.flags & CQSA_FLAG_HOST_ACC) && c.dev) continue;
+    if ((p.flags & CQSA_FLAG_KV_SINGLE) && c.kv != 1) continue;
+    const int64_t bytes = stream_layout(p, c.dev, c.kv).total;
+    if (smallest < 0 || bytes < smallest) smallest = bytes;
+    if (p.budget == 0 || bytes + desc <= p.budget) {
+      p.stream_fp = {c.dev, c.kv, bytes};
+      p.host_acc_bytes = c.dev ? 0 : p.n * p.row_part_bytes();
+      return CQSA_OK;
+    }
+  }
+  why = "no staging mode fits the budget of " + std::to_string(p.budget) + " bytes (smallest needs " +
+        std::to_string(smallest + desc) + ")";
+  return CQSA_EBUDGET;
+}
+
+cqsa_status build_fixed(int64_t n, int heads, int d, cqsa_dtype dtype, const std::vector<int>& ls,
+                        int64_t budget, uint32_t flags, Plan& p, std::string& why) {
+  p.n = n;
+  p.heads = heads;
+  p.d = d;
+  p.dtype = dtype;
+  p.ls = ls;
+  p.cs.clear();
+  p.sets.clear();
+  p.budget = budget;
+  p.flags = flags;
+  int64_t prod_c = 1, prod_l = 1;
+  for (int l : ls) {
+    std::vector<int> dset;
+    const cqsa_status st = difference_set(l, dset, why);
+    if (st != CQSA_OK) return st;
+    p.sets.push_back(dset);
+    p.cs.push_back(l * (l - 1) + 1);
+    prod_c *= p.cs.back();
+    prod_l *= l;
+    if (prod_c > n) break;
+  }
+  if (static_cast<int>(p.cs.size()) != static_cast<int>(ls.size()) || n % prod_c != 0) {
+    why = "N=" + std::to_string(n) + " is not a multiple of prod(c)";
+    return CQSA_EDIVIDE;
+  }
+  p.n_units = prod_c;
+  p.unit = n / prod_c;
+  p.visits = prod_l;
+  if (p.unit * prod_l > INT32_MAX) {
+    why = "a task holds more than 2^31-1 tokens";
+    return CQSA_EINVAL;
+  }
+  cqsa_status st = build_tasks(p, why);
+  if (st != CQSA_OK) return st;
+  build_schedule(p);
+  build_descriptors(p);
+  p.device_ws = align_up(p.visits * p.n * heads * int64_t(d) * 4) + align_up(p.visits * p.n * heads * int64_t(2) * 4);
+  return choose_mode(p, why);
+}
+
+}  // namespace
+
+cqsa_status build_plan(int64_t n, int heads, int d, cqsa_dtype dtype, const int32_t* ls, int n_levels,
+                       int64_t budget, uint32_t flags, Plan& out, std::string& why) {
+  if (n < 1 || heads < 1 || (d != 64 && d != 128) || ls == nullptr || n_levels < 0 ||
+      n_levels > CQSA_MAX_LEVELS || budget < 0 || (dtype != CQSA_BF16 && dtype != CQSA_F32) ||
+      (flags & ~(CQSA_FLAG_HOST_ACC | CQSA_FLAG_KV_SINGLE)) != 0) {
+    why = "invalid argument (need n>=1, heads>=1, head_dim 64 or 128, 0<=n_levels<=8, budget>=0, known dtype/flags)";
+    return CQSA_EINVAL;
+  }
+  if (n > (int64_t(1) << 40) || int64_t(heads) * d > (int64_t(1) << 20)) {
+    why = "problem too large";
+    return CQSA_EINVAL;
+  }
+  if (n_levels > 0) {
+    std::vector<int> levels(ls, ls + n_levels);
+    for (int l : levels)
+      if (l < 1 || l > CQSA_MAX_L) {
+        why = "each l must be in 1..10";
+        return CQSA_EINVAL;
+      }
+    return build_fixed(n, heads, d, dtype, levels, budget, flags, out, why);
+  }
+  // auto: repeat l until the host-pinned path fits the budget
+  const int l = ls[0];
+  if (l < 2 || l > CQSA_MAX_L) {
+    why = "auto levels need l in 2..10";
+    return CQSA_EINVAL;
+  }
+  std::vector<int> levels;
+  cqsa_status last = CQSA_EBUDGET;
+  std::string last_why;
+  for (int k = 1; k <= CQSA_MAX_LEVELS; ++k) {
+    levels.push_back(l);
+    std::string w;
+    last = build_fixed(n, heads, d, dtype, levels, budget, flags, out, w);
+    if (last == CQSA_OK) return CQSA_OK;
+    last_why = w;
+    if (last == CQSA_EDIVIDE && k == 1) {
+      why = w;
+      return last;
+    }
+    if (last == CQSA_EDIVIDE) {
+      why = "no level count fits the budget before N stops dividing (" + w + ")";
+      return CQSA_EBUDGET;
+    }
+    if (last != CQSA_EBUDGET) break;
+  }
+  why = last_why;
+  return last;
+}
+
+}  // namespace cqsa

@@ -1,0 +1,99 @@
+// Host CQS planner: difference sets, task construction over levels, the CQS Mask,
+// coverage table, canonical schedule record, kernel descriptor tables and the
+// device-memory footprint model.  Pure C++17, no HIP dependency.
+#pragma once
+
+#include <cstdint>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/cqsa.h"
+#include "descriptors.hpp"
+
+namespace cqsa {
+
+struct Error {
+  cqsa_status status;
+  std::string msg;
+};
+
+// Lexicographically smallest perfect difference set with {0,1} (l >= 2) or {0} (l = 1).
+cqsa_status difference_set(int l, std::vector<int>& out, std::string& why);
+
+struct Segment {     // a globally contiguous piece of a task's token list
+  int64_t global_start, length, local_offset;  // tokens
+};
+
+struct UnitRun {     // admitted keys of one query unit, task-local units
+  int32_t start, count;
+};
+
+struct Task {
+  int64_t tid = 0;
+  std::vector<int> ids;                 // per-level subsequence index
+  std::vector<int64_t> units;           // global unit of each local unit
+  std::vector<Segment> segments;
+  std::vector<std::vector<UnitRun>> runs;  // per local query unit
+  std::vector<int32_t> slot;            // visit ordinal of this task for each local unit
+  int64_t admitted_units = 0;           // admitted (query unit, key unit) pairs
+};
+
+struct Footprint {
+  bool acc_on_device;
+  int kv_buffers;
+  int64_t bytes;
+};
+
+struct Plan {
+  int64_t n = 0;
+  int heads = 0, d = 0;
+  cqsa_dtype dtype = CQSA_BF16;
+  std::vector<int> ls, cs;
+  std::vector<std::vector<int>> sets;
+  int64_t unit = 0, n_units = 0, visits = 0, task_units = 0;
+  int64_t budget = 0;
+  uint32_t flags = 0;
+  std::vector<Task> tasks;
+
+  std::vector<int64_t> schedule;        // canonical record
+  std::vector<int32_t> coverage;        // [U*U]
+
+  // kernel descriptors
+  std::vector<WorkItem> dev_items;      // all (task, unit) items, global coordinates
+  std::vector<KeyRun> dev_runs;
+  std::vector<WorkItem> stream_items;   // item (t, a) at index t*task_units + a, block coordinates
+  std::vector<KeyRun> stream_runs;
+
+  Footprint stream_fp{};
+  int64_t device_ws = 0;                // slots bytes of the device-resident path
+  int64_t host_acc_bytes = 0;
+
+  // device copies of the descriptor tables, uploaded lazily per device
+  mutable std::mutex dev_mu;
+  mutable std::vector<std::pair<int, void*>> dev_tables;  // (device, allocation)
+
+  int64_t elem_bytes() const { return dtype == CQSA_BF16 ? 2 : 4; }
+  int64_t row_in_bytes() const { return int64_t(heads) * d * elem_bytes(); }
+  int64_t row_part_bytes() const { return int64_t(heads) * (d + 2) * 4; }
+  int64_t row_out_bytes() const { return int64_t(heads) * (d * elem_bytes() + 4); }
+  int64_t task_tokens() const { return task_units * unit; }
+};
+
+// Byte size of each piece of the streamed path's workspace, in the order it is carved.
+struct StreamLayout {
+  int64_t kv_stage;     // one K or V staging buffer (task_tokens rows)
+  int64_t q_blk, n_blk, ml_blk, o_blk, lse_blk;  // per ring slot (unit rows)
+  int64_t acc_n, acc_ml; // device accumulator (0 when on host)
+  int64_t total;
+};
+StreamLayout stream_layout(const Plan& p, bool acc_on_device, int kv_buffers);
+
+constexpr int64_t kAlign = 256;
+inline int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Build a plan; on failure returns the status and fills why.
+cqsa_status build_plan(int64_t n, int heads, int d, cqsa_dtype dtype, const int32_t* ls,
+                       int n_levels, int64_t budget, uint32_t flags, Plan& out, std::string& why);
+
+}  // namespace cqsa

@@ -1,0 +1,181 @@
+"""CPU tests of the C ABI: exported symbols, the host planner against the oracle
+planner (bit-exact schedule and coverage), the footprint model and error paths.
+No call here touches a GPU.
+"""
+import os
+import re
+
+import numpy as np
+import pytest
+
+from memory_bounded_streaming_amd import cqsa
+from oracle.plan import difference_set, make_plan
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GiB = 1 << 30
+
+CONFIGS = {  # name: (N, H, d, dtype, levels, budget)
+    "C1": (3584, 1, 64, cqsa.CQSA_F32, [3], 0),
+    "C2": (57344, 8, 128, cqsa.CQSA_BF16, [3], 0),
+    "C3": (212992, 16, 128, cqsa.CQSA_BF16, [4], 16 * GiB),
+    "C4": (1376256, 8, 128, cqsa.CQSA_BF16, [5], 8 * GiB),
+    "C5": (12845056, 1, 128, cqsa.CQSA_BF16, [3, 3], 2 * GiB),
+}
+
+
+def _header_symbols():
+    text = open(os.path.join(ROOT, "include", "cqsa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cqsa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = _header_symbols()
+    assert len(names) == 13
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(cqsa.EXPORTS)
+
+
+def test_difference_sets_match_oracle(lib):
+    for l in range(1, 11):
+        if l == 7:
+            with pytest.raises(cqsa.CqsaError) as e:
+                cqsa.cqsa_difference_set(7)
+            assert e.value.status == -2
+            continue
+        assert cqsa.cqsa_difference_set(l) == difference_set(l)
+    for bad in (0, 11, -3):
+        with pytest.raises(cqsa.CqsaError) as e:
+            cqsa.cqsa_difference_set(bad)
+        assert e.value.status == -1
+
+
+SMALL_PLANS = [([1], 1), ([1], 37), ([2], 3), ([3], 7), ([3], 21), ([4], 13), ([5], 42), ([6], 31),
+               ([2, 2], 9), ([3, 2], 21), ([2, 3], 42), ([3, 3], 49), ([4, 2], 39), ([2, 2, 2], 27)]
+
+
+@pytest.mark.parametrize("levels,n", SMALL_PLANS + [(v[4], v[0]) for v in CONFIGS.values()])
+def test_schedule_and_coverage_bit_exact(levels, n):
+    ref = make_plan(n, levels)
+    with cqsa.Plan(n, 2, 64, cqsa.CQSA_BF16, levels) as p:
+        sched = p.schedule()
+        want = ref.serialize()
+        assert sched.dtype == np.int64 and sched.shape == want.shape
+        assert sched.tobytes() == want.tobytes()
+        cov = p.coverage()
+        assert cov.tobytes() == ref.coverage().tobytes()
+        assert (cov >= 0).all()
+        info = p.info
+        assert info["levels"] == len(levels) and info["l"] == levels
+        assert info["c"] == ref.cs
+        assert info["n_tasks"] == len(ref.tasks)
+        assert info["unit_tokens"] == ref.unit_tokens and info["visits"] == int(np.prod(levels))
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_footprint_fits_budget(name):
+    n, h, d, dt, levels, budget = CONFIGS[name]
+    with cqsa.Plan(n, h, d, dt, levels, budget_bytes=budget) as p:
+        info = p.info
+        e = 2 if dt == cqsa.CQSA_BF16 else 4
+        if budget:
+            assert info["stream_workspace_bytes"] <= budget
+        assert p.workspace_size(cqsa.CQSA_RES_HOST_PINNED) == info["stream_workspace_bytes"]
+        # device-resident slots: V partial triples per (row, head)
+        assert info["device_workspace_bytes"] >= info["visits"] * n * h * (d + 2) * 4
+        assert info["useful_flop"] == pytest.approx(4.0 * n * n * d * h)
+        # the K/V staging alone: kv_buffers x (K + V) x task tokens
+        assert info["stream_workspace_bytes"] >= info["kv_buffers"] * 2 * info["task_tokens"] * h * d * e
+    modes = {"C1": 1, "C2": 1, "C3": 1, "C4": 2, "C5": 4}
+    assert info["stream_mode"] == modes[name]
+
+
+def test_c4_device_accumulator_does_not_fit_8gib():
+    # a device accumulator for all N rows (5.33 GiB) + the K/V double buffer (2.5 GiB) + the
+    # two-slot query ring exceeds 8 GiB, so the accumulator moves to pinned host memory
+    n, h, d = 1376256, 8, 128
+    acc = n * h * (d + 2) * 4
+    kv2 = 2 * 2 * 5 * 65536 * h * d * 2
+    ring = 2 * 65536 * h * (d * 2 + (d + 2) * 4 + d * 2 + 4)
+    assert acc + kv2 + ring > 8 * GiB
+    with cqsa.Plan(n, h, d, cqsa.CQSA_BF16, [5]) as p:
+        assert p.info["stream_mode"] == 1 and p.info["stream_workspace_bytes"] > 8 * GiB
+    with cqsa.Plan(n, h, d, cqsa.CQSA_BF16, [5], budget_bytes=8 * GiB) as p:
+        assert p.info["host_acc_bytes"] == n * h * (d + 2) * 4
+
+
+def test_auto_levels_follow_the_budget():
+    with cqsa.Plan(12845056, 1, 128, cqsa.CQSA_BF16, [3], n_levels=0, budget_bytes=2 * GiB) as p:
+        assert p.info["levels"] == 2 and p.info["l"] == [3, 3]
+    with cqsa.Plan(12845056, 1, 128, cqsa.CQSA_BF16, [3], n_levels=0, budget_bytes=64 * GiB) as p:
+        assert p.info["levels"] == 1
+    with pytest.raises(cqsa.CqsaError) as e:  # a third level would not divide
+        cqsa.Plan(12845056, 1, 128, cqsa.CQSA_BF16, [3], n_levels=0, budget_bytes=256 << 20)
+    assert e.value.status == -4
+
+
+def test_forced_modes():
+    n = 13 * 64
+    for flags, mode in ((0, 1), (cqsa.CQSA_FLAG_HOST_ACC, 2), (cqsa.CQSA_FLAG_KV_SINGLE, 3),
+                        (cqsa.CQSA_FLAG_HOST_ACC | cqsa.CQSA_FLAG_KV_SINGLE, 4)):
+        with cqsa.Plan(n, 2, 64, cqsa.CQSA_BF16, [4], flags=flags) as p:
+            assert p.info["stream_mode"] == mode
+            assert p.info["kv_buffers"] == (1 if mode in (3, 4) else 2)
+            assert (p.info["host_acc_bytes"] > 0) == (mode in (2, 4))
+
+
+def test_budget_selects_modes_in_order():
+    n, h, d = 13 * 256, 2, 64
+    sizes = {}
+    for flags in (0, 1, 2, 3):
+        with cqsa.Plan(n, h, d, cqsa.CQSA_BF16, [4], flags=flags) as p:
+            sizes[p.info["stream_mode"]] = p.info["stream_workspace_bytes"]
+    for mode, size in sizes.items():
+        with cqsa.Plan(n, h, d, cqsa.CQSA_BF16, [4], budget_bytes=size + 65536) as p:
+            chosen = p.info["stream_mode"]
+            assert sizes[chosen] <= size + 65536
+            assert chosen <= mode or sizes[chosen] <= sizes[mode]
+    with pytest.raises(cqsa.CqsaError) as e:
+        cqsa.Plan(n, h, d, cqsa.CQSA_BF16, [4], budget_bytes=min(sizes.values()) // 2)
+    assert e.value.status == -4
+
+
+@pytest.mark.parametrize("args,status", [
+    ((100, 1, 64, cqsa.CQSA_BF16, [3]), -3),        # 100 is not a multiple of 7
+    ((43, 1, 64, cqsa.CQSA_BF16, [7]), -2),         # no difference set
+    ((49, 1, 96, cqsa.CQSA_BF16, [3]), -1),         # unsupported head_dim
+    ((49, 0, 64, cqsa.CQSA_BF16, [3]), -1),         # no heads
+    ((0, 1, 64, cqsa.CQSA_BF16, [3]), -1),          # no tokens
+    ((49, 1, 64, 7, [3]), -1),                      # unknown dtype
+    ((49, 1, 64, cqsa.CQSA_BF16, [11]), -1),        # l out of range
+    ((7 ** 4, 1, 64, cqsa.CQSA_BF16, [3] * 9), -1),  # more than 8 levels
+])
+def test_plan_errors(args, status):
+    with pytest.raises(cqsa.CqsaError) as e:
+        cqsa.cqsa_plan_create(*args)
+    assert e.value.status == status
+    assert cqsa.cqsa_last_error()
+
+
+def test_bad_flags_and_null_arguments(lib):
+    with pytest.raises(cqsa.CqsaError) as e:
+        cqsa.cqsa_plan_create(49, 1, 64, cqsa.CQSA_BF16, [3], flags=0x10)
+    assert e.value.status == -1
+    import ctypes
+    assert lib.cqsa_plan_create(49, 1, 64, 0, None, 1, 0, 0, ctypes.byref(ctypes.c_void_p())) == -1
+    assert lib.cqsa_plan_info_get(None, None) == -1
+    assert lib.cqsa_forward(None, None, None, None, None, None, 0, None, 0, None, None) == -1
+    with cqsa.Plan(49, 1, 64, cqsa.CQSA_BF16, [3]) as p:
+        needed = ctypes.c_int64()
+        small = np.zeros(3, np.int64)
+        assert lib.cqsa_plan_schedule(p.handle, small.ctypes.data, 3, ctypes.byref(needed)) == -7
+        assert needed.value > 3
+        assert lib.cqsa_forward(p.handle, 1, 1, 1, 1, None, 5, None, 0, None, None) == -1
+    lib.cqsa_plan_destroy(None)
+
+
+def test_status_strings(lib):
+    for s in (0, -1, -2, -3, -4, -5, -6, -7):
+        assert cqsa.cqsa_status_string(s)
+    assert "unknown" in cqsa.cqsa_status_string(42)
