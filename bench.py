@@ -1,0 +1,247 @@
+"""Benchmark of the CQS attention forward on one MI355X.
+
+A step is one pass of the whole hot path over the workload: the masked attention
+partials of every CQS task followed by the merge into O and LSE.  The default
+workload is N=57344 tokens, 8 heads, d=128, bf16, CQS l=3 (7 chunks of 8192),
+Q/K/V resident in HBM (inputs are resident before the timed region starts).
+
+Prints one JSON line: useful attention TFLOP/s (4 N^2 d H per step), the fraction
+of the bf16 dense MFMA peak, the roofline of the partial kernel (its average launch
+duration measured with HIP events on the stream it runs on), the fp64 oracle timed
+on a bounded sample of host cores, and the host-pinned streamed run of the
+N=212992, 16-head workload under a 16 GiB budget (PCIe-inclusive, reported beside
+the value, never as it).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0
+METRIC = "useful attention TFLOP/s + % bf16 MFMA peak, CQS-streamed fwd at fixed mem budget"
+GiB = 1 << 30
+
+WORKLOADS = {
+    # name: (N, H, d, levels, budget, residency description)
+    "c2": (57344, 8, 128, [3], 0, "device"),
+    "c3": (212992, 16, 128, [4], 16 * GiB, "host_pinned"),
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    path = os.path.join(ROOT, "memory_bounded_streaming_amd", "csrc", "kernels.hip")
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel_hash, units_per_launch):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it matches this kernel."""
+    path = os.path.join(ROOT, "profiles", "attn_partial_c2_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256_16") != kernel_hash:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(rows_wanted=1024):
+    """The fp64 oracle on a bounded sample of the C2 workload (all keys, sampled query rows)."""
+    from memory_bounded_streaming_amd.inputs import gen_qkv, sample_rows
+    from oracle.attention import attention_fp64
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    n, h, d = 57344, 8, 128
+    q, k, v = gen_qkv(0, n, h, d, "bf16")
+    rows = sample_rows(n, rows_wanted, 0)
+    t0 = time.perf_counter()
+    attention_fp64(q, k, v, rows=rows, dtype="bf16")
+    dt = time.perf_counter() - t0
+    flop = 4.0 * rows.size * n * d * h
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{rows.size} sampled query rows x {h} heads of the N={n}, d={d} workload against all "
+                      f"{n} keys, fp64 two-pass softmax; {dt:.1f} s wall; rate = 4*rows*N*d*H / time"}
+
+
+def run_device(args, torch, cqsa):
+    from memory_bounded_streaming_amd.inputs import gen_qkv
+    n, h, d, levels, _, _ = WORKLOADS["c2"]
+    q, k, v = gen_qkv(args.seed, n, h, d, "bf16")
+    dev = [torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda() for x in (q, k, v)]
+    plan = cqsa.Plan(n, h, d, cqsa.CQSA_BF16, levels)
+    V = plan.info["visits"]
+    ws_n = torch.empty((V, n, h, d), dtype=torch.float32, device="cuda")
+    ws_ml = torch.empty((V, n, h, 2), dtype=torch.float32, device="cuda")
+    o = torch.empty((n, h, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((h, n), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        plan.partials(*dev, ws_n, ws_ml, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        plan.merge(ws_n, ws_ml, o, lse, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    attn_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    merge_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    flop = plan.info["useful_flop"]
+    ms = total_ms / args.steps
+    attn_avg = float(np.mean(attn_ms))
+    merge_avg = float(np.mean(merge_ms))
+    merge_bytes = n * h * ((d + 2) * 4 * V + d * 2 + 4)  # read V partial triples, write O (bf16) + LSE
+    out = {
+        "plan": plan.info,
+        "ms_per_step": ms,
+        "value": flop / (ms / 1e3) / 1e12,
+        "attn_ms": attn_avg,
+        "attn_tflops": flop / (attn_avg / 1e3) / 1e12,
+        "merge_ms": merge_avg,
+        "merge_gbs": merge_bytes / (merge_avg / 1e3) / 1e9,
+        "merge_bytes": merge_bytes,
+    }
+    plan.close()
+    return out
+
+
+def run_streamed(args, torch, cqsa):
+    from memory_bounded_streaming_amd.inputs import gen_tensor
+    n, h, d, levels, budget, _ = WORKLOADS["c3"]
+    ts = []
+    for i in range(3):
+        t = torch.empty((n, h, d), dtype=torch.int16, pin_memory=True)
+        gen_tensor(args.seed, i, n, h, d, "bf16", out=t.numpy().view(np.uint16))
+        ts.append(t)
+    o = torch.empty((n, h, d), dtype=torch.int16, pin_memory=True)
+    lse = torch.empty((h, n), dtype=torch.float32, pin_memory=True)
+    with cqsa.Plan(n, h, d, cqsa.CQSA_BF16, levels, budget_bytes=budget) as plan:
+        ws = torch.empty(plan.workspace_size(cqsa.CQSA_RES_HOST_PINNED), dtype=torch.uint8, device="cuda")
+        plan.forward(*ts, o, lse, residency=cqsa.CQSA_RES_HOST_PINNED, workspace=ws)  # warm-up
+        t0 = time.perf_counter()
+        st = plan.forward(*ts, o, lse, residency=cqsa.CQSA_RES_HOST_PINNED, workspace=ws, stats=True)
+        wall = time.perf_counter() - t0
+        flop = plan.info["useful_flop"]
+        return {
+            "workload": f"N={n}, H={h}, d={d}, bf16, CQS l={levels[0]} (c=13), Q/K/V in pinned host memory, "
+                        f"device budget {budget // GiB} GiB",
+            "mode": cqsa.MODE_NAMES[plan.info["stream_mode"]],
+            "tflops_pcie_inclusive": flop / wall / 1e12,
+            "wall_s": wall,
+            "attn_tflops": flop / (st["t_attn_ms"] / 1e3) / 1e12,
+            "h2d_gbs": st["bytes_h2d"] / (st["t_h2d_ms"] / 1e3) / 1e9 if st["t_h2d_ms"] else None,
+            "d2h_gbs": st["bytes_d2h"] / (st["t_d2h_ms"] / 1e3) / 1e9 if st["t_d2h_ms"] else None,
+            "bytes_h2d": st["bytes_h2d"],
+            "bytes_d2h": st["bytes_d2h"],
+            "peak_device_bytes": st["peak_device_bytes"],
+            "budget_bytes": budget,
+        }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-streamed", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=1024)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from memory_bounded_streaming_amd import cqsa
+    cqsa.load()
+    torch.cuda.set_device(0)
+
+    log("bench: device-resident workload")
+    dres = run_device(args, torch, cqsa)
+    log(f"bench: {dres['value']:.1f} TFLOP/s end-to-end, partial kernel {dres['attn_tflops']:.1f} TFLOP/s")
+    stream_res = None
+    if not args.no_streamed:
+        log("bench: host-pinned streamed workload")
+        stream_res = run_streamed(args, torch, cqsa)
+        log(f"bench: streamed {stream_res['tflops_pcie_inclusive']:.1f} TFLOP/s PCIe-inclusive")
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: oracle cpu baseline")
+        cpu = cpu_baseline(args.cpu_rows)
+
+    n, h, d, levels, _, _ = WORKLOADS["c2"]
+    flop = dres["plan"]["useful_flop"]
+    khash = kernel_source_hash()
+    traffic = measured_traffic(khash, 1)
+    line = {
+        "metric": METRIC,
+        "value": round(dres["value"], 3),
+        "unit": "TFLOP/s",
+        "pct_bf16_mfma_peak": round(100.0 * dres["value"] / BF16_MFMA_PEAK_TFLOPS, 3),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dres["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: Q/K/V i.i.d. N(0,1) rounded to bf16, seed %d" % args.seed,
+        "config": {"workload": f"N={n} tokens, {h} heads, d={d}, bf16, non-causal, CQS l={levels[0]} "
+                               f"(c=7 chunks of 8192), Q/K/V device-resident",
+                   "n_tokens": n, "heads": h, "head_dim": d, "levels": levels, "residency": "device"},
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "attn_partial_bf16<128>",
+            "achieved": round(dres["attn_tflops"], 3),
+            "peak": BF16_MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(dres["attn_tflops"] / BF16_MFMA_PEAK_TFLOPS, 4),
+            "traffic": traffic,
+            "flop_per_launch": flop,
+            "avg_launch_ms": round(dres["attn_ms"], 4),
+        },
+        "merge": {"bound": "hbm", "achieved": round(dres["merge_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                  "frac": round(dres["merge_gbs"] / HBM_PEAK_GBS, 4), "bytes_per_launch": dres["merge_bytes"],
+                  "avg_launch_ms": round(dres["merge_ms"], 4)},
+        "streamed": stream_res,
+        "cpu_baseline": cpu,
+        "kernel_source_sha256_16": khash,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

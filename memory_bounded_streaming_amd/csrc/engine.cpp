@@ -16,8 +16,11 @@
 // staging buffer or ring slot.
 #include "engine.hpp"
 
+#include <algorithm>
 #include <chrono>
 #include <cmath>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <vector>
 
@@ -332,8 +335,9 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
   }
   for (auto& s : R.s) HIP_TRY(hipStreamCreateWithFlags(&s, hipStreamNonBlocking));
   hipStream_t s_kv = R.s[0], s_q = R.s[1], s_c = R.s[2], s_d = R.s[3];
-  hipEvent_t start, kv_ready[2], kv_free[2], q_ready[2], c_done[2], slot_free[2];
+  hipEvent_t start, kv_ready[2], kv_free[2], q_ready[2], c_done[2], slot_free[2], task_done[3];
   HIP_TRY(R.event(start));
+  for (int i = 0; i < 3; ++i) HIP_TRY(R.event(task_done[i]));
   for (int i = 0; i < 2; ++i) {
     HIP_TRY(R.event(kv_ready[i]));
     HIP_TRY(R.event(kv_free[i]));
@@ -354,9 +358,22 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
   std::vector<int64_t> last_block(p.n_units, -4);  // ring block that last wrote a unit's host accumulator
   int64_t blk = 0;
 
+  const bool progress = std::getenv("CQSA_PROGRESS") != nullptr;
+  const int64_t n_tasks = static_cast<int64_t>(p.tasks.size());
+  auto report = [&](int64_t done) {
+    const double s = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
+    std::fprintf(stderr, "cqsa: task %lld/%lld done, %.1f s\n", static_cast<long long>(done + 1),
+                 static_cast<long long>(n_tasks), s);
+    std::fflush(stderr);
+  };
   for (size_t ti = 0; ti < p.tasks.size(); ++ti) {
     const Task& task = p.tasks[ti];
     const int b = static_cast<int>(ti % fp.kv_buffers);
+    // keep the host at most two tasks ahead of the GPU
+    if (ti >= 2) {
+      HIP_TRY(hipEventSynchronize(task_done[(ti - 2) % 3]));
+      if (progress) report(static_cast<int64_t>(ti) - 2);
+    }
     if (static_cast<int64_t>(ti) >= fp.kv_buffers) HIP_TRY(hipStreamWaitEvent(s_kv, kv_free[b], 0));
     HIP_TRY(tm.begin(PH_H2D, s_kv, tev));
     for (const Segment& g : task.segments) {
@@ -494,8 +511,11 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
       HIP_TRY(tm.end(PH_D2H, s_d));
       HIP_TRY(hipEventRecord(slot_free[j], s_d));
     }
+    HIP_TRY(hipEventRecord(task_done[ti % 3], s_c));
   }
   for (hipStream_t s : R.s) HIP_TRY(hipStreamSynchronize(s));
+  if (progress)
+    for (int64_t t = std::max<int64_t>(0, n_tasks - 2); t < n_tasks; ++t) report(t);
   HIP_TRY(hipGetLastError());
   if (stats) {
     std::memset(stats, 0, sizeof(*stats));

@@ -1,0 +1,64 @@
+"""Helpers for the GPU tests: moving seeded inputs into device or pinned host memory
+and reading results back (torch is used for memory only)."""
+import numpy as np
+
+from memory_bounded_streaming_amd import cqsa
+from memory_bounded_streaming_amd.inputs import bf16_bits_to_f32, gen_tensor
+
+DT = {"bf16": cqsa.CQSA_BF16, "f32": cqsa.CQSA_F32}
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def to_device(arr, dtype):
+    torch = torch_mod()
+    arr = np.ascontiguousarray(arr)
+    if dtype == "bf16":
+        return torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(arr).cuda()
+
+
+def empty_device(shape, dtype):
+    torch = torch_mod()
+    return torch.empty(shape, dtype=torch.bfloat16 if dtype == "bf16" else torch.float32, device="cuda")
+
+
+def to_numpy(t, dtype):
+    torch = torch_mod()
+    if dtype == "bf16":
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def as_f64(arr, dtype):
+    if dtype == "bf16":
+        return bf16_bits_to_f32(arr).astype(np.float64)
+    return np.asarray(arr, dtype=np.float64)
+
+
+def pinned(shape, dtype):
+    """A pinned host tensor and a numpy view of it (uint16 bits for bf16)."""
+    torch = torch_mod()
+    if dtype == "bf16":
+        t = torch.empty(shape, dtype=torch.int16, pin_memory=True)
+        return t, t.numpy().view(np.uint16)
+    t = torch.empty(shape, dtype=torch.float32, pin_memory=True)
+    return t, t.numpy()
+
+
+def pinned_qkv(seed, n, h, d, dtype):
+    """Q, K, V drawn straight into pinned host memory: ((tq, tk, tv), (q, k, v) numpy views)."""
+    ts, views = [], []
+    for i in range(3):
+        t, a = pinned((n, h, d), dtype)
+        gen_tensor(seed, i, n, h, d, dtype, out=a)
+        ts.append(t)
+        views.append(a)
+    return tuple(ts), tuple(views)
+
+
+def log(msg):
+    print(msg, flush=True)

@@ -1,0 +1,95 @@
+"""GPU tests of the host-pinned stream engine (needs an MI355X).
+
+Inputs live in pinned host memory; tasks stream through device staging under the
+plan's budget.  Each staging mode is forced in turn; the streamed output must equal
+the device-resident output bit for bit (same key tiles, same merge order) and match
+the fp64 oracle within tolerance.
+"""
+import numpy as np
+import pytest
+
+from memory_bounded_streaming_amd import cqsa
+from memory_bounded_streaming_amd.inputs import gen_qkv
+from oracle.attention import attention_fp64
+from oracle.tolerance import BF16_REL_TOL, F32_ABS_TOL, max_abs_err, rowwise_rel_err
+
+from gpu_util import DT, as_f64, empty_device, log, pinned, to_device, to_numpy
+
+pytestmark = pytest.mark.gpu
+
+MODES = [0, cqsa.CQSA_FLAG_HOST_ACC, cqsa.CQSA_FLAG_KV_SINGLE, cqsa.CQSA_FLAG_HOST_ACC | cqsa.CQSA_FLAG_KV_SINGLE]
+
+CASES = [  # levels, unit, heads, d, dtype
+    ([4], 256, 2, 128, "bf16"),
+    ([3, 2], 40, 2, 64, "bf16"),
+    ([2, 2], 100, 1, 128, "bf16"),
+    ([3], 96, 2, 64, "f32"),
+    ([1], 500, 1, 128, "bf16"),
+]
+
+
+def _device_forward(p, q, k, v, n, h, d, dtype):
+    import torch
+    o = empty_device((n, h, d), dtype)
+    lse = torch.empty((h, n), device="cuda")
+    p.forward(to_device(q, dtype), to_device(k, dtype), to_device(v, dtype), o, lse)
+    torch.cuda.synchronize()
+    return to_numpy(o, dtype), lse.cpu().numpy()
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"l{'x'.join(map(str, c[0]))}-u{c[1]}-h{c[2]}-d{c[3]}-{c[4]}")
+@pytest.mark.parametrize("flags", MODES, ids=["devacc-kv2", "hostacc-kv2", "devacc-kv1", "hostacc-kv1"])
+def test_stream_modes_equal_device_path(case, flags):
+    torch = pytest.importorskip("torch")
+    levels, u, h, d, dtype = case
+    n = int(np.prod([l * (l - 1) + 1 for l in levels])) * u
+    log(f"stream {levels} u={u} h={h} d={d} {dtype} flags={flags}")
+    q, k, v = gen_qkv(41 + n, n, h, d, dtype)
+    with cqsa.Plan(n, h, d, DT[dtype], levels, flags=flags) as p:
+        o_dev, lse_dev = _device_forward(p, q, k, v, n, h, d, dtype)
+        tq, qa = pinned((n, h, d), dtype)
+        tk, ka = pinned((n, h, d), dtype)
+        tv, va = pinned((n, h, d), dtype)
+        qa[...], ka[...], va[...] = q, k, v
+        to, oa = pinned((n, h, d), dtype)
+        tl = torch.empty((h, n), dtype=torch.float32, pin_memory=True)
+        st = p.forward(tq, tk, tv, to, tl, residency=cqsa.CQSA_RES_HOST_PINNED, stats=True)
+        assert st["peak_device_bytes"] >= p.info["stream_workspace_bytes"]
+        e = 2 if dtype == "bf16" else 4
+        visits = int(np.prod(levels))
+        assert st["bytes_h2d"] >= 3 * visits * n * h * d * e
+        assert np.array_equal(oa, o_dev), "streamed output equals the device-resident output bit for bit"
+        assert np.array_equal(tl.numpy(), lse_dev)
+    o_ref, _ = attention_fp64(q, k, v, dtype=dtype)
+    out = as_f64(oa, dtype)
+    if dtype == "f32":
+        assert max_abs_err(out, o_ref) <= F32_ABS_TOL
+    else:
+        assert rowwise_rel_err(out, o_ref) <= BF16_REL_TOL
+
+
+def test_stream_respects_budget_and_reports_phases():
+    torch = pytest.importorskip("torch")
+    n, h, d = 13 * 512, 4, 128
+    q, k, v = gen_qkv(7, n, h, d, "bf16")
+    with cqsa.Plan(n, h, d, cqsa.CQSA_BF16, [4]) as probe:
+        need = probe.workspace_size(cqsa.CQSA_RES_HOST_PINNED)
+    budget = need // 2 + (64 << 20)
+    with cqsa.Plan(n, h, d, cqsa.CQSA_BF16, [4], budget_bytes=budget) as p:
+        assert p.info["stream_workspace_bytes"] <= budget
+        tq, qa = pinned((n, h, d), "bf16")
+        tk, ka = pinned((n, h, d), "bf16")
+        tv, va = pinned((n, h, d), "bf16")
+        qa[...], ka[...], va[...] = q, k, v
+        to, oa = pinned((n, h, d), "bf16")
+        free0, _ = torch.cuda.mem_get_info()
+        st = p.forward(tq, tk, tv, to, None, residency=cqsa.CQSA_RES_HOST_PINNED, stats=True)
+        assert st["peak_device_bytes"] <= budget
+        assert st["n_attn_launches"] == 13 * 4
+        for key in ("t_h2d_ms", "t_attn_ms", "t_merge_ms", "t_d2h_ms"):
+            assert st[key] > 0.0, key
+        free1, _ = torch.cuda.mem_get_info()
+        assert abs(free1 - free0) < (64 << 20), "the call frees its workspace"
+    rows = np.arange(0, n, 37)
+    o_ref, _ = attention_fp64(q, k, v, rows=rows, dtype="bf16")
+    assert rowwise_rel_err(as_f64(oa[rows], "bf16"), o_ref) <= BF16_REL_TOL
