@@ -50,8 +50,8 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t grid) {
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
 // ---------------------------------------------------------------------------------
-// bf16 partials on MFMA.  Workgroup = 4 wave64 = 128 query rows (32 per wave); the
-// key loop walks the item's admitted runs in tiles of 64 keys staged in LDS.
+// bf16 partials on MFMA.  Workgroup = 8 wave64 = 256 query rows (32 per wave); all
+// eight waves share each 64-key K/V tile, so a tile fetched from L2 feeds 256 queries.
 //
 // S^T (keys x queries) = K_tile * Q^T with v_mfma_f32_32x32x16_bf16: A = 32 key rows
 // read from LDS, B = this lane's query slice held in registers.  Each lane then owns
@@ -59,21 +59,57 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast
 // statistics are lane-local plus one exchange with lane^32.  The K rows of an MFMA
 // tile are read in an order that swaps bits 2 and 3 of the row index; with that order
 // the 16 accumulator values a lane holds are exactly the B operand (8 consecutive
-// keys per half-wave) of O^T += V^T * P^T, so P never leaves registers.  V is
-// transposed on its way into LDS (dim-major) so the A operand of that product is one
-// 16-byte LDS read per lane.
+// keys per half-wave) of O^T += V^T * P^T, so P never leaves registers.  V stays
+// row-major in LDS and the A operand of that product (8 consecutive keys of one dim
+// per lane) is fetched with two LDS transpose reads (ds_read_b64_tr_b16).
+//
+// Pipeline: the next tile is fetched from global memory into registers while the
+// current one is computed from LDS, then written to the other LDS stage; one barrier
+// per tile.  The running max is rescaled lazily: the reference max only moves when a
+// score exceeds it by more than 2^8, so every exponent stays <= 2^8 and the triple
+// (m, l, n) remains exact for whatever m it carries.
 // ---------------------------------------------------------------------------------
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+constexpr float kLazyRescale = 8.0f;  // log2 units
+
 template <int D>
-__global__ __launch_bounds__(256) void attn_partial_bf16(AttnParams P) {
-  constexpr int QT = 128;
-  constexpr int KT = 64;
-  constexpr int KSTR = D + 8;   // u16 per K row in LDS (16-byte pad)
-  constexpr int VSTR = KT + 8;  // u16 per V^T row in LDS
-  constexpr int NKK = D / 16;   // k-steps of Q K^T
-  constexpr int NDT = D / 32;   // 32-dim output tiles
-  constexpr int DCH = D / 8;    // 16-byte chunks per row
-  __shared__ __attribute__((aligned(16))) u16 ks[KT * KSTR];
-  __shared__ __attribute__((aligned(16))) u16 vt[D * VSTR];
+struct Bf16Tile {
+  static constexpr int NW = 8;          // waves per workgroup
+  static constexpr int NT = 64 * NW;    // threads
+  static constexpr int QT = 32 * NW;    // query rows per workgroup
+  static constexpr int KT = 64;         // keys per tile
+  static constexpr int KSTR = D + 8;    // K row stride in LDS (u16): 16-byte pad
+  static constexpr int VSTR = D + 32;   // V row stride in LDS (u16): rows 16 dwords apart mod 64 banks
+  static constexpr int DCH = D / 8;     // 16-byte chunks per row
+  static constexpr int CPT = KT * DCH / NT;  // chunks of K (and of V) per thread per tile
+  static constexpr int KBYTES = KT * KSTR * 2;
+  static constexpr int VBYTES = KT * VSTR * 2;
+  static constexpr int STAGE = KBYTES + VBYTES;
+  static_assert(CPT >= 1 && KT * DCH == CPT * NT, "tile split");
+};
+
+// Cursor over the tiles of an item's key runs.
+struct TileCursor {
+  int run;   // index of the current run
+  int k0;    // first key of the tile within the run
+};
+
+__device__ __forceinline__ void cursor_next(TileCursor& c, const KeyRun* runs, int nrun, int kt) {
+  c.k0 += kt;
+  if (c.run < nrun && c.k0 >= runs[c.run].len) {
+    ++c.run;
+    c.k0 = 0;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(512) void attn_partial_bf16(AttnParams P) {
+  using T = Bf16Tile<D>;
+  constexpr int NKK = D / 16;
+  constexpr int NDT = D / 32;
+  __shared__ __attribute__((aligned(16))) char smem[2 * T::STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -83,12 +119,14 @@ __global__ __launch_bounds__(256) void attn_partial_bf16(AttnParams P) {
   const int64_t rest = b / P.tiles_per_item;
   const int head = static_cast<int>(rest % P.heads);
   const WorkItem it = P.items[rest / P.heads];
+  const KeyRun* runs = P.runs + it.run0;
+  const int nrun = it.nrun;
   const int64_t rs = static_cast<int64_t>(P.heads) * D;
   const u16* __restrict__ Q = static_cast<const u16*>(P.q);
-  const u16* __restrict__ K = static_cast<const u16*>(P.k);
-  const u16* __restrict__ V = static_cast<const u16*>(P.v);
+  const u16* __restrict__ K = static_cast<const u16*>(P.k) + head * D;
+  const u16* __restrict__ V = static_cast<const u16*>(P.v) + head * D;
 
-  const int qi = tile * QT + wave * 32 + col;
+  const int qi = tile * T::QT + wave * 32 + col;
   const bool qok = qi < it.q_len;
   bf16x8 qf[NKK];
   {
@@ -101,6 +139,36 @@ __global__ __launch_bounds__(256) void attn_partial_bf16(AttnParams P) {
     }
   }
 
+  // global -> register fetch of one tile (rows past the run end read as zero)
+  uint4 kr[T::CPT], vr[T::CPT];
+  auto fetch = [&](const TileCursor& c) {
+    const int64_t start = runs[c.run].start + c.k0;
+    const int nv = min(T::KT, runs[c.run].len - c.k0);
+#pragma unroll
+    for (int i = 0; i < T::CPT; ++i) {
+      const int ch = tid + i * T::NT;
+      const int row = ch / T::DCH, cc = ch % T::DCH;
+      kr[i] = make_uint4(0, 0, 0, 0);
+      vr[i] = make_uint4(0, 0, 0, 0);
+      if (row < nv) {
+        const int64_t off = (start + row) * rs + cc * 8;
+        kr[i] = *reinterpret_cast<const uint4*>(K + off);
+        vr[i] = *reinterpret_cast<const uint4*>(V + off);
+      }
+    }
+  };
+  auto stash = [&](int stage) {
+    u16* ks = reinterpret_cast<u16*>(smem + stage * T::STAGE);
+    u16* vs = reinterpret_cast<u16*>(smem + stage * T::STAGE + T::KBYTES);
+#pragma unroll
+    for (int i = 0; i < T::CPT; ++i) {
+      const int ch = tid + i * T::NT;
+      const int row = ch / T::DCH, cc = ch % T::DCH;
+      *reinterpret_cast<uint4*>(ks + row * T::KSTR + cc * 8) = kr[i];
+      *reinterpret_cast<uint4*>(vs + row * T::VSTR + cc * 8) = vr[i];
+    }
+  };
+
   f32x16 o[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
@@ -109,102 +177,97 @@ __global__ __launch_bounds__(256) void attn_partial_bf16(AttnParams P) {
   float m_run = -INFINITY, l_run = 0.f;
   const float c2 = P.scale_log2;
   const int prow = (col & ~12) | ((col & 4) << 1) | ((col & 8) >> 1);
+  // LDS transpose-read address of this lane inside a 4-key x 16-dim block
+  const int grp = lane >> 4, sl = lane & 15;
+  const int tr_off = (8 * (grp >> 1) + (sl >> 2)) * T::VSTR + 16 * (grp & 1) + 4 * (sl & 3);
 
-  for (int ri = 0; ri < it.nrun; ++ri) {
-    const KeyRun run = P.runs[it.run0 + ri];
-    for (int k0 = 0; k0 < run.len; k0 += KT) {
-      const int nv = min(KT, run.len - k0);
-      const int64_t kbase = (run.start + k0) * rs + head * D;
-      __syncthreads();
-      // K tile, row-major [key][dim]
-      for (int c = tid; c < KT * DCH; c += 256) {
-        const int kr = c / DCH, kc = c % DCH;
-        uint4 val = make_uint4(0, 0, 0, 0);
-        if (kr < nv) val = *reinterpret_cast<const uint4*>(K + kbase + kr * rs + kc * 8);
-        *reinterpret_cast<uint4*>(ks + kr * KSTR + kc * 8) = val;
-      }
-      // V tile, transposed to [dim][key]: each thread moves a 4-key x 8-dim block
-      for (int c = tid; c < (KT / 4) * DCH; c += 256) {
-        const int kg = c / DCH, db = c % DCH;
-        uint4 rw[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          rw[j] = make_uint4(0, 0, 0, 0);
-          if (4 * kg + j < nv) rw[j] = *reinterpret_cast<const uint4*>(V + kbase + (4 * kg + j) * rs + db * 8);
-        }
-        const u32* w0 = reinterpret_cast<const u32*>(&rw[0]);
-        const u32* w1 = reinterpret_cast<const u32*>(&rw[1]);
-        const u32* w2 = reinterpret_cast<const u32*>(&rw[2]);
-        const u32* w3 = reinterpret_cast<const u32*>(&rw[3]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int wd = e >> 1;
-          u32 lo, hi;
-          if (e & 1) {
-            lo = (w0[wd] >> 16) | (w1[wd] & 0xFFFF0000u);
-            hi = (w2[wd] >> 16) | (w3[wd] & 0xFFFF0000u);
-          } else {
-            lo = (w0[wd] & 0xFFFFu) | (w1[wd] << 16);
-            hi = (w2[wd] & 0xFFFFu) | (w3[wd] << 16);
-          }
-          *reinterpret_cast<uint2*>(vt + (db * 8 + e) * VSTR + 4 * kg) = make_uint2(lo, hi);
-        }
-      }
-      __syncthreads();
+  TileCursor cur{0, 0};
+  while (cur.run < nrun && runs[cur.run].len <= 0) cursor_next(cur, runs, nrun, T::KT);
+  TileCursor nxt = cur;
+  int stage = 0;
+  if (cur.run < nrun) {
+    fetch(cur);
+    stash(0);
+    cursor_next(nxt, runs, nrun, T::KT);
+    if (nxt.run < nrun) fetch(nxt);
+  }
+  __syncthreads();
 
-      // scores S^T for keys [0,32) and [32,64)
-      f32x16 s[2];
+  while (cur.run < nrun) {
+    const int nv = min(T::KT, runs[cur.run].len - cur.k0);
+    const u16* ks = reinterpret_cast<const u16*>(smem + stage * T::STAGE);
+    const u16* vs = reinterpret_cast<const u16*>(smem + stage * T::STAGE + T::KBYTES);
+
+    // scores S^T for keys [0,32) and [32,64)
+    f32x16 s[2];
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
+    for (int st = 0; st < 2; ++st) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[st][i] = 0.f;
-        const u16* kp = ks + (32 * st + prow) * KSTR + 8 * hl;
+      for (int i = 0; i < 16; ++i) s[st][i] = 0.f;
+      const u16* kp = ks + (32 * st + prow) * T::KSTR + 8 * hl;
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(kp + 16 * kk));
-          s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[st], 0, 0, 0);
-        }
-      }
-      // accumulator element i of tile st holds key 32*st + 16*(i/8) + 8*hl + i%8
-      float mx = -INFINITY;
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = 32 * st + 16 * (i >> 3) + 8 * hl + (i & 7);
-          const float x = key < nv ? s[st][i] * c2 : -INFINITY;
-          s[st][i] = x;
-          mx = fmaxf(mx, x);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      float ps = 0.f;
-      bf16x8 pf[4];
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float pv = __builtin_amdgcn_exp2f(s[st][i] - m_use);
-          ps += pv;
-          pf[2 * st + (i >> 3)][i & 7] = static_cast<__bf16>(pv);
-        }
-      l_run = l_run * alpha + ps;
-      m_run = m_new;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
-      // O^T (dims x queries) += V^T * P^T, 16 keys per step
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const u16* vp = vt + (32 * dt + col) * VSTR + 8 * hl;
-#pragma unroll
-        for (int kp4 = 0; kp4 < 4; ++kp4) {
-          const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(vp + 16 * kp4));
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kp4], o[dt], 0, 0, 0);
-        }
+      for (int kk = 0; kk < NKK; ++kk) {
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(kp + 16 * kk));
+        s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[st], 0, 0, 0);
       }
     }
+    // accumulator element i of tile st holds key 32*st + 16*(i/8) + 8*hl + i%8
+    if (nv < T::KT) {
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (32 * st + 16 * (i >> 3) + 8 * hl + (i & 7) >= nv) s[st][i] = -INFINITY;
+    }
+    float mx = s[0][0];
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[st][i]);
+    mx *= c2;
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (__any(mx > m_run + kLazyRescale)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+      m_run = m_new;
+    }
+    float ps = 0.f;
+    bf16x8 pf[4];
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float pv = __builtin_amdgcn_exp2f(fmaf(s[st][i], c2, -m_run));
+        ps += pv;
+        pf[2 * st + (i >> 3)][i & 7] = static_cast<__bf16>(pv);
+      }
+    l_run += ps;
+    // O^T (dims x queries) += V^T * P^T, 16 keys per step
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+      for (int kp4 = 0; kp4 < 4; ++kp4) {
+        const u16* vp = vs + tr_off + 16 * kp4 * T::VSTR + 32 * dt;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp + 4 * T::VSTR));
+        const v4i16 both[2] = {lo, hi};
+        const bf16x8 a = __builtin_bit_cast(bf16x8, both);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kp4], o[dt], 0, 0, 0);
+      }
+    }
+
+    // advance: stash the prefetched tile into the other stage, prefetch the one after
+    cur = nxt;
+    if (cur.run < nrun) {
+      stash(stage ^ 1);
+      cursor_next(nxt, runs, nrun, T::KT);
+      if (nxt.run < nrun) fetch(nxt);
+    }
+    stage ^= 1;
+    __syncthreads();
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -390,7 +453,7 @@ __global__ __launch_bounds__(256) void merge_partials(MergeParams P) {
 
 }  // namespace
 
-int attn_query_tile(cqsa_dtype dtype) { return dtype == CQSA_BF16 ? 128 : 64; }
+int attn_query_tile(cqsa_dtype dtype) { return dtype == CQSA_BF16 ? Bf16Tile<128>::QT : 64; }
 
 hipError_t launch_attn(const AttnLaunch& a, hipStream_t stream) {
   if (a.n_items <= 0 || a.q_len <= 0) return hipSuccess;
@@ -411,9 +474,9 @@ hipError_t launch_attn(const AttnLaunch& a, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(blocks));
   if (a.dtype == CQSA_BF16) {
     if (a.d == 128)
-      hipLaunchKernelGGL(attn_partial_bf16<128>, grid, dim3(256), 0, stream, p);
+      hipLaunchKernelGGL(attn_partial_bf16<128>, grid, dim3(Bf16Tile<128>::NT), 0, stream, p);
     else if (a.d == 64)
-      hipLaunchKernelGGL(attn_partial_bf16<64>, grid, dim3(256), 0, stream, p);
+      hipLaunchKernelGGL(attn_partial_bf16<64>, grid, dim3(Bf16Tile<64>::NT), 0, stream, p);
     else
       return hipErrorInvalidValue;
   } else {
