@@ -62,3 +62,26 @@ def pinned_qkv(seed, n, h, d, dtype):
 
 def log(msg):
     print(msg, flush=True)
+
+
+def oracle_rows(q, k, v, rows, dtype, workers=None):
+    """attention_fp64 over disjoint chunks of the sampled rows in parallel threads.
+
+    Each thread runs the unchanged oracle on its rows with BLAS limited to one thread,
+    so the host's cores are used once each; results are reassembled in row order.
+    """
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+
+    from oracle.attention import attention_fp64
+
+    rows = np.asarray(rows, dtype=np.int64)
+    if workers is None:
+        workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    chunks = [c for c in np.array_split(rows, workers) if c.size]
+    with threadpool_limits(1):
+        with ThreadPoolExecutor(max_workers=len(chunks)) as pool:
+            parts = list(pool.map(lambda c: attention_fp64(q, k, v, rows=c, dtype=dtype, key_block=8192), chunks))
+    return np.concatenate([p[0] for p in parts], axis=0), np.concatenate([p[1] for p in parts], axis=1)

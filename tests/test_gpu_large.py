@@ -1,0 +1,70 @@
+"""Full-size host-pinned workloads on the GPU, checked on seeded sampled rows.
+
+* N=212992, H=16, d=128, bf16, l=4 (c=13), device budget 16 GiB
+* N=1376256, H=8, d=128, bf16, l=5 (c=21), device budget 8 GiB (accumulator on host)
+* N=12845056, H=1, d=128, bf16, two levels l=(3,3), device budget 2 GiB
+
+Q/K/V are drawn straight into pinned host memory; the call streams every task through
+the budget; the oracle evaluates the sampled rows (plus every unit's first and last
+token) in fp64.  The bound is 2e-2 row-wise relative error.
+"""
+import os
+import time
+
+import numpy as np
+import pytest
+
+from memory_bounded_streaming_amd import cqsa
+from memory_bounded_streaming_amd.inputs import sample_rows
+from oracle.tolerance import BF16_REL_TOL, error_report
+
+from gpu_util import as_f64, log, oracle_rows, pinned, pinned_qkv
+
+pytestmark = pytest.mark.gpu
+GiB = 1 << 30
+
+WORKLOADS = {
+    "n212992_h16_l4_16GiB": (212992, 16, 128, [4], 16 * GiB, 4096, 1),
+    "n1376256_h8_l5_8GiB": (1376256, 8, 128, [5], 8 * GiB, 4096, 2),
+    "n12845056_h1_l3x3_2GiB": (12845056, 1, 128, [3, 3], 2 * GiB, 1024, 4),
+}
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_streamed_workload_sampled_rows(name):
+    torch = pytest.importorskip("torch")
+    n, h, d, levels, budget, r_count, mode = WORKLOADS[name]
+    os.environ["CQSA_PROGRESS"] = "1"
+    log(f"{name}: drawing inputs into pinned memory")
+    t0 = time.time()
+    (tq, tk, tv), (q, k, v) = pinned_qkv(0, n, h, d, "bf16")
+    to, oa = pinned((n, h, d), "bf16")
+    tl = torch.empty((h, n), dtype=torch.float32, pin_memory=True)
+    log(f"  inputs ready in {time.time() - t0:.1f} s")
+    with cqsa.Plan(n, h, d, cqsa.CQSA_BF16, levels, budget_bytes=budget) as p:
+        info = p.info
+        assert info["stream_mode"] == mode
+        assert info["stream_workspace_bytes"] <= budget
+        free0, _ = torch.cuda.mem_get_info()
+        t0 = time.time()
+        st = p.forward(tq, tk, tv, to, tl, residency=cqsa.CQSA_RES_HOST_PINNED, stats=True)
+        wall = time.time() - t0
+        free1, _ = torch.cuda.mem_get_info()
+    log(f"  forward {wall:.1f} s: {info['useful_flop'] / wall / 1e12:.1f} TFLOP/s end-to-end, "
+        f"partial kernel {info['useful_flop'] / (st['t_attn_ms'] / 1e3) / 1e12:.1f} TFLOP/s, "
+        f"peak device {st['peak_device_bytes'] / GiB:.3f} GiB of {budget / GiB:.0f} GiB")
+    assert st["peak_device_bytes"] <= budget
+    assert abs(free1 - free0) < (256 << 20)
+    e = 2
+    visits = info["visits"]
+    assert st["bytes_h2d"] >= 3 * visits * n * h * d * e
+    rows = sample_rows(n, r_count, 0, unit_tokens=info["unit_tokens"])
+    log(f"  oracle on {rows.size} rows")
+    t0 = time.time()
+    o_ref, lse_ref = oracle_rows(q, k, v, rows, "bf16")
+    log(f"  oracle {time.time() - t0:.1f} s")
+    rep = error_report(as_f64(oa[rows], "bf16"), o_ref)
+    log(f"  {rep}")
+    assert rep["rowwise_rel"] <= BF16_REL_TOL
+    assert np.abs(tl.numpy()[:, rows] - lse_ref).max() <= 2e-3
