@@ -177,6 +177,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-streamed", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run one plain device copy of 1 GiB first (reference for HBM traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path",
@@ -188,6 +190,13 @@ def main():
     cqsa.load()
     torch.cuda.set_device(0)
 
+    if args.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("bench: calibration copy of 1 GiB done")
     log("bench: device-resident workload")
     dres = run_device(args, torch, cqsa)
     log(f"bench: {dres['value']:.1f} TFLOP/s end-to-end, partial kernel {dres['attn_tflops']:.1f} TFLOP/s")
