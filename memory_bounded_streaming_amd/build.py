@@ -37,6 +37,14 @@ def _run(cmd):
     return out
 
 
+def _check_stubs(lib):
+    """Every kernel launch stub the host code references must be defined in the library."""
+    nm = subprocess.run(["nm", lib], stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True).stdout
+    missing = [ln.split()[-1] for ln in nm.splitlines() if ln.split()[:1] == ["U"] and "__device_stub__" in ln]
+    if missing:
+        raise RuntimeError("kernel launch stubs missing from the host pass: " + ", ".join(missing))
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source and link libcqsa.so; returns its path."""
     os.makedirs(OBJ, exist_ok=True)
@@ -56,6 +64,7 @@ def build(verbose: bool = False) -> str:
     tmp = OUT + ".tmp"
     logs.append(_run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs,
                       f"-L{ROCM}/lib", "-lamdhip64", f"-Wl,-rpath,{ROCM}/lib"]))
+    _check_stubs(tmp)
     os.replace(tmp, OUT)
     if verbose:
         for log in logs:

@@ -16,10 +16,20 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["F32_ABS_TOL", "BF16_REL_TOL", "max_abs_err", "rowwise_rel_err", "error_report"]
+__all__ = ["F32_ABS_TOL", "BF16_REL_TOL", "F32_LSE_TOL", "BF16_LSE_TOL", "max_abs_err", "rowwise_rel_err",
+           "error_report"]
 
 F32_ABS_TOL = 1e-5
 BF16_REL_TOL = 2e-2
+
+# Log-sum-exp bounds (absolute, natural log).  The pages fix no tolerance for LSE; these
+# follow from the arithmetic of a 16-bit path: the softmax weights enter the P V product
+# rounded to bf16 (round to nearest even, relative error <= 2^-9), and the denominator l
+# sums those same rounded weights, so ln l carries a relative error of at most 2^-9 on
+# top of float32 rounding; 2^-8 leaves a factor of two for the latter.  For float32
+# inputs every step is float32, so 2e-5 covers the accumulated rounding.
+F32_LSE_TOL = 2e-5
+BF16_LSE_TOL = 2.0 ** -8
 
 
 def max_abs_err(out, ref) -> float:
