@@ -49,27 +49,6 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t grid) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
-// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
-constexpr int kVmcntZero = 0x0F70;  // vmcnt(0), other counters unconstrained
-template <int IPW>
-constexpr int kVmcntKeepTile() {  // vmcnt(2*IPW): all but the newest tile's direct loads done
-  return 0x0F70 | ((2 * IPW) & 0xF) | (((2 * IPW) >> 4) << 14);
-}
-constexpr int kLgkmcntZero = 0xC07F;  // lgkmcnt(0), vmcnt and expcnt unconstrained
-
-// Workgroup barrier for LDS hand-offs.  __syncthreads() carries a workgroup fence that
-// makes the compiler drain every outstanding vector-memory operation, including the
-// direct-to-LDS loads of tiles still being prefetched; here each wave only completes
-// its LDS operations (the direct loads are awaited explicitly with vmcnt), and the empty
-// asm statements keep the compiler from moving memory accesses across the barrier.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(kLgkmcntZero);
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-
 // ---------------------------------------------------------------------------------
 // bf16 partials on MFMA.  Workgroup = 8 wave64 = 256 query rows (32 per wave); all
 // eight waves share each 64-key K/V tile, so a tile fetched from L2 feeds 256 queries.
@@ -82,56 +61,34 @@ __device__ __forceinline__ void lds_barrier() {
 // the 16 accumulator values a lane holds are exactly the B operand (8 consecutive
 // keys per half-wave) of O^T += V^T * P^T, so P never leaves registers.  V stays
 // row-major in LDS and the A operand of that product (8 consecutive keys of one dim
-// per lane) is fetched with two LDS transpose reads (ds_read_b64_tr_b16: inside each
-// 16-lane group, lane i receives element i%4 of the 8-byte chunks addressed by lanes
-// 4j + i/4, j = 0..3).
+// per lane) is fetched with two LDS transpose reads (ds_read_b64_tr_b16).
 //
-// Tiles reach LDS by direct global->LDS loads (global_load_lds_dwordx4: lane l of a
-// wave writes 16 bytes at a wave-uniform LDS base + 16*l) into a ring of four stages,
-// three tiles ahead of the one being consumed; no registers hold tiles in flight.  K
-// and V rows are stored unpadded with their 16-byte chunks XOR-permuted per row, so
-// the b128 reads of K and the transpose reads of V are free of bank conflicts.
-//
-// The two waves that share a SIMD work half a tile apart (see the phase loop), so one
-// keeps the matrix pipe busy while the other runs its softmax on the vector ALU.
-// The running max is rescaled lazily: the reference max only moves when a score
-// exceeds it by more than 2^8, so every exponential stays <= 2^8 and (m, l, n) remains
-// exact for the m it carries.  The row sum l adds the bf16-rounded weights (the same
-// values the P V product uses) with v_dot2_f32_bf16.
+// Pipeline: the next tile is fetched from global memory into registers while the
+// current one is computed from LDS, then written to the other LDS stage; one barrier
+// per tile.  The running max is rescaled lazily: the reference max only moves when a
+// score exceeds it by more than 2^8, so every exponent stays <= 2^8 and the triple
+// (m, l, n) remains exact for whatever m it carries.
 // ---------------------------------------------------------------------------------
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) void lds_void;
-
-// 16-byte direct global->LDS load (global_load_lds_dwordx4).  The builtin exists only
-// for the device target; clang's host pass must not see it, or it drops the kernel's
-// launch stub, so the body is compiled in the device pass only.
-__device__ __forceinline__ void lds_dma16(const void* src, char* lds_dst) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_dst, 16, 0, 0);
-#endif
-}
 
 constexpr float kLazyRescale = 8.0f;  // log2 units
 
 template <int D>
 struct Bf16Tile {
-  static constexpr int NW = 8;            // waves per workgroup
-  static constexpr int NT = 64 * NW;      // threads
-  static constexpr int QT = 32 * NW;      // query rows per workgroup
-  static constexpr int KT = 64;           // keys per tile
-  static constexpr int RB = 2 * D;        // bytes per K or V row
-  static constexpr int CH = D / 8;        // 16-byte chunks per row
-  static constexpr int RPL = 256 / RB;    // rows per 256-byte bank line (64 banks x 4 bytes)
-  static constexpr int TB = KT * RB;      // bytes of one K (or V) tile
-  static constexpr int STAGE = 2 * TB;    // K tile then V tile
-  static constexpr int NSTAGE = 4;
-  static constexpr int IPW = TB / 1024 / NW;  // 1 KiB direct loads per wave per tensor per tile
-  static_assert(IPW >= 1 && TB == IPW * 1024 * NW, "tile split");
-  // physical 16-byte chunk of logical chunk c in row r
-  __device__ static int kswz(int r) { return (r / RPL) % CH; }
-  __device__ static int vswz(int r) { return 4 * ((r / RPL) % (CH / 4)); }
+  static constexpr int NW = 8;          // waves per workgroup
+  static constexpr int NT = 64 * NW;    // threads
+  static constexpr int QT = 32 * NW;    // query rows per workgroup
+  static constexpr int KT = 64;         // keys per tile
+  static constexpr int KSTR = D + 8;    // K row stride in LDS (u16): 16-byte pad
+  static constexpr int VSTR = D + 32;   // V row stride in LDS (u16): rows 16 dwords apart mod 64 banks
+  static constexpr int DCH = D / 8;     // 16-byte chunks per row
+  static constexpr int CPT = KT * DCH / NT;  // chunks of K (and of V) per thread per tile
+  static constexpr int KBYTES = KT * KSTR * 2;
+  static constexpr int VBYTES = KT * VSTR * 2;
+  static constexpr int STAGE = KBYTES + VBYTES;
+  static_assert(CPT >= 1 && KT * DCH == CPT * NT, "tile split");
 };
 
 // Cursor over the tiles of an item's key runs.  The current run's start and length
@@ -177,7 +134,7 @@ __global__ __launch_bounds__(512) void attn_partial_bf16(AttnParams P) {
   using T = Bf16Tile<D>;
   constexpr int NKK = D / 16;
   constexpr int NDT = D / 32;
-  __shared__ __attribute__((aligned(1024))) char smem[T::NSTAGE * T::STAGE];
+  __shared__ __attribute__((aligned(16))) char smem[2 * T::STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -189,7 +146,7 @@ __global__ __launch_bounds__(512) void attn_partial_bf16(AttnParams P) {
   const WorkItem it = P.items[rest / P.heads];
   const KeyRun* runs = P.runs + it.run0;
   const int nrun = it.nrun;
-  const int rs = P.heads * D;  // elements per token row
+  const int64_t rs = static_cast<int64_t>(P.heads) * D;
   const u16* __restrict__ Q = static_cast<const u16*>(P.q);
   const u16* __restrict__ K = static_cast<const u16*>(P.k) + head * D;
   const u16* __restrict__ V = static_cast<const u16*>(P.v) + head * D;
@@ -198,7 +155,7 @@ __global__ __launch_bounds__(512) void attn_partial_bf16(AttnParams P) {
   const bool qok = qi < it.q_len;
   bf16x8 qf[NKK];
   {
-    const u16* qp = Q + (it.q_row0 + (qok ? qi : 0)) * static_cast<int64_t>(rs) + head * D + 8 * hl;
+    const u16* qp = Q + (it.q_row0 + (qok ? qi : 0)) * rs + head * D + 8 * hl;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       uint4 u = make_uint4(0, 0, 0, 0);
@@ -207,60 +164,33 @@ __global__ __launch_bounds__(512) void attn_partial_bf16(AttnParams P) {
     }
   }
 
-  // direct loads: row and XOR-permuted source offsets of this lane, per 1 KiB block
-  int dma_row[T::IPW], dma_koff[T::IPW], dma_voff[T::IPW];
+  // global -> register fetch of one tile (rows past the run end read as zero)
+  uint4 kr[T::CPT], vr[T::CPT];
+  auto fetch = [&](const TileCursor& c) {
+    const int64_t start = c.start + c.k0;
+    const int nv = min(T::KT, c.len - c.k0);
 #pragma unroll
-  for (int i = 0; i < T::IPW; ++i) {
-    const int byte = (wave * T::IPW + i) * 1024 + 16 * lane;
-    const int r = byte / T::RB, pch = (byte % T::RB) / 16;
-    dma_row[i] = r;
-    dma_koff[i] = 8 * (pch ^ T::kswz(r));
-    dma_voff[i] = 8 * (pch ^ T::vswz(r));
-  }
-  int n_tiles = 0;
-  for (int r = 0; r < nrun; ++r) n_tiles += (max(runs[r].len, 0) + T::KT - 1) / T::KT;
-  TileCursor ld = cursor_begin(runs, nrun);
-  // DMA the tile under the cursor into a stage; returns its valid key count
-  auto issue = [&](int stage) -> int {
-    const int64_t start = ld.start + ld.k0;
-    const int nv = min(T::KT, ld.len - ld.k0);
-    char* kb = smem + stage * T::STAGE;
-#pragma unroll
-    for (int i = 0; i < T::IPW; ++i) {
-      const int64_t g = (start + min(dma_row[i], nv - 1)) * rs;  // rows past the run end repeat a valid row
-      char* blk = kb + (wave * T::IPW + i) * 1024;
-      lds_dma16(K + g + dma_koff[i], blk);
-      lds_dma16(V + g + dma_voff[i], blk + T::TB);
-    }
-    cursor_next(ld, runs, nrun, T::KT);
-    return nv;
-  };
-
-  // LDS read offsets of this lane
-  const int prow = (col & ~12) | ((col & 4) << 1) | ((col & 8) >> 1);
-  int k_rd[2];
-#pragma unroll
-  for (int st = 0; st < 2; ++st) k_rd[st] = (32 * st + prow) * T::RB;
-  const int k_swz = T::kswz(prow);  // same for rows prow and 32 + prow
-  const int grp = lane >> 4, sl = lane & 15;
-  const int v_row = 8 * hl + (sl >> 2);            // + 16 * kstep, + 4 for the second read
-  const int v_swz = T::vswz(v_row);                 // unchanged by +16*kstep or +4
-  const int v_cg = 2 * (grp & 1) + ((sl & 3) >> 1);  // logical chunk within the 32-dim tile
-  int v_rd[NDT];
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) v_rd[dt] = T::TB + v_row * T::RB + 16 * ((4 * dt + v_cg) ^ v_swz) + 8 * (sl & 1);
-
-  auto scores = [&](int stage, f32x16 (&s)[2]) {
-    const char* kb = smem + stage * T::STAGE;
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[st][i] = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(kb + k_rd[st] + 16 * ((2 * kk + hl) ^ k_swz)));
-        s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[st], 0, 0, 0);
+    for (int i = 0; i < T::CPT; ++i) {
+      const int ch = tid + i * T::NT;
+      const int row = ch / T::DCH, cc = ch % T::DCH;
+      kr[i] = make_uint4(0, 0, 0, 0);
+      vr[i] = make_uint4(0, 0, 0, 0);
+      if (row < nv) {
+        const int64_t off = (start + row) * rs + cc * 8;
+        kr[i] = *reinterpret_cast<const uint4*>(K + off);
+        vr[i] = *reinterpret_cast<const uint4*>(V + off);
       }
+    }
+  };
+  auto stash = [&](int stage) {
+    u16* ks = reinterpret_cast<u16*>(smem + stage * T::STAGE);
+    u16* vs = reinterpret_cast<u16*>(smem + stage * T::STAGE + T::KBYTES);
+#pragma unroll
+    for (int i = 0; i < T::CPT; ++i) {
+      const int ch = tid + i * T::NT;
+      const int row = ch / T::DCH, cc = ch % T::DCH;
+      *reinterpret_cast<uint4*>(ks + row * T::KSTR + cc * 8) = kr[i];
+      *reinterpret_cast<uint4*>(vs + row * T::VSTR + cc * 8) = vr[i];
     }
   };
 
@@ -272,12 +202,41 @@ __global__ __launch_bounds__(512) void attn_partial_bf16(AttnParams P) {
   float m_run = -INFINITY, l_run = 0.f;
   const float c2 = P.scale_log2;
   const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-  f32x16 s[2];
-  bf16x8 pf[4];
+  const int prow = (col & ~12) | ((col & 4) << 1) | ((col & 8) >> 1);
+  // LDS transpose-read address of this lane inside a 4-key x 16-dim block
+  const int grp = lane >> 4, sl = lane & 15;
+  const int tr_off = (8 * (grp >> 1) + (sl >> 2)) * T::VSTR + 16 * (grp & 1) + 4 * (sl & 3);
 
-  // vector phase of one tile: scores -> bf16 weights, running max and row sum
-  auto softmax = [&](int nv) {
-    // mask a ragged tile; accumulator element i of tile st holds key 32*st + 16*(i/8) + 8*hl + i%8
+  TileCursor cur = cursor_begin(runs, nrun);
+  TileCursor nxt = cur;
+  int stage = 0;
+  if (cur.run < nrun) {
+    fetch(cur);
+    stash(0);
+    cursor_next(nxt, runs, nrun, T::KT);
+    if (nxt.run < nrun) fetch(nxt);
+  }
+  __syncthreads();
+
+  while (cur.run < nrun) {
+    const int nv = min(T::KT, cur.len - cur.k0);
+    const u16* ks = reinterpret_cast<const u16*>(smem + stage * T::STAGE);
+    const u16* vs = reinterpret_cast<const u16*>(smem + stage * T::STAGE + T::KBYTES);
+
+    // scores S^T for keys [0,32) and [32,64)
+    f32x16 s[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[st][i] = 0.f;
+      const u16* kp = ks + (32 * st + prow) * T::KSTR + 8 * hl;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(kp + 16 * kk));
+        s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[st], 0, 0, 0);
+      }
+    }
+    // accumulator element i of tile st holds key 32*st + 16*(i/8) + 8*hl + i%8
     if (nv < T::KT) {
 #pragma unroll
       for (int st = 0; st < 2; ++st)
@@ -291,8 +250,8 @@ __global__ __launch_bounds__(512) void attn_partial_bf16(AttnParams P) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[st][i]);
     // Each half-wave holds 32 of the 64 scores of a query.  The reference max is
-    // shared by both halves; it only needs to move (rare) when some half's local max
-    // passes it by more than 2^8, and only then do the halves exchange their maxima.
+    // shared by both halves; it only moves (rare) when some half's local max passes
+    // it by more than 2^8, and only then do the halves exchange their maxima.
     mx *= c2;
     if (__any(mx > m_run + kLazyRescale)) {
       const float m_new = fmaxf(m_run, fmaxf(mx, __shfl_xor(mx, 32)));
@@ -302,11 +261,13 @@ __global__ __launch_bounds__(512) void attn_partial_bf16(AttnParams P) {
       for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
       m_run = m_new;
     }
+    bf16x8 pf[4];
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         pf[2 * st + (i >> 3)][i & 7] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(s[st][i], c2, -m_run)));
+    // the row sum adds the bf16-rounded weights, the same values the P V product uses
     float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -316,60 +277,29 @@ __global__ __launch_bounds__(512) void attn_partial_bf16(AttnParams P) {
       ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[q], pf[q], 6, 7), ones, ps1, false);
     }
     l_run += ps0 + ps1;
-  };
-  // O^T (dims x queries) += V^T * P^T for the tile in a stage, 16 keys per MFMA
-  auto pv = [&](int stage) {
-    const char* vb = smem + stage * T::STAGE;
+    // O^T (dims x queries) += V^T * P^T, 16 keys per step
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
       for (int kp4 = 0; kp4 < 4; ++kp4) {
-        const char* vp = vb + v_rd[dt] + 16 * kp4 * T::RB;
+        const u16* vp = vs + tr_off + 16 * kp4 * T::VSTR + 32 * dt;
         const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp));
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp + 4 * T::RB));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp + 4 * T::VSTR));
         const v4i16 both[2] = {lo, hi};
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), pf[kp4], o[dt], 0, 0, 0);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, both);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kp4], o[dt], 0, 0, 0);
       }
     }
-  };
 
-  // Ping-pong over phases separated by workgroup barriers.  Waves 0-3 and 4-7 (one of
-  // each per SIMD) run half a tile apart: in every phase one group issues matrix work
-  // (P V of the previous tile, then the scores of this tile) while the other runs the
-  // softmax of its current tile on the vector ALU.  For group g, tile j is scored in
-  // phase 2j+g and its softmax runs in phase 2j+1+g; tile j is resident from phase 2j
-  // to 2j+3, and the direct loads for tile t+2 are issued in phase 2t.
-  const int g = wave >> 2;
-  TileCursor mc = cursor_begin(runs, nrun);  // tile whose softmax comes next (for its valid key count)
-  if (n_tiles > 0) issue(0);
-  if (n_tiles > 1) {
-    issue(1);
-    __builtin_amdgcn_s_waitcnt(kVmcntKeepTile<T::IPW>());
-  } else {
-    __builtin_amdgcn_s_waitcnt(kVmcntZero);
-  }
-  lds_barrier();
-  const int n_phase = n_tiles > 0 ? 2 * n_tiles + 2 : 0;
-  for (int p = 0; p < n_phase; ++p) {
-    if (!(p & 1) && (p >> 1) + 2 < n_tiles) issue(((p >> 1) + 2) & 3);
-    const int q = p - g;
-    if (q >= 0) {
-      const int j = q >> 1;
-      if (!(q & 1)) {
-        if (j >= 1) pv((j - 1) & 3);
-        if (j < n_tiles) scores(j & 3, s);
-      } else if (j < n_tiles) {
-        softmax(min(T::KT, mc.len - mc.k0));
-        cursor_next(mc, runs, nrun, T::KT);
-      }
+    // advance: stash the prefetched tile into the other stage, prefetch the one after
+    cur = nxt;
+    if (cur.run < nrun) {
+      stash(stage ^ 1);
+      cursor_next(nxt, runs, nrun, T::KT);
+      if (nxt.run < nrun) fetch(nxt);
     }
-    if (p & 1) {  // tile (p+1)/2 must be resident for the next phase
-      if (((p + 1) >> 1) + 1 < n_tiles)
-        __builtin_amdgcn_s_waitcnt(kVmcntKeepTile<T::IPW>());
-      else
-        __builtin_amdgcn_s_waitcnt(kVmcntZero);
-    }
-    lds_barrier();
+    stage ^= 1;
+    __syncthreads();
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
