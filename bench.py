@@ -135,6 +135,22 @@ def run_device(args, torch, cqsa):
     return out
 
 
+def pcie_achievable(torch, nbytes=512 << 20, reps=5):
+    """Plain pinned-memory copies of 512 MiB in each direction: the achievable PCIe rate."""
+    h = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    d = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    out = {}
+    for name, fn in (("h2d_gbs", lambda: d.copy_(h, non_blocking=True)), ("d2h_gbs", lambda: h.copy_(d, non_blocking=True))):
+        fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        out[name] = reps * nbytes / (time.perf_counter() - t0) / 1e9
+    return out
+
+
 def run_streamed(args, torch, cqsa):
     from memory_bounded_streaming_amd.inputs import gen_tensor
     n, h, d, levels, budget, _ = WORKLOADS["c3"]
@@ -152,6 +168,9 @@ def run_streamed(args, torch, cqsa):
         st = plan.forward(*ts, o, lse, residency=cqsa.CQSA_RES_HOST_PINNED, workspace=ws, stats=True)
         wall = time.perf_counter() - t0
         flop = plan.info["useful_flop"]
+        pcie = pcie_achievable(torch)
+        h2d = st["bytes_h2d"] / (st["t_h2d_ms"] / 1e3) / 1e9 if st["t_h2d_ms"] else None
+        d2h = st["bytes_d2h"] / (st["t_d2h_ms"] / 1e3) / 1e9 if st["t_d2h_ms"] else None
         return {
             "workload": f"N={n}, H={h}, d={d}, bf16, CQS l={levels[0]} (c=13), Q/K/V in pinned host memory, "
                         f"device budget {budget // GiB} GiB",
@@ -159,8 +178,14 @@ def run_streamed(args, torch, cqsa):
             "tflops_pcie_inclusive": flop / wall / 1e12,
             "wall_s": wall,
             "attn_tflops": flop / (st["t_attn_ms"] / 1e3) / 1e12,
-            "h2d_gbs": st["bytes_h2d"] / (st["t_h2d_ms"] / 1e3) / 1e9 if st["t_h2d_ms"] else None,
-            "d2h_gbs": st["bytes_d2h"] / (st["t_d2h_ms"] / 1e3) / 1e9 if st["t_d2h_ms"] else None,
+            "h2d_gbs": h2d,
+            "d2h_gbs": d2h,
+            "h2d_achievable_gbs": pcie["h2d_gbs"],
+            "d2h_achievable_gbs": pcie["d2h_gbs"],
+            "h2d_frac_of_achievable": h2d / pcie["h2d_gbs"] if h2d else None,
+            "d2h_frac_of_achievable": d2h / pcie["d2h_gbs"] if d2h else None,
+            "merge_ms": st["t_merge_ms"],
+            "attn_ms": st["t_attn_ms"],
             "bytes_h2d": st["bytes_h2d"],
             "bytes_d2h": st["bytes_d2h"],
             "peak_device_bytes": st["peak_device_bytes"],

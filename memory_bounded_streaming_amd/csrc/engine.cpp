@@ -494,10 +494,12 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
         bytes_d2h += U * H * D * e;
         ++n_d2h;
         if (lse != nullptr) {
-          HIP_TRY(hipMemcpy2DAsync(lse + pu * U, N * sizeof(float), S.lse, U * sizeof(float), U * sizeof(float), H,
-                                   hipMemcpyDeviceToHost, s_d));
+          // one contiguous copy per head: LSE is [H][N] on the host and [H][U] in the block
+          // (a strided 2-D copy of the same bytes runs several times slower)
+          for (int64_t h = 0; h < H; ++h)
+            HIP_TRY(hipMemcpyAsync(lse + h * N + pu * U, S.lse + h * U, U * sizeof(float), hipMemcpyDeviceToHost, s_d));
           bytes_d2h += H * U * 4;
-          ++n_d2h;
+          n_d2h += H;
         }
       } else if (!fp.acc_on_device) {
         const float* sn = first ? S.n : S.an;
