@@ -40,7 +40,7 @@ typedef enum {
   CQSA_OK = 0,
   CQSA_EINVAL = -1,   /* bad argument (null pointer, size, unsupported d/dtype/flag) */
   CQSA_ENOSET = -2,   /* no perfect difference set for this l (l = 7) */
-  CQSA_EDIVIDE = -3,  /* N is not a multiple of prod(c_k) over the levels */
+  CQSA_EDIVIDE = -3,  /* N is not a multiple of prod(c_k) (and CQSA_FLAG_PAD unset) or N < prod(c_k) */
   CQSA_EBUDGET = -4,  /* no staging mode fits the memory budget */
   CQSA_EHIP = -5,     /* a HIP runtime call failed */
   CQSA_ENOMEM = -6,   /* a host or device allocation failed */
@@ -63,6 +63,10 @@ typedef enum {
 /* plan_create flags (all optional; 0 = let the footprint model choose). */
 #define CQSA_FLAG_HOST_ACC 0x1u  /* only consider modes with the accumulator on the host */
 #define CQSA_FLAG_KV_SINGLE 0x2u /* only consider single-buffered K/V staging */
+/* Accept any N: the division runs over N_pad = ceil(N / prod(c_k)) * prod(c_k) tokens and
+ * positions >= N are padding that no query block, key run or copy touches, so the result
+ * is attention over the N real tokens.  Without this flag an N off the unit grid is EDIVIDE. */
+#define CQSA_FLAG_PAD 0x4u
 
 #define CQSA_MAX_LEVELS 8
 #define CQSA_MAX_L 10
@@ -87,6 +91,7 @@ typedef struct {
   int64_t device_workspace_bytes; /* device bytes the device-resident path needs */
   int64_t host_acc_bytes;       /* pinned host accumulator the host-pinned path allocates (0 if on device) */
   double useful_flop;           /* 4 * N^2 * d * H */
+  int64_t padded_tokens;        /* N_pad = unit_tokens * n_units (== n_tokens unless padded) */
 } cqsa_plan_info;
 
 typedef struct {
@@ -115,8 +120,9 @@ cqsa_status cqsa_difference_set(int32_t l, int32_t* out, int32_t cap);
  * Build the CQS plan for an N-token attention ("The 'CQS Divide'" and "The Recursive
  * Benefit" sections of the wispaper explainer; the Lattice summary's memory budget).
  *   l_levels[0..n_levels): l per level, outer level first.  n_levels = 0 means
- *     "auto": repeat l_levels[0] (one value read) until the host-pinned path fits
- *     budget_bytes (at most CQSA_MAX_LEVELS levels).
+ *     "auto" (out-of-memory recovery): the undivided plan (l = 1) if the host-pinned
+ *     path fits budget_bytes, else l_levels[0] (one value read, 2..10) repeated over
+ *     the fewest levels that fit (at most CQSA_MAX_LEVELS); EBUDGET if none does.
  *   Task t (mixed radix over levels, outer first) holds the chunks
  *     sorted{(t_k + d) mod c_k : d in D_k} of its parent at each level; inside a task,
  *     query unit i and key unit j are admitted iff at every level they lie in
@@ -125,7 +131,8 @@ cqsa_status cqsa_difference_set(int32_t l, int32_t* out, int32_t cap);
  *     footprint model picks the first fitting mode in the order of cqsa_mode.
  *   flags: CQSA_FLAG_* above.
  * Host-only (no HIP call).  *out receives a plan owned by the caller (free with
- * cqsa_plan_destroy) or NULL on error.  Errors: EINVAL, ENOSET, EDIVIDE, EBUDGET.
+ * cqsa_plan_destroy) or NULL on error.  Errors: EINVAL, ENOSET, EDIVIDE (N off the unit
+ * grid without CQSA_FLAG_PAD, or N < prod(c_k)), EBUDGET.
  * Supported: dtype BF16 with head_dim 64 or 128, dtype F32 with head_dim 64 or 128.
  */
 cqsa_status cqsa_plan_create(int64_t n, int32_t heads, int32_t head_dim, cqsa_dtype dtype,

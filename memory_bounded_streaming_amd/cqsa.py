@@ -18,7 +18,7 @@ import numpy as np
 
 __all__ = [
     "CqsaError", "load", "CQSA_BF16", "CQSA_F32", "CQSA_RES_DEVICE", "CQSA_RES_HOST_PINNED",
-    "CQSA_FLAG_HOST_ACC", "CQSA_FLAG_KV_SINGLE", "MODE_NAMES",
+    "CQSA_FLAG_HOST_ACC", "CQSA_FLAG_KV_SINGLE", "CQSA_FLAG_PAD", "MODE_NAMES",
     "cqsa_version", "cqsa_difference_set", "cqsa_plan_create", "cqsa_plan_info_get", "cqsa_plan_schedule",
     "cqsa_plan_coverage", "cqsa_plan_destroy", "cqsa_workspace_size", "cqsa_partials", "cqsa_merge",
     "cqsa_forward", "cqsa_status_string", "cqsa_last_error", "Plan",
@@ -26,7 +26,7 @@ __all__ = [
 
 CQSA_BF16, CQSA_F32 = 0, 1
 CQSA_RES_DEVICE, CQSA_RES_HOST_PINNED = 0, 1
-CQSA_FLAG_HOST_ACC, CQSA_FLAG_KV_SINGLE = 0x1, 0x2
+CQSA_FLAG_HOST_ACC, CQSA_FLAG_KV_SINGLE, CQSA_FLAG_PAD = 0x1, 0x2, 0x4
 MODE_NAMES = {1: "device_acc_kv2", 2: "host_acc_kv2", 3: "device_acc_kv1", 4: "host_acc_kv1"}
 MAX_LEVELS = 8
 
@@ -51,6 +51,7 @@ class PlanInfo(ctypes.Structure):
         ("stream_mode", ctypes.c_int32), ("kv_buffers", ctypes.c_int32),
         ("stream_workspace_bytes", ctypes.c_int64), ("device_workspace_bytes", ctypes.c_int64),
         ("host_acc_bytes", ctypes.c_int64), ("useful_flop", ctypes.c_double),
+        ("padded_tokens", ctypes.c_int64),
     ]
 
 

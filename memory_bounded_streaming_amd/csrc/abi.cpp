@@ -122,6 +122,7 @@ cqsa_status cqsa_plan_info_get(const cqsa_plan* plan, cqsa_plan_info* out) {
     out->device_workspace_bytes = p.device_ws;
     out->host_acc_bytes = p.host_acc_bytes;
     out->useful_flop = 4.0 * double(p.n) * double(p.n) * p.d * p.heads;
+    out->padded_tokens = p.n_pad;
     return ok();
   });
 }

@@ -392,6 +392,8 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
       const int j = static_cast<int>(blk % 2);
       Slot& S = slot[j];
       const int64_t pu = task.units[a];
+      const int64_t R = p.unit_rows(pu);  // U, fewer in the last unit of a padded plan
+      if (R == 0) continue;               // a unit of padding only: nothing to compute or copy
       const int visit = task.slot[a];
       const bool first = visit == 0, last = visit == p.visits - 1;
       if (blk >= 2) HIP_TRY(hipStreamWaitEvent(s_q, slot_free[j], 0));
@@ -399,13 +401,13 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
         HIP_TRY(hipStreamWaitEvent(s_q, slot_free[(blk - 1) % 2], 0));
       // H2D: Q block (+ accumulator block)
       HIP_TRY(tm.begin(PH_H2D, s_q, tev));
-      HIP_TRY(hipMemcpyAsync(S.q, q + pu * U * row_in, U * row_in, hipMemcpyHostToDevice, s_q));
-      bytes_h2d += U * row_in;
+      HIP_TRY(hipMemcpyAsync(S.q, q + pu * U * row_in, R * row_in, hipMemcpyHostToDevice, s_q));
+      bytes_h2d += R * row_in;
       ++n_h2d;
       if (!fp.acc_on_device && !first) {
-        HIP_TRY(hipMemcpyAsync(S.an, host_n + pu * U * nrow_f, U * nrow_f * 4, hipMemcpyHostToDevice, s_q));
-        HIP_TRY(hipMemcpyAsync(S.aml, host_ml + pu * U * mlrow_f, U * mlrow_f * 4, hipMemcpyHostToDevice, s_q));
-        bytes_h2d += U * (nrow_f + mlrow_f) * 4;
+        HIP_TRY(hipMemcpyAsync(S.an, host_n + pu * U * nrow_f, R * nrow_f * 4, hipMemcpyHostToDevice, s_q));
+        HIP_TRY(hipMemcpyAsync(S.aml, host_ml + pu * U * mlrow_f, R * mlrow_f * 4, hipMemcpyHostToDevice, s_q));
+        bytes_h2d += R * (nrow_f + mlrow_f) * 4;
         n_h2d += 2;
       }
       HIP_TRY(tm.end(PH_H2D, s_q));
@@ -443,7 +445,7 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
       m.dtype = p.dtype;
       m.d = p.d;
       m.heads = p.heads;
-      m.rows = U;
+      m.rows = R;
       m.final_out = last;
       m.o_out = S.o;
       m.lse_out = S.lse;
@@ -484,35 +486,35 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
         ++n_merge;
       }
       HIP_TRY(hipEventRecord(c_done[j], s_c));
-      if (a == tu - 1) HIP_TRY(hipEventRecord(kv_free[b], s_c));
 
       // D2H: finished output block, or the accumulator block back to host memory
       HIP_TRY(hipStreamWaitEvent(s_d, c_done[j], 0));
       HIP_TRY(tm.begin(PH_D2H, s_d, tev));
       if (last) {
-        HIP_TRY(hipMemcpyAsync(o + pu * U * H * D * e, S.o, U * H * D * e, hipMemcpyDeviceToHost, s_d));
-        bytes_d2h += U * H * D * e;
+        HIP_TRY(hipMemcpyAsync(o + pu * U * H * D * e, S.o, R * H * D * e, hipMemcpyDeviceToHost, s_d));
+        bytes_d2h += R * H * D * e;
         ++n_d2h;
         if (lse != nullptr) {
           // one contiguous copy per head: LSE is [H][N] on the host and [H][U] in the block
           // (a strided 2-D copy of the same bytes runs several times slower)
           for (int64_t h = 0; h < H; ++h)
-            HIP_TRY(hipMemcpyAsync(lse + h * N + pu * U, S.lse + h * U, U * sizeof(float), hipMemcpyDeviceToHost, s_d));
-          bytes_d2h += H * U * 4;
+            HIP_TRY(hipMemcpyAsync(lse + h * N + pu * U, S.lse + h * U, R * sizeof(float), hipMemcpyDeviceToHost, s_d));
+          bytes_d2h += H * R * 4;
           n_d2h += H;
         }
       } else if (!fp.acc_on_device) {
         const float* sn = first ? S.n : S.an;
         const float* sml = first ? S.ml : S.aml;
-        HIP_TRY(hipMemcpyAsync(host_n + pu * U * nrow_f, sn, U * nrow_f * 4, hipMemcpyDeviceToHost, s_d));
-        HIP_TRY(hipMemcpyAsync(host_ml + pu * U * mlrow_f, sml, U * mlrow_f * 4, hipMemcpyDeviceToHost, s_d));
-        bytes_d2h += U * (nrow_f + mlrow_f) * 4;
+        HIP_TRY(hipMemcpyAsync(host_n + pu * U * nrow_f, sn, R * nrow_f * 4, hipMemcpyDeviceToHost, s_d));
+        HIP_TRY(hipMemcpyAsync(host_ml + pu * U * mlrow_f, sml, R * mlrow_f * 4, hipMemcpyDeviceToHost, s_d));
+        bytes_d2h += R * (nrow_f + mlrow_f) * 4;
         n_d2h += 2;
         last_block[pu] = blk;
       }
       HIP_TRY(tm.end(PH_D2H, s_d));
       HIP_TRY(hipEventRecord(slot_free[j], s_d));
     }
+    HIP_TRY(hipEventRecord(kv_free[b], s_c));  // after the task's last launch on s_c
     HIP_TRY(hipEventRecord(task_done[ti % 3], s_c));
   }
   for (hipStream_t s : R.s) HIP_TRY(hipStreamSynchronize(s));

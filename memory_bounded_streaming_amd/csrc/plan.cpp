@@ -161,6 +161,11 @@ cqsa_status build_tasks(Plan& p, std::string& why) {
       else
         task.segments.push_back({g * p.unit, p.unit, a * p.unit});
     }
+    // padding (CQSA_FLAG_PAD): cut every segment at N, drop those that start past it
+    std::vector<Segment> real;
+    for (const Segment& g : task.segments)
+      if (g.global_start < p.n) real.push_back({g.global_start, std::min(g.length, p.n - g.global_start), g.local_offset});
+    task.segments.swap(real);
     task.slot.resize(tu);
     for (int64_t a = 0; a < tu; ++a) task.slot[a] = seen[task.units[a]]++;
   }
@@ -212,7 +217,7 @@ void build_descriptors(Plan& p) {
       WorkItem di{}, si{};
       di.q_row0 = t.units[a] * p.unit;
       di.out_row0 = int64_t(t.slot[a]) * p.n + t.units[a] * p.unit;
-      di.q_len = si.q_len = static_cast<int32_t>(p.unit);
+      di.q_len = si.q_len = static_cast<int32_t>(p.unit_rows(t.units[a]));
       di.run0 = static_cast<int32_t>(p.dev_runs.size());
       si.run0 = static_cast<int32_t>(p.stream_runs.size());
       int64_t keys = 0;
@@ -222,17 +227,20 @@ void build_descriptors(Plan& p) {
         while (b < end) {
           int64_t e = b + 1;
           while (e < end && t.units[e] == t.units[e - 1] + 1) ++e;
-          const int64_t len = (e - b) * p.unit;
-          p.dev_runs.push_back({t.units[b] * p.unit, static_cast<int32_t>(len), 0});
-          p.stream_runs.push_back({b * p.unit, static_cast<int32_t>(len), 0});
-          keys += len;
+          // keys at or past N are padding: clip the run there (units are ascending in it)
+          const int64_t len = std::min((e - b) * p.unit, p.n - t.units[b] * p.unit);
+          if (len > 0) {
+            p.dev_runs.push_back({t.units[b] * p.unit, static_cast<int32_t>(len), 0});
+            p.stream_runs.push_back({b * p.unit, static_cast<int32_t>(len), 0});
+            keys += len;
+          }
           b = e;
         }
       }
       di.nrun = si.nrun = static_cast<int32_t>(p.dev_runs.size()) - di.run0;
       di.keys = si.keys = static_cast<int32_t>(std::min<int64_t>(keys, INT32_MAX));
-      p.dev_items.push_back(di);
-      p.stream_items.push_back(si);
+      if (di.q_len > 0) p.dev_items.push_back(di);  // a unit of padding only has no rows
+      p.stream_items.push_back(si);                 // indexed by (task, unit): kept, engine skips it
     }
   }
   // heaviest query blocks first in the one-launch device path (load balance only)
@@ -293,12 +301,18 @@ cqsa_status build_fixed(int64_t n, int heads, int d, cqsa_dtype dtype, const std
     prod_l *= l;
     if (prod_c > n) break;
   }
-  if (static_cast<int>(p.cs.size()) != static_cast<int>(ls.size()) || n % prod_c != 0) {
-    why = "N=" + std::to_string(n) + " is not a multiple of prod(c)";
+  if (static_cast<int>(p.cs.size()) != static_cast<int>(ls.size()) || prod_c > n) {
+    why = "N=" + std::to_string(n) + " is smaller than prod(c)";
+    return CQSA_EDIVIDE;
+  }
+  if (n % prod_c != 0 && !(flags & CQSA_FLAG_PAD)) {
+    why = "N=" + std::to_string(n) + " is not a multiple of prod(c)=" + std::to_string(prod_c) +
+          " (CQSA_FLAG_PAD pads it)";
     return CQSA_EDIVIDE;
   }
   p.n_units = prod_c;
-  p.unit = n / prod_c;
+  p.unit = (n + prod_c - 1) / prod_c;
+  p.n_pad = p.unit * prod_c;
   p.visits = prod_l;
   if (p.unit * prod_l > INT32_MAX) {
     why = "a task holds more than 2^31-1 tokens";
@@ -318,7 +332,7 @@ cqsa_status build_plan(int64_t n, int heads, int d, cqsa_dtype dtype, const int3
                        int64_t budget, uint32_t flags, Plan& out, std::string& why) {
   if (n < 1 || heads < 1 || (d != 64 && d != 128) || ls == nullptr || n_levels < 0 ||
       n_levels > CQSA_MAX_LEVELS || budget < 0 || (dtype != CQSA_BF16 && dtype != CQSA_F32) ||
-      (flags & ~(CQSA_FLAG_HOST_ACC | CQSA_FLAG_KV_SINGLE)) != 0) {
+      (flags & ~(CQSA_FLAG_HOST_ACC | CQSA_FLAG_KV_SINGLE | CQSA_FLAG_PAD)) != 0) {
     why = "invalid argument (need n>=1, heads>=1, head_dim 64 or 128, 0<=n_levels<=8, budget>=0, known dtype/flags)";
     return CQSA_EINVAL;
   }
@@ -335,11 +349,20 @@ cqsa_status build_plan(int64_t n, int heads, int d, cqsa_dtype dtype, const int3
       }
     return build_fixed(n, heads, d, dtype, levels, budget, flags, out, why);
   }
-  // auto: repeat l until the host-pinned path fits the budget
+  // auto: the undivided plan first; divide (repeating l) only while the host-pinned path
+  // does not fit the budget -- the out-of-memory recovery of the method
   const int l = ls[0];
   if (l < 2 || l > CQSA_MAX_L) {
     why = "auto levels need l in 2..10";
     return CQSA_EINVAL;
+  }
+  {
+    std::string w;
+    const cqsa_status st = build_fixed(n, heads, d, dtype, std::vector<int>{1}, budget, flags, out, w);
+    if (st != CQSA_EBUDGET) {
+      if (st != CQSA_OK) why = w;
+      return st;
+    }
   }
   std::vector<int> levels;
   cqsa_status last = CQSA_EBUDGET;

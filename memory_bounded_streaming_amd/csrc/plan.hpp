@@ -3,6 +3,7 @@
 // device-memory footprint model.  Pure C++17, no HIP dependency.
 #pragma once
 
+#include <algorithm>
 #include <cstdint>
 #include <mutex>
 #include <string>
@@ -46,7 +47,8 @@ struct Footprint {
 };
 
 struct Plan {
-  int64_t n = 0;
+  int64_t n = 0;                        // real tokens
+  int64_t n_pad = 0;                    // tokens the division covers (unit * n_units >= n)
   int heads = 0, d = 0;
   cqsa_dtype dtype = CQSA_BF16;
   std::vector<int> ls, cs;
@@ -78,6 +80,8 @@ struct Plan {
   int64_t row_part_bytes() const { return int64_t(heads) * (d + 2) * 4; }
   int64_t row_out_bytes() const { return int64_t(heads) * (d * elem_bytes() + 4); }
   int64_t task_tokens() const { return task_units * unit; }
+  // real query rows of global unit u (0 for a unit that is all padding)
+  int64_t unit_rows(int64_t u) const { return std::max<int64_t>(0, std::min(unit, n - u * unit)); }
 };
 
 // Byte size of each piece of the streamed path's workspace, in the order it is carved.

@@ -100,5 +100,5 @@ def sample_rows(n: int, count: int, seed: int, unit_tokens: int | None = None) -
     extra = []
     if unit_tokens:
         starts = np.arange(0, n, unit_tokens, dtype=np.int64)
-        extra = [starts, starts + unit_tokens - 1]
+        extra = [starts, np.minimum(starts + unit_tokens - 1, n - 1)]
     return np.unique(np.concatenate([rows] + extra))

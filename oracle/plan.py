@@ -34,6 +34,11 @@ R5  Recursion: R2-R4 are applied to each task's token list with the next
     level's l; admission is the AND of all levels' masks; the task id is
     mixed-radix, outer level most significant; tasks run in ascending id.
 R6  Unit = N / prod(c_k) tokens; every ownership boundary is unit aligned.
+R12 Padding (optional): an N >= prod(c_k) that is not a multiple of prod(c_k) is
+    divided as N_pad = ceil(N / prod(c_k)) * prod(c_k) tokens; positions >= N are padding.
+    They belong to no segment, no key run and no query block, so every real
+    query still meets every real key exactly once and the result is attention
+    over the N real tokens.
 """
 from __future__ import annotations
 
@@ -131,15 +136,21 @@ class Task:
                 runs.append([b, 1])
         return [tuple(r) for r in runs]
 
-    def segments(self, unit_tokens: int) -> list:
-        """Maximal globally contiguous pieces: (global_start, length, local_offset) in tokens."""
+    def segments(self, unit_tokens: int, n_real: int | None = None) -> list:
+        """Maximal globally contiguous pieces: (global_start, length, local_offset) in tokens.
+
+        With ``n_real`` (reading R12) the pieces are cut at the first padding token.
+        """
         segs = []
         for a, g in enumerate(self.units):
             if segs and segs[-1][0] + segs[-1][1] == g:
                 segs[-1][1] += 1
             else:
                 segs.append([g, 1, a])
-        return [(g * unit_tokens, n * unit_tokens, a * unit_tokens) for g, n, a in segs]
+        out = [(g * unit_tokens, n * unit_tokens, a * unit_tokens) for g, n, a in segs]
+        if n_real is not None:
+            out = [(g, min(ln, n_real - g), a) for g, ln, a in out if g < n_real]
+        return out
 
 
 @dataclass
@@ -151,6 +162,7 @@ class Plan:
     unit_tokens: int
     n_units: int
     tasks: list
+    n_pad: int = 0   # tokens the division covers (n_pad >= n; == n unless padded)
 
     def coverage(self) -> np.ndarray:
         """[U, U] int32: entry [p][q] is the id of the task owning (query unit p, key unit q).
@@ -183,7 +195,7 @@ class Plan:
         for task in self.tasks:
             out.append(task.tid)
             out += list(task.ids)
-            segs = task.segments(self.unit_tokens)
+            segs = task.segments(self.unit_tokens, self.n)
             out.append(len(segs))
             for s in segs:
                 out += list(s)
@@ -196,16 +208,19 @@ class Plan:
         return np.asarray(out, dtype=np.int64)
 
 
-def make_plan(n: int, ls: list) -> Plan:
-    """Build the plan for N tokens and per-level l values (readings R1-R6)."""
+def make_plan(n: int, ls: list, pad: bool = False) -> Plan:
+    """Build the plan for N tokens and per-level l values (readings R1-R6; R12 if pad)."""
     if n <= 0 or not ls:
         raise ValueError("need n > 0 and at least one level")
     sets = [difference_set(l) for l in ls]
     cs = [l * (l - 1) + 1 for l in ls]
     prod_c = int(np.prod(cs))
-    if n % prod_c:
+    if n % prod_c and not pad:
         raise DivideError(f"N={n} is not a multiple of prod(c)={prod_c}")
-    unit = n // prod_c
+    if prod_c > n:
+        raise DivideError(f"N={n} is smaller than prod(c)={prod_c}")
+    n_pad = -(-n // prod_c) * prod_c
+    unit = n_pad // prod_c
 
     # (global units, per-level chunk indices, per-level ids) of partially divided tasks
     frontier = [(list(range(prod_c)), [], ())]
@@ -230,4 +245,4 @@ def make_plan(n: int, ls: list) -> Plan:
         tasks.append(Task(tid=tid, ids=ids, units=units, chunk=chunks))
     tasks.sort(key=lambda t: t.tid)
     return Plan(n=n, ls=list(ls), cs=cs, sets=sets, unit_tokens=unit,
-                n_units=prod_c, tasks=tasks)
+                n_units=prod_c, tasks=tasks, n_pad=n_pad)

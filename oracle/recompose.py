@@ -30,13 +30,14 @@ __all__ = ["task_partials_fp64", "merge_fp64", "finalize_fp64", "recompose_fp64"
 
 
 def _key_tokens(plan: Plan, task, a: int) -> np.ndarray:
-    """Global token indices of the keys task admits for its local query unit a."""
+    """Global token indices of the keys task admits for its local query unit a
+    (padding positions >= N excluded, reading R12 of oracle.plan)."""
     u = plan.unit_tokens
     parts = []
     for b0, cnt in task.key_runs(a):
         for b in range(b0, b0 + cnt):
             g = task.units[b]
-            parts.append(np.arange(g * u, (g + 1) * u, dtype=np.int64))
+            parts.append(np.arange(g * u, min((g + 1) * u, plan.n), dtype=np.int64))
     if not parts:
         return np.zeros(0, dtype=np.int64)
     return np.concatenate(parts)
@@ -57,7 +58,7 @@ def task_partials_fp64(q, k, v, plan: Plan, task, dtype="f32", scale=None,
     out = {}
     for a, p in enumerate(task.units):
         if rows_of_unit is None:
-            rows = np.arange(p * u, (p + 1) * u, dtype=np.int64)
+            rows = np.arange(p * u, min((p + 1) * u, plan.n), dtype=np.int64)
         else:
             rows = np.asarray(rows_of_unit.get(p, []), dtype=np.int64)
         keys = _key_tokens(plan, task, a)

@@ -108,8 +108,11 @@ def test_c4_device_accumulator_does_not_fit_8gib():
 def test_auto_levels_follow_the_budget():
     with cqsa.Plan(12845056, 1, 128, cqsa.CQSA_BF16, [3], n_levels=0, budget_bytes=2 * GiB) as p:
         assert p.info["levels"] == 2 and p.info["l"] == [3, 3]
+    with cqsa.Plan(12845056, 1, 128, cqsa.CQSA_BF16, [3], n_levels=0, budget_bytes=16 * GiB) as p:
+        assert p.info["levels"] == 1 and p.info["l"] == [3]
+    # the undivided plan when it fits (nothing to recover from)
     with cqsa.Plan(12845056, 1, 128, cqsa.CQSA_BF16, [3], n_levels=0, budget_bytes=64 * GiB) as p:
-        assert p.info["levels"] == 1
+        assert p.info["levels"] == 1 and p.info["l"] == [1] and p.info["stream_workspace_bytes"] <= 64 * GiB
     with pytest.raises(cqsa.CqsaError) as e:  # a third level would not divide
         cqsa.Plan(12845056, 1, 128, cqsa.CQSA_BF16, [3], n_levels=0, budget_bytes=256 << 20)
     assert e.value.status == -4
@@ -179,3 +182,44 @@ def test_status_strings(lib):
     for s in (0, -1, -2, -3, -4, -5, -6, -7):
         assert cqsa.cqsa_status_string(s)
     assert "unknown" in cqsa.cqsa_status_string(42)
+
+
+PADDED_PLANS = [([3], 50), ([3], 8), ([3], 7 * 192 + 5), ([4], 100), ([2, 2], 20), ([3, 2], 100), ([2], 4),
+                ([2, 2, 2], 28), ([5], 21 * 64 - 1), ([3, 3], 12845055)]
+
+
+@pytest.mark.parametrize("levels,n", PADDED_PLANS)
+def test_padded_schedule_bit_exact(levels, n):
+    # reading R12 of the oracle planner: N is rounded up to the unit grid, segments stop at N
+    ref = make_plan(n, levels, pad=True)
+    with cqsa.Plan(n, 2, 64, cqsa.CQSA_BF16, levels, flags=cqsa.CQSA_FLAG_PAD) as p:
+        assert p.schedule().tobytes() == ref.serialize().tobytes()
+        assert p.coverage().tobytes() == ref.coverage().tobytes()
+        info = p.info
+        assert info["n_tokens"] == n and info["padded_tokens"] == ref.n_pad
+        assert info["unit_tokens"] == ref.unit_tokens and info["unit_tokens"] * info["n_units"] == ref.n_pad
+        assert info["useful_flop"] == pytest.approx(4.0 * n * n * 64 * 2)
+    with pytest.raises(cqsa.CqsaError) as e:
+        cqsa.Plan(n, 2, 64, cqsa.CQSA_BF16, levels)
+    assert e.value.status == -3
+
+
+def test_pad_flag_is_a_no_op_on_the_grid():
+    with cqsa.Plan(49, 1, 64, cqsa.CQSA_BF16, [3]) as a, \
+            cqsa.Plan(49, 1, 64, cqsa.CQSA_BF16, [3], flags=cqsa.CQSA_FLAG_PAD) as b:
+        assert a.schedule().tobytes() == b.schedule().tobytes()
+        assert a.info["padded_tokens"] == b.info["padded_tokens"] == 49
+    with pytest.raises(cqsa.CqsaError) as e:  # fewer tokens than units: no division at all
+        cqsa.Plan(5, 1, 64, cqsa.CQSA_BF16, [3], flags=cqsa.CQSA_FLAG_PAD)
+    assert e.value.status == -3
+
+
+def test_auto_levels_with_padding():
+    # an N off every grid still recovers once padding is allowed
+    with pytest.raises(cqsa.CqsaError) as e:
+        cqsa.Plan(12845057, 1, 128, cqsa.CQSA_BF16, [3], n_levels=0, budget_bytes=2 * GiB)
+    assert e.value.status == -3
+    with cqsa.Plan(12845057, 1, 128, cqsa.CQSA_BF16, [3], n_levels=0, budget_bytes=2 * GiB,
+                   flags=cqsa.CQSA_FLAG_PAD) as p:
+        assert p.info["l"] == [3, 3] and p.info["stream_workspace_bytes"] <= 2 * GiB
+        assert p.info["padded_tokens"] == 12845057 + 48

@@ -103,3 +103,28 @@ def test_partials_cover_each_pair_once_by_key_count():
             for a, p in enumerate(task.units):
                 total[p] += sum(c for _, c in task.key_runs(a))
         assert (total == plan.n_units).all()
+
+
+@pytest.mark.parametrize("ls,n", [([3], 50), ([3], 8), ([4], 100), ([2, 2], 20), ([3, 2], 100), ([2], 4), ([1], 5)])
+def test_padded_recompose_equals_dense_attention(ls, n):
+    # reading R12: positions past N are padding and are never attended
+    plan = make_plan(n, ls, pad=True)
+    assert plan.n == n and plan.n_pad >= n and plan.n_pad % plan.n_units == 0
+    assert plan.n_pad - n < plan.n_units
+    q, k, v = gen_qkv(300 + n, n, 2, 8, dtype="f32")
+    o_ref, lse_ref = attention_fp64(q, k, v, dtype="f32")
+    o, lse = recompose_fp64(q, k, v, plan, dtype="f32")
+    np.testing.assert_allclose(o, o_ref, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, lse_ref, rtol=1e-12)
+
+
+def test_padded_segments_stop_at_n():
+    plan = make_plan(50, [3], pad=True)  # 7 units of 8 tokens: 56 padded positions
+    assert plan.unit_tokens == 8
+    for task in plan.tasks:
+        for g, ln, off in task.segments(plan.unit_tokens, plan.n):
+            assert 0 < ln and g + ln <= 50
+    with pytest.raises(Exception):
+        make_plan(50, [3])
+    with pytest.raises(Exception):  # fewer tokens than units
+        make_plan(5, [3], pad=True)
