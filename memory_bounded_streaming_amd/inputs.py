@@ -65,7 +65,8 @@ def _fill_block(seed, tensor_index, block, n, h, d, dtype, out):
 
 def gen_tensor(seed: int, tensor_index: int, n: int, h: int, d: int, dtype: str = "bf16",
                out: np.ndarray | None = None) -> np.ndarray:
-    """One of Q (0), K (1), V (2) as [n, h, d]; float32, or uint16 bf16 bits.
+    """One of Q (0), K (1), V (2) or an upstream gradient dO (3) as [n, h, d]; float32,
+    or uint16 bf16 bits.
 
     ``out`` may be a preallocated array (e.g. a view of pinned host memory).
     """

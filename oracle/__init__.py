@@ -27,6 +27,7 @@ Modules
 ``plan``       reference CQS planner: difference set, subsequences, recursion,
                ownership mask, coverage table, canonical serialisation.
 ``recompose``  per-task float64 partials and their merge (the method's steps).
+``backward``   gradients of attention (the definition) and their per-task sums.
 ``tolerance``  the error metrics the parity tests apply.
 
 Every function states which of the above it follows.  Readings taken where the

@@ -1,0 +1,137 @@
+"""Gradients of exact softmax attention, and their CQS decomposition, in float64
+(oracle; test infrastructure only).
+
+"Stream-CQSA: Exact Out-of-Memory Recovery for Attention" (arXiv 2604.20819),
+abstract: the decomposition is exact for the backward pass as well as the
+forward, with gradient error on par with FlashAttention-2.  The pages give no
+formulas for it, so the oracle is the definition -- the derivative of
+
+    O[i] = sum_j P_ij V[j],   P_ij = exp(s_ij - LSE_i),   s_ij = scale <Q[i], K[j]>
+
+for an upstream gradient dO, per head:
+
+    dV[j]  = sum_i P_ij dO[i]
+    dP_ij  = <dO[i], V[j]>
+    Delta_i = sum_j P_ij dP_ij  (= <dO[i], O[i]>)
+    dS_ij  = P_ij (dP_ij - Delta_i)
+    dQ[i]  = scale sum_j dS_ij K[j]
+    dK[j]  = scale sum_i dS_ij Q[i]
+
+(the chain rule through the softmax: d softmax = P (dP - <P, dP>)).
+
+CQS decomposition (reading R15): every (query, key) pair is admitted by exactly
+one task (readings R4/R5 of ``oracle.plan``), and with the final LSE each pair's
+terms above no longer depend on any other pair, so each gradient is the sum over
+tasks of the terms of the pairs the task admits; tasks are summed in ascending
+id.  Nothing is rescaled across tasks (the forward's merge is not needed).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .attention import default_scale, to_f64
+from .plan import Plan
+
+__all__ = ["attention_backward_fp64", "task_backward_fp64", "recompose_backward_fp64"]
+
+
+def _dense_head(q, k, v, do, scale):
+    """All of the definition for one head: (dq, dk, dv, lse) in float64, N x N at once."""
+    s = (q @ k.T) * scale
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    lse = m[:, 0] + np.log(e.sum(axis=1))
+    p = np.exp(s - lse[:, None])
+    dv = p.T @ do
+    dp = do @ v.T
+    delta = (p * dp).sum(axis=1)
+    ds = p * (dp - delta[:, None])
+    return scale * (ds @ k), scale * (ds.T @ q), dv, lse
+
+
+def attention_backward_fp64(q, k, v, do, dtype="f32", scale=None):
+    """(dQ, dK, dV) [N, H, d] float64 of exact attention for upstream gradient dO.
+
+    q, k, v, do: [N, H, d] float32 arrays or bf16 bit patterns (uint16), widened
+    exactly.  Dense per head (N x N scores), for the sizes the parity tests check
+    element by element.
+    """
+    n, h_count, d = q.shape
+    if scale is None:
+        scale = default_scale(d)
+    out = [np.zeros((n, h_count, d)) for _ in range(3)]
+    for h in range(h_count):
+        qh, kh, vh, doh = (to_f64(x[:, h, :], dtype) for x in (q, k, v, do))
+        dq, dk, dv, _ = _dense_head(qh, kh, vh, doh, scale)
+        out[0][:, h], out[1][:, h], out[2][:, h] = dq, dk, dv
+    return tuple(out)
+
+
+def _unit_rows(plan: Plan, p: int) -> np.ndarray:
+    u = plan.unit_tokens
+    return np.arange(p * u, min((p + 1) * u, plan.n), dtype=np.int64)
+
+
+def task_backward_fp64(q, k, v, do, lse, delta, plan: Plan, task, dtype="f32", scale=None):
+    """Gradient terms of the pairs one task admits.
+
+    lse [H, N] and delta [H, N] are the final (natural-log) LSE and Delta rows.
+    Returns three dicts keyed by global unit p: dQ terms of p's rows as queries,
+    dK and dV terms of p's rows as keys, each [rows, H, d].
+    """
+    n, h_count, d = q.shape
+    if scale is None:
+        scale = default_scale(d)
+    dq_t, dk_t, dv_t = {}, {}, {}
+    for p in task.units:
+        r = _unit_rows(plan, p).size
+        for acc in (dq_t, dk_t, dv_t):
+            acc[p] = np.zeros((r, h_count, d))
+    for a, pa in enumerate(task.units):
+        qi = _unit_rows(plan, pa)
+        if qi.size == 0:
+            continue
+        for b, pb in enumerate(task.units):
+            if not task.admitted(a, b):
+                continue
+            kj = _unit_rows(plan, pb)
+            if kj.size == 0:
+                continue
+            for h in range(h_count):
+                qh, doh = to_f64(q[qi, h], dtype), to_f64(do[qi, h], dtype)
+                kh, vh = to_f64(k[kj, h], dtype), to_f64(v[kj, h], dtype)
+                p_ = np.exp((qh @ kh.T) * scale - lse[h, qi][:, None])
+                dp = doh @ vh.T
+                ds = p_ * (dp - delta[h, qi][:, None])
+                dq_t[pa][:, h] += scale * (ds @ kh)
+                dk_t[pb][:, h] += scale * (ds.T @ qh)
+                dv_t[pb][:, h] += p_.T @ doh
+    return dq_t, dk_t, dv_t
+
+
+def recompose_backward_fp64(q, k, v, do, plan: Plan, dtype="f32", scale=None):
+    """Sum every task's gradient terms in ascending task id: (dQ, dK, dV) [N, H, d].
+
+    The final LSE and Delta come from the dense definition (they are inputs of a
+    backward pass: the forward's saved statistics).
+    """
+    n, h_count, d = q.shape
+    if scale is None:
+        scale = default_scale(d)
+    lse = np.zeros((h_count, n))
+    delta = np.zeros((h_count, n))
+    for h in range(h_count):
+        qh, kh, vh, doh = (to_f64(x[:, h, :], dtype) for x in (q, k, v, do))
+        s = (qh @ kh.T) * scale
+        m = s.max(axis=1, keepdims=True)
+        lse[h] = m[:, 0] + np.log(np.exp(s - m).sum(axis=1))
+        o = np.exp(s - lse[h][:, None]) @ vh
+        delta[h] = (doh * o).sum(axis=1)
+    grads = [np.zeros((n, h_count, d)) for _ in range(3)]
+    for task in plan.tasks:
+        parts = task_backward_fp64(q, k, v, do, lse, delta, plan, task, dtype=dtype, scale=scale)
+        for g, part in zip(grads, parts):
+            for p, val in part.items():
+                rows = _unit_rows(plan, p)
+                g[rows] += val
+    return tuple(grads)
