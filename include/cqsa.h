@@ -219,6 +219,39 @@ cqsa_status cqsa_forward(const cqsa_plan* plan, const void* q, const void* k, co
                          void* o, float* lse, cqsa_residency res, void* workspace,
                          int64_t workspace_bytes, void* stream, cqsa_stats* stats);
 
+/*
+ * Device workspace bytes cqsa_backward needs for res (CQSA_RES_DEVICE only): Delta
+ * [H][N] fp32, for bf16 three transposed copies (Q, K, dO) [H][d][round_up(N, 64)], and
+ * the visit slots of dQ, dK, dV [V][N][H][d] fp32 (V = prod(l_k)).
+ * Errors: EINVAL (NULL, or a residency the backward does not run on).
+ */
+cqsa_status cqsa_backward_workspace_size(const cqsa_plan* plan, cqsa_residency res, int64_t* bytes);
+
+/*
+ * Backward of the CQS forward: gradients of O = softmax(Q K^T / sqrt(d)) V for an
+ * upstream gradient dO ("Stream-CQSA: Exact Out-of-Memory Recovery for Attention",
+ * abstract: the decomposition is exact for the backward pass as well).  With the
+ * forward's final LSE every admitted (query, key) pair contributes independently:
+ *     P = exp(s - LSE), Delta_i = <dO_i, O_i>, dS = P (dO_i.v_j - Delta_i),
+ *     dV_j += P dO_i, dK_j += dS q_i / sqrt(d), dQ_i += dS k_j / sqrt(d),
+ * and the CQS Mask gives each pair to exactly one task, so each task's terms go to
+ * the rows' visit slots and the slots are summed in ascending task order
+ * (deterministic; no rescaling across tasks).
+ *   q, k, v, o, d_o: device [N, H, d] in the plan's dtype (read only); o and lse are
+ *     the forward's outputs (lse: device float32 [H, N], natural log).
+ *   dq, dk, dv: device [N, H, d] in the plan's dtype (written; round to nearest even).
+ *   res: CQSA_RES_DEVICE (CQSA_RES_HOST_PINNED is rejected with EINVAL).
+ *   workspace: device buffer >= cqsa_backward_workspace_size bytes, or NULL (the
+ *     library allocates and frees it).  Stream-ordered like cqsa_forward.
+ *   stats: optional; t_attn_ms = the two gradient kernels, t_merge_ms = the Delta /
+ *     transpose pass and the slot sums, useful_flop = 10 N^2 d H.
+ * Errors: EINVAL, ESMALL, EBUDGET (workspace over the plan's budget), EHIP, ENOMEM.
+ */
+cqsa_status cqsa_backward(const cqsa_plan* plan, const void* q, const void* k, const void* v,
+                          const void* o, const float* lse, const void* d_o, void* dq, void* dk,
+                          void* dv, cqsa_residency res, void* workspace, int64_t workspace_bytes,
+                          void* stream, cqsa_stats* stats);
+
 /* Static text for a status code. */
 const char* cqsa_status_string(cqsa_status status);
 

@@ -21,7 +21,7 @@ __all__ = [
     "CQSA_FLAG_HOST_ACC", "CQSA_FLAG_KV_SINGLE", "CQSA_FLAG_PAD", "MODE_NAMES",
     "cqsa_version", "cqsa_difference_set", "cqsa_plan_create", "cqsa_plan_info_get", "cqsa_plan_schedule",
     "cqsa_plan_coverage", "cqsa_plan_destroy", "cqsa_workspace_size", "cqsa_partials", "cqsa_merge",
-    "cqsa_forward", "cqsa_status_string", "cqsa_last_error", "Plan",
+    "cqsa_forward", "cqsa_backward_workspace_size", "cqsa_backward", "cqsa_status_string", "cqsa_last_error", "Plan",
 ]
 
 CQSA_BF16, CQSA_F32 = 0, 1
@@ -82,6 +82,9 @@ EXPORTS = {
     "cqsa_merge": (ctypes.c_int, [ctypes.c_void_p] + [ctypes.c_void_p] * 5),
     "cqsa_forward": (ctypes.c_int, [ctypes.c_void_p] + [ctypes.c_void_p] * 5 +
                      [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.POINTER(Stats)]),
+    "cqsa_backward_workspace_size": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_int64)]),
+    "cqsa_backward": (ctypes.c_int, [ctypes.c_void_p] + [ctypes.c_void_p] * 9 +
+                      [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.POINTER(Stats)]),
     "cqsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "cqsa_last_error": (ctypes.c_char_p, []),
 }
@@ -223,6 +226,25 @@ def cqsa_forward(plan: int, q, k, v, o, lse=None, residency: int = CQSA_RES_DEVI
     return {name: getattr(st, name) for name, _ in Stats._fields_}
 
 
+def cqsa_backward_workspace_size(plan: int, residency: int = CQSA_RES_DEVICE) -> int:
+    out = ctypes.c_int64()
+    _check(load().cqsa_backward_workspace_size(plan, residency, ctypes.byref(out)))
+    return out.value
+
+
+def cqsa_backward(plan: int, q, k, v, o, lse, d_o, dq, dk, dv, residency: int = CQSA_RES_DEVICE, workspace=None,
+                  workspace_bytes: int = 0, stream=None, stats: bool = False) -> dict | None:
+    st = Stats() if stats else None
+    if workspace is not None and workspace_bytes == 0 and hasattr(workspace, "numel"):
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(load().cqsa_backward(plan, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(d_o), _ptr(dq), _ptr(dk),
+                                _ptr(dv), residency, _ptr(workspace), workspace_bytes, _stream(stream),
+                                ctypes.byref(st) if st is not None else None))
+    if st is None:
+        return None
+    return {name: getattr(st, name) for name, _ in Stats._fields_}
+
+
 class Plan:
     """Owning wrapper of a plan handle (the same calls, with the handle bound)."""
 
@@ -247,6 +269,12 @@ class Plan:
 
     def forward(self, *a, **kw):
         return cqsa_forward(self.handle, *a, **kw)
+
+    def backward_workspace_size(self, residency=CQSA_RES_DEVICE):
+        return cqsa_backward_workspace_size(self.handle, residency)
+
+    def backward(self, *a, **kw):
+        return cqsa_backward(self.handle, *a, **kw)
 
     def close(self):
         if self.handle:

@@ -218,4 +218,30 @@ cqsa_status cqsa_forward(const cqsa_plan* plan, const void* q, const void* k, co
   });
 }
 
+
+cqsa_status cqsa_backward_workspace_size(const cqsa_plan* plan, cqsa_residency res, int64_t* bytes) {
+  return guarded([&]() -> cqsa_status {
+    if (plan == nullptr || bytes == nullptr) return fail(CQSA_EINVAL, "NULL argument");
+    if (res != CQSA_RES_DEVICE) return fail(CQSA_EINVAL, "the backward pass runs on device-resident tensors only");
+    *bytes = plan->p.bwd_device_ws;
+    return ok();
+  });
+}
+
+cqsa_status cqsa_backward(const cqsa_plan* plan, const void* q, const void* k, const void* v, const void* o,
+                          const float* lse, const void* d_o, void* dq, void* dk, void* dv, cqsa_residency res,
+                          void* workspace, int64_t workspace_bytes, void* stream, cqsa_stats* stats) {
+  return guarded([&]() -> cqsa_status {
+    if (plan == nullptr || q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr ||
+        d_o == nullptr || dq == nullptr || dk == nullptr || dv == nullptr)
+      return fail(CQSA_EINVAL, "NULL argument");
+    if (res != CQSA_RES_DEVICE && res != CQSA_RES_HOST_PINNED) return fail(CQSA_EINVAL, "unknown residency");
+    if (workspace != nullptr && workspace_bytes <= 0) return fail(CQSA_EINVAL, "workspace size must be positive");
+    std::string why;
+    const cqsa_status s = cqsa::run_backward(plan->p, q, k, v, o, lse, d_o, dq, dk, dv, res, workspace,
+                                             workspace_bytes, static_cast<hipStream_t>(stream), stats, why);
+    return s == CQSA_OK ? ok() : fail(s, why);
+  });
+}
+
 }  // extern "C"

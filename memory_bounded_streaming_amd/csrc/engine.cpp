@@ -542,6 +542,137 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
 
 }  // namespace
 
+// ----------------------------------------------------------------------------------
+// backward, device-resident: prep (Delta, transposed copies), dK/dV terms and dQ terms
+// of every (task, unit) into visit slots, then one slot sum per gradient
+// ----------------------------------------------------------------------------------
+cqsa_status run_backward(const Plan& p, const void* q, const void* k, const void* v, const void* o,
+                         const float* lse, const void* d_o, void* dq, void* dk, void* dv, cqsa_residency res,
+                         void* ws, int64_t ws_bytes, hipStream_t stream, cqsa_stats* stats, std::string& why) {
+  if (res != CQSA_RES_DEVICE) {
+    why = "the backward pass runs on device-resident tensors only";
+    return CQSA_EINVAL;
+  }
+  if (p.budget > 0 && p.bwd_device_ws > p.budget) {
+    why = "device-resident backward needs " + std::to_string(p.bwd_device_ws) + " workspace bytes, over the budget";
+    return CQSA_EBUDGET;
+  }
+  DeviceTables t{};
+  cqsa_status st = device_tables(p, t, why);
+  if (st != CQSA_OK) return st;
+  const BwdLayout L = bwd_layout(p);
+  bool owned = false;
+  if (ws == nullptr) {
+    HIP_TRY(hipMalloc(&ws, L.total));
+    owned = true;
+  } else if (ws_bytes < L.total) {
+    why = "workspace of " + std::to_string(ws_bytes) + " bytes, need " + std::to_string(L.total);
+    return CQSA_ESMALL;
+  }
+  struct Release {
+    void* p;
+    hipStream_t s;
+    ~Release() {
+      if (p) {
+        (void)hipStreamSynchronize(s);
+        (void)hipFree(p);
+      }
+    }
+  } release{owned ? ws : nullptr, stream};
+  char* cur = static_cast<char*>(ws);
+  auto take = [&](int64_t bytes) {
+    char* r = cur;
+    cur += bytes;
+    return r;
+  };
+  float* delta = reinterpret_cast<float*>(take(L.delta));
+  void* qt = L.trans ? take(L.trans) : nullptr;
+  void* kt = L.trans ? take(L.trans) : nullptr;
+  void* dot = L.trans ? take(L.trans) : nullptr;
+  float* dq_s = reinterpret_cast<float*>(take(L.slots));
+  float* dk_s = reinterpret_cast<float*>(take(L.slots));
+  float* dv_s = reinterpret_cast<float*>(take(L.slots));
+
+  PhaseTimer tm;
+  tm.on = stats != nullptr;
+  hipEvent_t ev;
+  const auto t0 = std::chrono::steady_clock::now();
+  PrepLaunch pr{};
+  pr.dtype = p.dtype;
+  pr.d = p.d;
+  pr.heads = p.heads;
+  pr.n = p.n;
+  pr.np = p.bwd_np;
+  pr.q = q;
+  pr.k = k;
+  pr.o = o;
+  pr.d_o = d_o;
+  pr.delta = delta;
+  pr.qt = qt;
+  pr.kt = kt;
+  pr.dot = dot;
+  HIP_TRY(tm.begin(PH_MERGE, stream, ev));
+  HIP_TRY(launch_bwd_prep(pr, stream));
+  HIP_TRY(tm.end(PH_MERGE, stream));
+
+  BwdLaunch b{};
+  b.dtype = p.dtype;
+  b.d = p.d;
+  b.heads = p.heads;
+  b.n = p.n;
+  b.np = p.bwd_np;
+  b.q = q;
+  b.k = k;
+  b.v = v;
+  b.d_o = d_o;
+  b.qt = qt;
+  b.kt = kt;
+  b.dot = dot;
+  b.lse = lse;
+  b.delta = delta;
+  b.dq_out = dq_s;
+  b.dk_out = dk_s;
+  b.dv_out = dv_s;
+  b.items = t.dev_items;
+  b.runs = t.dev_runs;
+  b.n_items = static_cast<int>(p.dev_items.size());
+  b.q_len = static_cast<int>(p.unit);
+  b.scale = static_cast<float>(1.0 / std::sqrt(double(p.d)));
+  HIP_TRY(tm.begin(PH_ATTN, stream, ev));
+  HIP_TRY(launch_bwd_dkdv(b, stream));
+  HIP_TRY(launch_bwd_dq(b, stream));
+  HIP_TRY(tm.end(PH_ATTN, stream));
+
+  SumLaunch sl{};
+  sl.dtype = p.dtype;
+  sl.d = p.d;
+  sl.heads = p.heads;
+  sl.rows = p.n;
+  sl.stride = p.n * p.heads * int64_t(p.d);
+  sl.nslot = static_cast<int>(p.visits);
+  HIP_TRY(tm.begin(PH_MERGE, stream, ev));
+  const float* ins[3] = {dq_s, dk_s, dv_s};
+  void* outs[3] = {dq, dk, dv};
+  for (int g = 0; g < 3; ++g) {
+    sl.in = ins[g];
+    sl.out = outs[g];
+    HIP_TRY(launch_sum_slots(sl, stream));
+  }
+  HIP_TRY(tm.end(PH_MERGE, stream));
+  if (owned || stats) HIP_TRY(hipStreamSynchronize(stream));
+  if (stats) {
+    std::memset(stats, 0, sizeof(*stats));
+    stats->t_total_ms = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+    stats->t_attn_ms = tm.total(PH_ATTN);
+    stats->t_merge_ms = tm.total(PH_MERGE);
+    stats->peak_device_bytes = L.total + t.bytes;
+    stats->n_attn_launches = 2;
+    stats->n_merge_launches = 4;
+    stats->useful_flop = 10.0 * double(p.n) * double(p.n) * p.d * p.heads;
+  }
+  return CQSA_OK;
+}
+
 cqsa_status run_forward(const Plan& p, const void* q, const void* k, const void* v, void* o, float* lse,
                         cqsa_residency res, void* ws, int64_t ws_bytes, hipStream_t stream, cqsa_stats* stats,
                         std::string& why) {

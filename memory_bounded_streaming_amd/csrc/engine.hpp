@@ -26,6 +26,10 @@ cqsa_status run_partials(const Plan& p, const void* q, const void* k, const void
                          float* ml_out, hipStream_t stream, std::string& why);
 cqsa_status run_merge(const Plan& p, const float* n_in, const float* ml_in, void* o, float* lse,
                       hipStream_t stream, std::string& why);
+// Gradients dQ, dK, dV of the forward for upstream gradient d_o (device-resident).
+cqsa_status run_backward(const Plan& p, const void* q, const void* k, const void* v, const void* o,
+                         const float* lse, const void* d_o, void* dq, void* dk, void* dv, cqsa_residency res,
+                         void* ws, int64_t ws_bytes, hipStream_t stream, cqsa_stats* stats, std::string& why);
 cqsa_status run_forward(const Plan& p, const void* q, const void* k, const void* v, void* o, float* lse,
                         cqsa_residency res, void* ws, int64_t ws_bytes, hipStream_t stream,
                         cqsa_stats* stats, std::string& why);

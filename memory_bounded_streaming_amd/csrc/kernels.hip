@@ -14,16 +14,15 @@
 // this library's own for CDNA4 wave64 hardware.
 #include <hip/hip_runtime.h>
 
+#include "device_common.hpp"
 #include "kernels.hpp"
 
 namespace cqsa {
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef unsigned short u16;
-typedef unsigned int u32;
+using namespace dev;
+
 
 struct AttnParams {
   const void* q;
@@ -38,16 +37,6 @@ struct AttnParams {
   float scale_log2;
 };
 
-// Workgroups are dealt round-robin to the 8 XCDs; renumber them so that each XCD
-// receives one contiguous range of tiles (tiles of one query block and head share
-// their K/V stream, which then stays in that XCD's L2).
-__device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t grid) {
-  const int64_t q = grid / 8, r = grid % 8;
-  const int64_t x = b % 8, k = b / 8;
-  return x * q + (x < r ? x : r) + k;
-}
-
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
 // ---------------------------------------------------------------------------------
 // bf16 partials on MFMA.  Workgroup = 8 wave64 = 256 query rows (32 per wave); all
@@ -71,7 +60,6 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast
 // ---------------------------------------------------------------------------------
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLazyRescale = 8.0f;  // log2 units
 
@@ -91,43 +79,6 @@ struct Bf16Tile {
   static_assert(CPT >= 1 && KT * DCH == CPT * NT, "tile split");
 };
 
-// Cursor over the tiles of an item's key runs.  The current run's start and length
-// are kept in (scalar) registers and reloaded only when the cursor enters a new run.
-struct TileCursor {
-  int run;        // index of the current run (nrun when exhausted)
-  int k0;         // first key of the tile within the run
-  int len;        // length of the current run
-  int64_t start;  // first key row of the current run
-};
-
-__device__ __forceinline__ void cursor_settle(TileCursor& c, const KeyRun* runs, int nrun) {
-  while (c.run < nrun) {
-    const KeyRun r = runs[c.run];
-    if (r.len > 0) {
-      c.start = r.start;
-      c.len = r.len;
-      return;
-    }
-    ++c.run;
-  }
-  c.len = 0;
-  c.start = 0;
-}
-
-__device__ __forceinline__ TileCursor cursor_begin(const KeyRun* runs, int nrun) {
-  TileCursor c{0, 0, 0, 0};
-  cursor_settle(c, runs, nrun);
-  return c;
-}
-
-__device__ __forceinline__ void cursor_next(TileCursor& c, const KeyRun* runs, int nrun, int kt) {
-  c.k0 += kt;
-  if (c.k0 >= c.len) {
-    ++c.run;
-    c.k0 = 0;
-    cursor_settle(c, runs, nrun);
-  }
-}
 
 template <int D>
 __global__ __launch_bounds__(512) void attn_partial_bf16(AttnParams P) {
@@ -429,19 +380,6 @@ struct MergeParams {
   int64_t lse_stride, lse_row0;
 };
 
-__device__ __forceinline__ void store_out(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
-
-__device__ __forceinline__ u32 bf16_rne(float x) {
-  const u32 u = __builtin_bit_cast(u32, x);
-  if ((u & 0x7F800000u) == 0x7F800000u) return (u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u);  // inf / nan
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
-__device__ __forceinline__ void store_out(u16* p, float4 v) {
-  const u32 a = bf16_rne(v.x) | (bf16_rne(v.y) << 16);
-  const u32 b = bf16_rne(v.z) | (bf16_rne(v.w) << 16);
-  *reinterpret_cast<uint2*>(p) = make_uint2(a, b);
-}
 
 template <int D, typename OutT>
 __global__ __launch_bounds__(256) void merge_partials(MergeParams P) {

@@ -52,4 +52,65 @@ int attn_query_tile(cqsa_dtype dtype);
 hipError_t launch_attn(const AttnLaunch& a, hipStream_t stream);
 hipError_t launch_merge(const MergeLaunch& m, hipStream_t stream);
 
+// ---- backward ----
+// Delta[h][i] = <dO[i,h,:], O[i,h,:]> (fp32); for bf16 also Q, K, dO transposed to
+// [H][d][np] (np >= n rounded up to 64, a multiple of 8; tokens past n are zero).
+struct PrepLaunch {
+  cqsa_dtype dtype;
+  int d, heads;
+  int64_t n, np;
+  const void* q;
+  const void* k;
+  const void* o;
+  const void* d_o;
+  float* delta;        // [H][n]
+  void* qt;            // bf16 only
+  void* kt;
+  void* dot;
+};
+
+// Gradient terms of the pairs the items admit, written to visit slots
+// ([slots][n][H][d] fp32, row = item.out_row0 + i).  dK/dV launches treat an item's rows
+// as keys and its runs as admitted query runs; dQ launches the other way round.
+struct BwdLaunch {
+  cqsa_dtype dtype;
+  int d, heads;
+  int64_t n, np;
+  const void* q;       // [n][H][d] bases (rows as in the descriptors)
+  const void* k;
+  const void* v;
+  const void* d_o;
+  const void* qt;      // bf16: transposed copies from the prep kernel
+  const void* kt;
+  const void* dot;
+  const float* lse;    // [H][n] natural log
+  const float* delta;  // [H][n]
+  float* dq_out;
+  float* dk_out;
+  float* dv_out;
+  const WorkItem* items;
+  const KeyRun* runs;
+  int n_items;
+  int q_len;           // rows of every item in this launch (upper bound)
+  float scale;
+};
+
+// out[i] = sum over s < nslot of in[s * stride + i] in slot order, as dtype.
+struct SumLaunch {
+  cqsa_dtype dtype;
+  int d, heads;
+  int64_t rows;
+  const float* in;
+  int64_t stride;      // floats between slots
+  int nslot;
+  void* out;
+};
+
+int bwd_key_tile(cqsa_dtype dtype);
+int bwd_query_tile(cqsa_dtype dtype);
+hipError_t launch_bwd_prep(const PrepLaunch& a, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const BwdLaunch& a, hipStream_t stream);
+hipError_t launch_bwd_dq(const BwdLaunch& a, hipStream_t stream);
+hipError_t launch_sum_slots(const SumLaunch& a, hipStream_t stream);
+
 }  // namespace cqsa

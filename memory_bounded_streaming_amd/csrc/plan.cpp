@@ -86,6 +86,15 @@ StreamLayout stream_layout(const Plan& p, bool acc_on_device, int kv_buffers) {
   return s;
 }
 
+BwdLayout bwd_layout(const Plan& p) {
+  BwdLayout b{};
+  b.delta = align_up(int64_t(p.heads) * p.n * 4);
+  b.trans = p.dtype == CQSA_BF16 ? align_up(int64_t(p.heads) * p.d * p.bwd_np * 2) : 0;
+  b.slots = align_up(p.visits * p.n * p.heads * int64_t(p.d) * 4);
+  b.total = b.delta + 3 * b.trans + 3 * b.slots;
+  return b;
+}
+
 namespace {
 
 // Every innermost task with its units, per-level chunk of each local unit, admitted
@@ -323,6 +332,8 @@ cqsa_status build_fixed(int64_t n, int heads, int d, cqsa_dtype dtype, const std
   build_schedule(p);
   build_descriptors(p);
   p.device_ws = align_up(p.visits * p.n * heads * int64_t(d) * 4) + align_up(p.visits * p.n * heads * int64_t(2) * 4);
+  p.bwd_np = (n + 63) / 64 * 64;
+  p.bwd_device_ws = bwd_layout(p).total;
   return choose_mode(p, why);
 }
 

@@ -69,6 +69,8 @@ struct Plan {
 
   Footprint stream_fp{};
   int64_t device_ws = 0;                // slots bytes of the device-resident path
+  int64_t bwd_np = 0;                   // row pitch (tokens) of the backward's transposed copies
+  int64_t bwd_device_ws = 0;            // workspace bytes of the device-resident backward
   int64_t host_acc_bytes = 0;
 
   // device copies of the descriptor tables, uploaded lazily per device
@@ -83,6 +85,15 @@ struct Plan {
   // real query rows of global unit u (0 for a unit that is all padding)
   int64_t unit_rows(int64_t u) const { return std::max<int64_t>(0, std::min(unit, n - u * unit)); }
 };
+
+// Byte size of each piece of the device-resident backward's workspace, in carve order.
+struct BwdLayout {
+  int64_t delta;        // [H][N] fp32
+  int64_t trans;        // one transposed copy [H][d][np] bf16 (0 for fp32 inputs)
+  int64_t slots;        // one gradient's visit slots [V][N][H][d] fp32
+  int64_t total;        // delta + 3 trans + 3 slots
+};
+BwdLayout bwd_layout(const Plan& p);
 
 // Byte size of each piece of the streamed path's workspace, in the order it is carved.
 struct StreamLayout {

@@ -32,7 +32,7 @@ import numpy as np
 from .attention import default_scale, to_f64
 from .plan import Plan
 
-__all__ = ["attention_backward_fp64", "task_backward_fp64", "recompose_backward_fp64"]
+__all__ = ["attention_backward_fp64", "task_backward_fp64", "recompose_backward_fp64", "dq_rows_fp64"]
 
 
 def _dense_head(q, k, v, do, scale):
@@ -135,3 +135,45 @@ def recompose_backward_fp64(q, k, v, do, plan: Plan, dtype="f32", scale=None):
                 rows = _unit_rows(plan, p)
                 g[rows] += val
     return tuple(grads)
+
+
+def dq_rows_fp64(q, k, v, do, rows, dtype="f32", scale=None, key_block=16384):
+    """dQ of selected query rows only (the definition restricted to those rows).
+
+    Needs each row's own LSE and Delta, which depend on that row alone, so the cost is
+    O(rows x N x d) per head: usable at sizes where the dense gradients are not.
+    Two passes over key blocks: (max, sum) for LSE and O, then the dQ sum.
+    Returns dQ [R, H, d] float64.
+    """
+    n, h_count, d = q.shape
+    if scale is None:
+        scale = default_scale(d)
+    rows = np.asarray(rows, dtype=np.int64)
+    out = np.zeros((rows.size, h_count, d))
+    for h in range(h_count):
+        qh = to_f64(q[rows, h, :], dtype)
+        doh = to_f64(do[rows, h, :], dtype)
+        m = np.full(rows.size, -np.inf)
+        for j0 in range(0, n, key_block):
+            kb = to_f64(k[j0:j0 + key_block, h, :], dtype)
+            m = np.maximum(m, ((qh @ kb.T) * scale).max(axis=1))
+        l = np.zeros(rows.size)
+        o = np.zeros((rows.size, d))
+        for j0 in range(0, n, key_block):
+            kb = to_f64(k[j0:j0 + key_block, h, :], dtype)
+            vb = to_f64(v[j0:j0 + key_block, h, :], dtype)
+            e = np.exp((qh @ kb.T) * scale - m[:, None])
+            l += e.sum(axis=1)
+            o += e @ vb
+        o /= l[:, None]
+        lse = m + np.log(l)
+        delta = (doh * o).sum(axis=1)
+        acc = np.zeros((rows.size, d))
+        for j0 in range(0, n, key_block):
+            kb = to_f64(k[j0:j0 + key_block, h, :], dtype)
+            vb = to_f64(v[j0:j0 + key_block, h, :], dtype)
+            p = np.exp((qh @ kb.T) * scale - lse[:, None])
+            ds = p * (doh @ vb.T - delta[:, None])
+            acc += ds @ kb
+        out[:, h, :] = scale * acc
+    return out

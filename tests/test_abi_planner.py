@@ -31,7 +31,7 @@ def _header_symbols():
 
 def test_library_exports_every_declared_symbol(lib):
     names = _header_symbols()
-    assert len(names) == 13
+    assert len(names) == 15
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(cqsa.EXPORTS)
@@ -223,3 +223,19 @@ def test_auto_levels_with_padding():
                    flags=cqsa.CQSA_FLAG_PAD) as p:
         assert p.info["l"] == [3, 3] and p.info["stream_workspace_bytes"] <= 2 * GiB
         assert p.info["padded_tokens"] == 12845057 + 48
+
+
+def test_backward_workspace_size_and_argument_errors(lib):
+    n, h, d = 7 * 100, 3, 128
+    with cqsa.Plan(n, h, d, cqsa.CQSA_BF16, [3]) as p:
+        np_ = -(-n // 64) * 64
+        al = lambda x: -(-x // 256) * 256  # noqa: E731
+        want = al(h * n * 4) + 3 * al(h * d * np_ * 2) + 3 * al(3 * n * h * d * 4)
+        assert p.backward_workspace_size() == want
+        with pytest.raises(cqsa.CqsaError) as e:
+            p.backward_workspace_size(cqsa.CQSA_RES_HOST_PINNED)
+        assert e.value.status == -1
+    with cqsa.Plan(n, h, d, cqsa.CQSA_F32, [3]) as p:
+        assert p.backward_workspace_size() == al(h * n * 4) + 3 * al(3 * n * h * d * 4)
+    assert lib.cqsa_backward(None, None, None, None, None, None, None, None, None, None, 0, None, 0, None,
+                             None) == -1

@@ -11,7 +11,7 @@ import pytest
 from scipy.special import softmax
 
 from memory_bounded_streaming_amd.inputs import gen_qkv, gen_tensor
-from oracle.backward import attention_backward_fp64, recompose_backward_fp64
+from oracle.backward import attention_backward_fp64, dq_rows_fp64, recompose_backward_fp64
 from oracle.plan import make_plan
 
 
@@ -121,3 +121,15 @@ def test_decomposition_misses_a_pair_if_a_task_is_dropped():
     plan.tasks = plan.tasks[1:]
     split = recompose_backward_fp64(q, k, v, do, plan, dtype="f32")
     assert max(np.abs(a - b).max() for a, b in zip(split, dense)) > 1e-4
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_dq_rows_equal_dense_rows(dtype):
+    # the row-restricted dQ (blocked keys, two passes) against the dense gradients
+    n, h, d = 70, 2, 8
+    q, k, v = gen_qkv(8, n, h, d, dtype)
+    do = gen_tensor(8, 3, n, h, d, dtype)
+    dq, _, _ = attention_backward_fp64(q, k, v, do, dtype=dtype)
+    rows = np.array([0, 3, 31, 69])
+    np.testing.assert_allclose(dq_rows_fp64(q, k, v, do, rows, dtype=dtype, key_block=16), dq[rows],
+                               rtol=1e-11, atol=1e-13)
