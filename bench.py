@@ -135,6 +135,50 @@ def run_device(args, torch, cqsa):
     return out
 
 
+def run_backward(args, torch, cqsa):
+    """The backward of the device-resident workload: one cqsa_backward call per step
+    (Delta/transposes, dK/dV and dQ kernels, slot sums), timed with HIP events on its
+    stream; O and LSE come from one forward beforehand."""
+    from memory_bounded_streaming_amd.inputs import gen_qkv, gen_tensor
+    n, h, d, levels, _, _ = WORKLOADS["c2"]
+    q, k, v = gen_qkv(args.seed, n, h, d, "bf16")
+    do = gen_tensor(args.seed, 3, n, h, d, "bf16")
+    dev = [torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda() for x in (q, k, v, do)]
+    plan = cqsa.Plan(n, h, d, cqsa.CQSA_BF16, levels)
+    o = torch.empty((n, h, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((h, n), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    plan.forward(dev[0], dev[1], dev[2], o, lse, stream=stream)
+    grads = [torch.empty((n, h, d), dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+    ws = torch.empty(plan.backward_workspace_size(), dtype=torch.uint8, device="cuda")
+    args_ = (dev[0], dev[1], dev[2], o, lse, dev[3], *grads)
+    for _ in range(args.warmup):
+        plan.backward(*args_, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        plan.backward(*args_, workspace=ws, stream=stream)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    st = plan.backward(*args_, workspace=ws, stream=stream, stats=True)
+    useful = 10.0 * n * n * d * h
+    executed = 14.0 * n * n * d * h  # S and dP are formed in both gradient kernels
+    plan.close()
+    return {
+        "workload": f"backward of the N={n}, H={h}, d={d} bf16 l={levels[0]} workload (device-resident)",
+        "ms_per_step": round(ms, 4),
+        "tflops_useful": round(useful / (ms / 1e3) / 1e12, 3),
+        "useful_flop": useful,
+        "grad_kernels_ms": round(st["t_attn_ms"], 4),
+        "grad_kernels_tflops_executed": round(executed / (st["t_attn_ms"] / 1e3) / 1e12, 3),
+        "executed_flop": executed,
+        "elementwise_ms": round(st["t_merge_ms"], 4),
+        "fwd_bwd_ratio_note": "ms_per_step here / the forward step's ms_per_step",
+    }
+
+
 def pcie_achievable(torch, nbytes=512 << 20, reps=5):
     """Plain pinned-memory copies of 512 MiB in each direction: the achievable PCIe rate."""
     h = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
@@ -201,6 +245,7 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-streamed", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one plain device copy of 1 GiB first (reference for HBM traffic counters)")
@@ -225,6 +270,13 @@ def main():
     log("bench: device-resident workload")
     dres = run_device(args, torch, cqsa)
     log(f"bench: {dres['value']:.1f} TFLOP/s end-to-end, partial kernel {dres['attn_tflops']:.1f} TFLOP/s")
+    bwd = None
+    if not args.no_backward:
+        log("bench: backward of the device-resident workload")
+        bwd = run_backward(args, torch, cqsa)
+        bwd["fwd_bwd_ratio"] = round((bwd["ms_per_step"] + dres["ms_per_step"]) / dres["ms_per_step"], 3)
+        bwd.pop("fwd_bwd_ratio_note")
+        log(f"bench: backward {bwd['tflops_useful']:.1f} useful TFLOP/s, {bwd['ms_per_step']:.2f} ms")
     stream_res = None
     if not args.no_streamed:
         log("bench: host-pinned streamed workload")
@@ -271,6 +323,7 @@ def main():
                   "frac": round(dres["merge_gbs"] / HBM_PEAK_GBS, 4), "bytes_per_launch": dres["merge_bytes"],
                   "avg_launch_ms": round(dres["merge_ms"], 4)},
         "streamed": stream_res,
+        "backward": bwd,
         "cpu_baseline": cpu,
         "kernel_source_sha256_16": khash,
     }

@@ -68,7 +68,7 @@ typedef enum {
  * is attention over the N real tokens.  Without this flag an N off the unit grid is EDIVIDE. */
 #define CQSA_FLAG_PAD 0x4u
 
-#define CQSA_MAX_LEVELS 8
+#define CQSA_MAX_LEVELS 12
 #define CQSA_MAX_L 10
 
 typedef struct cqsa_plan cqsa_plan; /* opaque; immutable once created */
@@ -102,6 +102,37 @@ typedef struct {
   int64_t n_attn_launches, n_merge_launches, n_h2d_copies, n_d2h_copies;
   double useful_flop;
 } cqsa_stats;
+
+/* Measured rates a dry run prices a plan with (all > 0). */
+typedef struct {
+  double attn_tflops;           /* partial kernel, useful TFLOP/s */
+  double merge_gbs;             /* merge kernel, HBM GB/s */
+  double h2d_gbs, d2h_gbs;      /* pinned host <-> device copies, GB/s */
+} cqsa_rates;
+
+/* Plan-only summary of a (possibly huge) CQS plan: what cqsa_forward with
+ * CQSA_RES_HOST_PINNED would stage, move and compute, and the time those rates give. */
+typedef struct {
+  int64_t n_tokens, padded_tokens;
+  int32_t heads, head_dim, dtype;
+  int32_t levels;
+  int32_t c[CQSA_MAX_LEVELS], l[CQSA_MAX_LEVELS];
+  int64_t n_tasks;              /* prod(c_k) */
+  int64_t unit_tokens;          /* padded_tokens / prod(c_k) */
+  int64_t visits;               /* prod(l_k) */
+  int64_t task_tokens;          /* unit_tokens * visits */
+  int32_t stream_mode;          /* cqsa_mode that fits the budget, 0 if none */
+  int32_t kv_buffers;
+  int64_t stream_workspace_bytes; /* device bytes of that mode (excluding descriptor tables) */
+  int64_t per_task_descriptor_bytes; /* upper bound of one task's work items + key runs */
+  int64_t host_pinned_bytes;    /* Q, K, V, O, LSE in pinned memory + the host accumulator */
+  int64_t bytes_h2d, bytes_d2h; /* exactly what the stream engine copies (LSE included) */
+  int64_t merge_bytes;          /* HBM bytes of all merge launches */
+  double useful_flop;           /* 4 N^2 d H */
+  double t_attn_s, t_merge_s, t_h2d_s, t_d2h_s;
+  double t_est_s;               /* max(attn + merge (+ unoverlapped K/V loads), h2d, d2h) */
+  int32_t materializable;       /* 1 if cqsa_plan_create builds this plan */
+} cqsa_estimate;
 
 /* Library version string. */
 const char* cqsa_version(void);
@@ -251,6 +282,23 @@ cqsa_status cqsa_backward(const cqsa_plan* plan, const void* q, const void* k, c
                           const void* o, const float* lse, const void* d_o, void* dq, void* dk,
                           void* dv, cqsa_residency res, void* workspace, int64_t workspace_bytes,
                           void* stream, cqsa_stats* stats);
+
+/*
+ * Dry run of the streamed forward for any N ("The Recursive Benefit" and "Precise
+ * Scaling" sections of the wispaper explainer: recursion depth for very long
+ * sequences): the same levels, footprint model and mode choice as cqsa_plan_create
+ * (n_levels = 0: undivided first, then l_levels[0] repeated, up to CQSA_MAX_LEVELS),
+ * but in closed form -- no task is built, so itr up to CQSA_MAX_LEVELS and billions of
+ * tokens cost nothing.  Bytes and FLOP are exact for the stream engine (with LSE
+ * returned); times come from `rates` (measured by the caller), overlapping copies
+ * with compute as the engine does (a single-buffered K/V stage is not overlapped).
+ * The descriptor tables are excluded from stream_workspace_bytes (the materialized
+ * engine holds them for all tasks; per_task_descriptor_bytes bounds one task's share).
+ * Host-only.  Errors: EINVAL, ENOSET, EDIVIDE, EBUDGET (no mode fits at any depth).
+ */
+cqsa_status cqsa_plan_estimate(int64_t n, int32_t heads, int32_t head_dim, cqsa_dtype dtype,
+                               const int32_t* l_levels, int32_t n_levels, int64_t budget_bytes,
+                               uint32_t flags, const cqsa_rates* rates, cqsa_estimate* out);
 
 /* Static text for a status code. */
 const char* cqsa_status_string(cqsa_status status);

@@ -21,14 +21,14 @@ __all__ = [
     "CQSA_FLAG_HOST_ACC", "CQSA_FLAG_KV_SINGLE", "CQSA_FLAG_PAD", "MODE_NAMES",
     "cqsa_version", "cqsa_difference_set", "cqsa_plan_create", "cqsa_plan_info_get", "cqsa_plan_schedule",
     "cqsa_plan_coverage", "cqsa_plan_destroy", "cqsa_workspace_size", "cqsa_partials", "cqsa_merge",
-    "cqsa_forward", "cqsa_backward_workspace_size", "cqsa_backward", "cqsa_status_string", "cqsa_last_error", "Plan",
+    "cqsa_forward", "cqsa_backward_workspace_size", "cqsa_backward", "cqsa_plan_estimate", "cqsa_status_string", "cqsa_last_error", "Plan",
 ]
 
 CQSA_BF16, CQSA_F32 = 0, 1
 CQSA_RES_DEVICE, CQSA_RES_HOST_PINNED = 0, 1
 CQSA_FLAG_HOST_ACC, CQSA_FLAG_KV_SINGLE, CQSA_FLAG_PAD = 0x1, 0x2, 0x4
 MODE_NAMES = {1: "device_acc_kv2", 2: "host_acc_kv2", 3: "device_acc_kv1", 4: "host_acc_kv1"}
-MAX_LEVELS = 8
+MAX_LEVELS = 12
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcqsa.so")
 _lib = None
@@ -65,6 +65,26 @@ class Stats(ctypes.Structure):
     ]
 
 
+class Rates(ctypes.Structure):
+    _fields_ = [("attn_tflops", ctypes.c_double), ("merge_gbs", ctypes.c_double), ("h2d_gbs", ctypes.c_double),
+                ("d2h_gbs", ctypes.c_double)]
+
+
+class Estimate(ctypes.Structure):
+    _fields_ = [
+        ("n_tokens", ctypes.c_int64), ("padded_tokens", ctypes.c_int64),
+        ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32), ("levels", ctypes.c_int32),
+        ("c", ctypes.c_int32 * MAX_LEVELS), ("l", ctypes.c_int32 * MAX_LEVELS),
+        ("n_tasks", ctypes.c_int64), ("unit_tokens", ctypes.c_int64), ("visits", ctypes.c_int64),
+        ("task_tokens", ctypes.c_int64), ("stream_mode", ctypes.c_int32), ("kv_buffers", ctypes.c_int32),
+        ("stream_workspace_bytes", ctypes.c_int64), ("per_task_descriptor_bytes", ctypes.c_int64),
+        ("host_pinned_bytes", ctypes.c_int64), ("bytes_h2d", ctypes.c_int64), ("bytes_d2h", ctypes.c_int64),
+        ("merge_bytes", ctypes.c_int64), ("useful_flop", ctypes.c_double),
+        ("t_attn_s", ctypes.c_double), ("t_merge_s", ctypes.c_double), ("t_h2d_s", ctypes.c_double),
+        ("t_d2h_s", ctypes.c_double), ("t_est_s", ctypes.c_double), ("materializable", ctypes.c_int32),
+    ]
+
+
 EXPORTS = {
     "cqsa_version": (ctypes.c_char_p, []),
     "cqsa_difference_set": (ctypes.c_int, [ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.c_int32]),
@@ -85,6 +105,9 @@ EXPORTS = {
     "cqsa_backward_workspace_size": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_int64)]),
     "cqsa_backward": (ctypes.c_int, [ctypes.c_void_p] + [ctypes.c_void_p] * 9 +
                       [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.POINTER(Stats)]),
+    "cqsa_plan_estimate": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int,
+                                          ctypes.POINTER(ctypes.c_int32), ctypes.c_int32, ctypes.c_int64,
+                                          ctypes.c_uint32, ctypes.POINTER(Rates), ctypes.POINTER(Estimate)]),
     "cqsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "cqsa_last_error": (ctypes.c_char_p, []),
 }
@@ -243,6 +266,23 @@ def cqsa_backward(plan: int, q, k, v, o, lse, d_o, dq, dk, dv, residency: int = 
     if st is None:
         return None
     return {name: getattr(st, name) for name, _ in Stats._fields_}
+
+
+def cqsa_plan_estimate(n: int, heads: int, head_dim: int, dtype: int, l_levels, n_levels: int | None = None,
+                       budget_bytes: int = 0, flags: int = 0, rates=None) -> dict:
+    """Closed-form dry run; rates: dict with attn_tflops, merge_gbs, h2d_gbs, d2h_gbs."""
+    levels = list(l_levels)
+    if n_levels is None:
+        n_levels = len(levels)
+    arr = (ctypes.c_int32 * max(1, len(levels)))(*levels)
+    r = Rates(**(rates or {}))
+    out = Estimate()
+    _check(load().cqsa_plan_estimate(n, heads, head_dim, dtype, arr, n_levels, budget_bytes, flags,
+                                     ctypes.byref(r), ctypes.byref(out)))
+    d = {name: getattr(out, name) for name, _ in Estimate._fields_}
+    d["c"] = list(out.c[:out.levels])
+    d["l"] = list(out.l[:out.levels])
+    return d
 
 
 class Plan:

@@ -244,4 +244,16 @@ cqsa_status cqsa_backward(const cqsa_plan* plan, const void* q, const void* k, c
   });
 }
 
+cqsa_status cqsa_plan_estimate(int64_t n, int32_t heads, int32_t head_dim, cqsa_dtype dtype,
+                               const int32_t* l_levels, int32_t n_levels, int64_t budget_bytes, uint32_t flags,
+                               const cqsa_rates* rates, cqsa_estimate* out) {
+  return guarded([&]() -> cqsa_status {
+    if (rates == nullptr || out == nullptr) return fail(CQSA_EINVAL, "NULL argument");
+    std::string why;
+    const cqsa_status s = cqsa::estimate_plan(n, heads, head_dim, dtype, l_levels, n_levels, budget_bytes, flags,
+                                              *rates, *out, why);
+    return s == CQSA_OK ? ok() : fail(s, why);
+  });
+}
+
 }  // extern "C"

@@ -13,6 +13,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstring>
 #include <numeric>
 
 namespace cqsa {
@@ -288,8 +289,9 @@ cqsa_status choose_mode(Plan& p, std::string& why) {
   return CQSA_EBUDGET;
 }
 
-cqsa_status build_fixed(int64_t n, int heads, int d, cqsa_dtype dtype, const std::vector<int>& ls,
-                        int64_t budget, uint32_t flags, Plan& p, std::string& why) {
+// Levels, difference sets, unit grid and visit count of a plan; no task is built.
+cqsa_status plan_shape(int64_t n, int heads, int d, cqsa_dtype dtype, const std::vector<int>& ls, int64_t budget,
+                       uint32_t flags, Plan& p, std::string& why) {
   p.n = n;
   p.heads = heads;
   p.d = d;
@@ -323,11 +325,33 @@ cqsa_status build_fixed(int64_t n, int heads, int d, cqsa_dtype dtype, const std
   p.unit = (n + prod_c - 1) / prod_c;
   p.n_pad = p.unit * prod_c;
   p.visits = prod_l;
-  if (p.unit * prod_l > INT32_MAX) {
+  p.task_units = prod_l;
+  if (p.unit * prod_l > INT32_MAX) {  // no staging of such a task exists: divide further
     why = "a task holds more than 2^31-1 tokens";
-    return CQSA_EINVAL;
+    return CQSA_EBUDGET;
   }
-  cqsa_status st = build_tasks(p, why);
+  return CQSA_OK;
+}
+
+// Largest plan cqsa_plan_create materializes: work items (task, unit) and mask cells.
+constexpr int64_t kMaxItems = int64_t(1) << 24;
+constexpr int64_t kMaxMaskCells = int64_t(1) << 32;
+
+bool materializable(const Plan& p) {
+  const int64_t tu = p.task_units;
+  return p.n_units <= kMaxItems / tu && p.n_units * tu <= kMaxMaskCells / tu;
+}
+
+cqsa_status build_fixed(int64_t n, int heads, int d, cqsa_dtype dtype, const std::vector<int>& ls,
+                        int64_t budget, uint32_t flags, Plan& p, std::string& why) {
+  cqsa_status st = plan_shape(n, heads, d, dtype, ls, budget, flags, p, why);
+  if (st != CQSA_OK) return st;
+  if (!materializable(p)) {
+    why = "a plan of " + std::to_string(p.n_units) + " tasks x " + std::to_string(p.task_units) +
+          " units is too large to build (cqsa_plan_estimate summarizes it)";
+    return CQSA_ENOMEM;
+  }
+  st = build_tasks(p, why);
   if (st != CQSA_OK) return st;
   build_schedule(p);
   build_descriptors(p);
@@ -396,6 +420,124 @@ cqsa_status build_plan(int64_t n, int heads, int d, cqsa_dtype dtype, const int3
   }
   why = last_why;
   return last;
+}
+
+// ----------------------------------------------------------------------------------
+// dry run: the plan's shape, footprint and traffic in closed form
+// ----------------------------------------------------------------------------------
+namespace {
+
+// First staging mode (in cqsa_mode order, respecting the flags) whose workspace fits.
+bool fit_mode(const Plan& p, Footprint& fp) {
+  struct Cand {
+    bool dev;
+    int kv;
+  };
+  const Cand order[4] = {{true, 2}, {false, 2}, {true, 1}, {false, 1}};
+  for (const Cand& c : order) {
+    if ((p.flags & CQSA_FLAG_HOST_ACC) && c.dev) continue;
+    if ((p.flags & CQSA_FLAG_KV_SINGLE) && c.kv != 1) continue;
+    const int64_t bytes = stream_layout(p, c.dev, c.kv).total;
+    if (p.budget == 0 || bytes <= p.budget) {
+      fp = {c.dev, c.kv, bytes};
+      return true;
+    }
+  }
+  return false;
+}
+
+}  // namespace
+
+cqsa_status estimate_plan(int64_t n, int heads, int d, cqsa_dtype dtype, const int32_t* ls, int n_levels,
+                          int64_t budget, uint32_t flags, const cqsa_rates& r, cqsa_estimate& out,
+                          std::string& why) {
+  if (n < 1 || heads < 1 || (d != 64 && d != 128) || ls == nullptr || n_levels < 0 ||
+      n_levels > CQSA_MAX_LEVELS || budget < 0 || (dtype != CQSA_BF16 && dtype != CQSA_F32) ||
+      (flags & ~(CQSA_FLAG_HOST_ACC | CQSA_FLAG_KV_SINGLE | CQSA_FLAG_PAD)) != 0 || !(r.attn_tflops > 0) ||
+      !(r.merge_gbs > 0) || !(r.h2d_gbs > 0) || !(r.d2h_gbs > 0)) {
+    why = "invalid argument (see cqsa_plan_create; every rate must be positive)";
+    return CQSA_EINVAL;
+  }
+  Plan p;
+  Footprint fp{};
+  cqsa_status st = CQSA_EBUDGET;
+  if (n_levels > 0) {
+    std::vector<int> levels(ls, ls + n_levels);
+    for (int l : levels)
+      if (l < 1 || l > CQSA_MAX_L) {
+        why = "each l must be in 1..10";
+        return CQSA_EINVAL;
+      }
+    st = plan_shape(n, heads, d, dtype, levels, budget, flags, p, why);
+    if (st != CQSA_OK) return st;
+    if (!fit_mode(p, fp)) {
+      why = "no staging mode fits the budget";
+      return CQSA_EBUDGET;
+    }
+  } else {
+    const int l = ls[0];
+    if (l < 2 || l > CQSA_MAX_L) {
+      why = "auto levels need l in 2..10";
+      return CQSA_EINVAL;
+    }
+    std::vector<int> levels{1};
+    for (int k = 0; k <= CQSA_MAX_LEVELS; ++k) {
+      if (k == 1) levels.clear();
+      if (k >= 1) levels.push_back(l);
+      std::string w;
+      st = plan_shape(n, heads, d, dtype, levels, budget, flags, p, w);
+      if (st == CQSA_OK && fit_mode(p, fp)) break;
+      if (st == CQSA_OK) st = CQSA_EBUDGET;
+      why = w.empty() ? "no level count fits the budget" : w;
+      if (st != CQSA_EBUDGET) {
+        if (k <= 1) return st;
+        why = "no level count fits the budget before N stops dividing (" + w + ")";
+        return CQSA_EBUDGET;
+      }
+    }
+    if (st != CQSA_OK) return st;
+  }
+  std::memset(&out, 0, sizeof(out));
+  out.n_tokens = p.n;
+  out.padded_tokens = p.n_pad;
+  out.heads = heads;
+  out.head_dim = d;
+  out.dtype = dtype;
+  out.levels = static_cast<int32_t>(p.ls.size());
+  for (size_t k = 0; k < p.ls.size(); ++k) {
+    out.c[k] = p.cs[k];
+    out.l[k] = p.ls[k];
+  }
+  out.n_tasks = p.n_units;
+  out.unit_tokens = p.unit;
+  out.visits = p.visits;
+  out.task_tokens = p.task_tokens();
+  out.stream_mode = fp.acc_on_device ? (fp.kv_buffers == 2 ? CQSA_MODE_DEVICE_ACC_KV2 : CQSA_MODE_DEVICE_ACC_KV1)
+                                     : (fp.kv_buffers == 2 ? CQSA_MODE_HOST_ACC_KV2 : CQSA_MODE_HOST_ACC_KV1);
+  out.kv_buffers = fp.kv_buffers;
+  out.stream_workspace_bytes = fp.bytes;
+  out.per_task_descriptor_bytes = p.task_units * int64_t(sizeof(WorkItem)) +
+                                  p.task_units * p.task_units * int64_t(sizeof(KeyRun));
+  const double N = double(p.n), V = double(p.visits), H = heads, D = d, e = double(p.elem_bytes());
+  const int64_t row_in = p.row_in_bytes(), rowp = p.row_part_bytes();
+  const bool host_acc = !fp.acc_on_device;
+  out.host_pinned_bytes = 4 * p.n * row_in + p.n * heads * 4 + (host_acc ? p.n * rowp : 0);
+  out.bytes_h2d = 3 * p.visits * p.n * row_in + (host_acc ? (p.visits - 1) * p.n * rowp : 0);
+  out.bytes_d2h = p.n * heads * int64_t(d) * p.elem_bytes() + p.n * heads * 4 +
+                  (host_acc ? (p.visits - 1) * p.n * rowp : 0);
+  // merge launches: a non-first visit reads accumulator + partial and writes the
+  // accumulator (or, at the last visit, O and LSE); a single visit reads its partial
+  const int64_t part = heads * int64_t(d + 2) * 4, fin = heads * (int64_t(d) * p.elem_bytes() + 4);
+  out.merge_bytes = p.visits == 1 ? p.n * (part + fin) : p.n * ((p.visits - 2) * 3 * part + 2 * part + fin);
+  out.useful_flop = 4.0 * N * N * D * H;
+  out.t_attn_s = out.useful_flop / (r.attn_tflops * 1e12);
+  out.t_merge_s = double(out.merge_bytes) / (r.merge_gbs * 1e9);
+  out.t_h2d_s = double(out.bytes_h2d) / (r.h2d_gbs * 1e9);
+  out.t_d2h_s = double(out.bytes_d2h) / (r.d2h_gbs * 1e9);
+  const double kv_serial = fp.kv_buffers == 1 ? 2.0 * V * N * H * D * e / (r.h2d_gbs * 1e9) : 0.0;
+  out.t_est_s = std::max({out.t_attn_s + out.t_merge_s + kv_serial, out.t_h2d_s, out.t_d2h_s});
+  out.materializable = materializable(p) ? 1 : 0;
+  return CQSA_OK;
 }
 
 }  // namespace cqsa

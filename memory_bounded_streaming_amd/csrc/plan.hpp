@@ -111,4 +111,9 @@ inline int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; 
 cqsa_status build_plan(int64_t n, int heads, int d, cqsa_dtype dtype, const int32_t* ls,
                        int n_levels, int64_t budget, uint32_t flags, Plan& out, std::string& why);
 
+// Closed-form dry run of the streamed forward (cqsa_plan_estimate).
+cqsa_status estimate_plan(int64_t n, int heads, int d, cqsa_dtype dtype, const int32_t* ls, int n_levels,
+                          int64_t budget, uint32_t flags, const cqsa_rates& r, cqsa_estimate& out,
+                          std::string& why);
+
 }  // namespace cqsa

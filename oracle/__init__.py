@@ -28,6 +28,7 @@ Modules
                ownership mask, coverage table, canonical serialisation.
 ``recompose``  per-task float64 partials and their merge (the method's steps).
 ``backward``   gradients of attention (the definition) and their per-task sums.
+``stream_bytes`` the bytes the streamed forward moves, counted task by task.
 ``tolerance``  the error metrics the parity tests apply.
 
 Every function states which of the above it follows.  Readings taken where the

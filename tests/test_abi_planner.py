@@ -31,7 +31,7 @@ def _header_symbols():
 
 def test_library_exports_every_declared_symbol(lib):
     names = _header_symbols()
-    assert len(names) == 15
+    assert len(names) == 16
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(cqsa.EXPORTS)
@@ -152,7 +152,7 @@ def test_budget_selects_modes_in_order():
     ((0, 1, 64, cqsa.CQSA_BF16, [3]), -1),          # no tokens
     ((49, 1, 64, 7, [3]), -1),                      # unknown dtype
     ((49, 1, 64, cqsa.CQSA_BF16, [11]), -1),        # l out of range
-    ((7 ** 4, 1, 64, cqsa.CQSA_BF16, [3] * 9), -1),  # more than 8 levels
+    ((7 ** 4, 1, 64, cqsa.CQSA_BF16, [3] * 13), -1),  # more than 12 levels
 ])
 def test_plan_errors(args, status):
     with pytest.raises(cqsa.CqsaError) as e:
@@ -239,3 +239,54 @@ def test_backward_workspace_size_and_argument_errors(lib):
         assert p.backward_workspace_size() == al(h * n * 4) + 3 * al(3 * n * h * d * 4)
     assert lib.cqsa_backward(None, None, None, None, None, None, None, None, None, None, 0, None, 0, None,
                              None) == -1
+
+
+RATES = {"attn_tflops": 800.0, "merge_gbs": 5000.0, "h2d_gbs": 50.0, "d2h_gbs": 40.0}
+
+
+@pytest.mark.parametrize("n,h,d,dt,levels,budget,flags", [
+    (3584, 1, 64, cqsa.CQSA_F32, [3], 0, 0),
+    (212992, 16, 128, cqsa.CQSA_BF16, [4], 16 * GiB, 0),
+    (1376256, 8, 128, cqsa.CQSA_BF16, [5], 8 * GiB, 0),
+    (12845056, 1, 128, cqsa.CQSA_BF16, [3, 3], 2 * GiB, 0),
+    (7 * 192 + 5, 2, 128, cqsa.CQSA_BF16, [3], 0, cqsa.CQSA_FLAG_PAD | cqsa.CQSA_FLAG_HOST_ACC),
+    (21 * 20 + 3, 1, 64, cqsa.CQSA_BF16, [3, 2], 0, cqsa.CQSA_FLAG_PAD | cqsa.CQSA_FLAG_KV_SINGLE),
+    (500, 2, 64, cqsa.CQSA_BF16, [1], 0, cqsa.CQSA_FLAG_HOST_ACC),
+])
+def test_estimate_matches_built_plan_and_walked_traffic(n, h, d, dt, levels, budget, flags):
+    from oracle.stream_bytes import stream_traffic
+    est = cqsa.cqsa_plan_estimate(n, h, d, dt, levels, budget_bytes=budget, flags=flags, rates=RATES)
+    with cqsa.Plan(n, h, d, dt, levels, budget_bytes=budget, flags=flags) as p:
+        info = p.info
+    for key in ("levels", "c", "l", "n_tasks", "unit_tokens", "visits", "task_tokens", "stream_mode", "kv_buffers",
+                "stream_workspace_bytes", "padded_tokens"):
+        assert est[key] == info[key], key
+    assert est["materializable"] == 1
+    e = 2 if dt == cqsa.CQSA_BF16 else 4
+    ref = stream_traffic(make_plan(n, levels, pad=bool(flags & cqsa.CQSA_FLAG_PAD)), h, d, e,
+                         host_acc=est["stream_mode"] in (2, 4))
+    for key in ("bytes_h2d", "bytes_d2h", "merge_bytes"):
+        assert est[key] == ref[key], key
+    assert est["useful_flop"] == pytest.approx(4.0 * n * n * d * h)
+    assert est["t_attn_s"] == pytest.approx(est["useful_flop"] / 800e12)
+    assert est["t_est_s"] >= max(est["t_h2d_s"], est["t_d2h_s"], est["t_attn_s"])
+
+
+def test_estimate_of_a_billion_tokens_needs_no_plan():
+    # 2^30 tokens, one head, d=128, bf16, l=3: nine levels would be 7^9 tasks; padding
+    # makes every depth divide, and the budget decides the depth
+    n = 1 << 30
+    est = cqsa.cqsa_plan_estimate(n, 1, 128, cqsa.CQSA_BF16, [3], n_levels=0, budget_bytes=16 * GiB,
+                                  flags=cqsa.CQSA_FLAG_PAD, rates=RATES)
+    assert est["stream_workspace_bytes"] <= 16 * GiB and est["levels"] >= 2 and set(est["l"]) == {3}
+    assert est["padded_tokens"] % est["n_tasks"] == 0 and est["padded_tokens"] - n < est["n_tasks"]
+    assert est["bytes_h2d"] >= 3 * est["visits"] * n * 256
+    nine = cqsa.cqsa_plan_estimate(n, 1, 128, cqsa.CQSA_BF16, [3] * 9, flags=cqsa.CQSA_FLAG_PAD, rates=RATES)
+    assert nine["n_tasks"] == 7 ** 9 and nine["visits"] == 3 ** 9 and nine["materializable"] == 0
+    assert nine["task_tokens"] == -(-n // 7 ** 9) * 3 ** 9
+    with pytest.raises(cqsa.CqsaError) as e:  # the engine does not build such a plan
+        cqsa.Plan(n, 1, 128, cqsa.CQSA_BF16, [3] * 9, flags=cqsa.CQSA_FLAG_PAD)
+    assert e.value.status == -6
+    with pytest.raises(cqsa.CqsaError) as e:
+        cqsa.cqsa_plan_estimate(n, 1, 128, cqsa.CQSA_BF16, [3], rates={**RATES, "h2d_gbs": 0.0})
+    assert e.value.status == -1
