@@ -12,7 +12,9 @@ method's algorithm:
     O[i,h] = sum_j exp(s_ij - M_i) V[j,h,:] / sum_j exp(s_ij - M_i)
     LSE    = M_i + ln sum_j exp(s_ij - M_i)
 
-Non-causal, batch 1, every one of the N keys.  Computed in two passes over key
+Batch 1.  Non-causal (every one of the N keys) by default; with causal=True row i
+attends the keys j <= i only (the causal variant, reading R16 of ``oracle.plan``).
+Computed in two passes over key
 blocks (pass 1: the row maximum; pass 2: the exponential sums), i.e. the
 textbook stable softmax with no running rescale.  Inputs are taken at their
 exact values: float32 arrays, or bfloat16 given as uint16 bit patterns, are
@@ -45,7 +47,7 @@ def default_scale(d: int) -> float:
 
 
 def attention_fp64(q, k, v, rows=None, dtype="f32", scale=None,
-                   key_block=16384, row_block=1024):
+                   key_block=16384, row_block=1024, causal=False):
     """Exact attention outputs for the selected query rows.
 
     Parameters
@@ -54,6 +56,7 @@ def attention_fp64(q, k, v, rows=None, dtype="f32", scale=None,
     rows    : 1-D int array of query rows to evaluate (default: all N).
     dtype   : "f32" or "bf16", how q/k/v are stored.
     scale   : softmax scale (default 1/sqrt(d)).
+    causal  : mask keys j > i (row i sees tokens 0..i).
 
     Returns
     -------
@@ -80,19 +83,26 @@ def attention_fp64(q, k, v, rows=None, dtype="f32", scale=None,
         for r0 in range(0, r_count, row_block):
             sel = rows[r0:r0 + row_block]
             qh = to_f64(q[sel, h, :], dtype)                       # [r, d]
-            # pass 1: M_i = max_j s_ij over all keys
-            row_max = np.full(sel.shape[0], -np.inf)
-            for k0 in range(0, n, key_block):
+            kend = int(sel.max()) + 1 if causal else n
+
+            def scores(k0):
                 kh = to_f64(k[k0:k0 + key_block, h, :], dtype)     # [b, d]
                 s = (qh @ kh.T) * scale                            # [r, b]
-                np.maximum(row_max, s.max(axis=1), out=row_max)
+                if causal:
+                    keys = np.arange(k0, k0 + kh.shape[0])
+                    s = np.where(keys[None, :] > sel[:, None], -np.inf, s)
+                return s
+
+            # pass 1: M_i = max_j s_ij over all (admitted) keys
+            row_max = np.full(sel.shape[0], -np.inf)
+            for k0 in range(0, kend, key_block):
+                np.maximum(row_max, scores(k0).max(axis=1), out=row_max)
             # pass 2: sums of exp(s - M_i) and of exp(s - M_i) * v_j
             denom = np.zeros(sel.shape[0])
             numer = np.zeros((sel.shape[0], d))
-            for k0 in range(0, n, key_block):
-                kh = to_f64(k[k0:k0 + key_block, h, :], dtype)
+            for k0 in range(0, kend, key_block):
                 vh = to_f64(v[k0:k0 + key_block, h, :], dtype)
-                p = np.exp((qh @ kh.T) * scale - row_max[:, None])
+                p = np.exp(scores(k0) - row_max[:, None])
                 denom += p.sum(axis=1)
                 numer += p @ vh
             out[r0:r0 + sel.shape[0], h, :] = numer / denom[:, None]

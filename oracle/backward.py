@@ -19,6 +19,8 @@ for an upstream gradient dO, per head:
 
 (the chain rule through the softmax: d softmax = P (dP - <P, dP>)).
 
+Causal variant (reading R16 of ``oracle.plan``): the same with P_ij = 0 for j > i.
+
 CQS decomposition (reading R15): every (query, key) pair is admitted by exactly
 one task (readings R4/R5 of ``oracle.plan``), and with the final LSE each pair's
 terms above no longer depend on any other pair, so each gradient is the sum over
@@ -35,9 +37,11 @@ from .plan import Plan
 __all__ = ["attention_backward_fp64", "task_backward_fp64", "recompose_backward_fp64", "dq_rows_fp64"]
 
 
-def _dense_head(q, k, v, do, scale):
+def _dense_head(q, k, v, do, scale, causal=False):
     """All of the definition for one head: (dq, dk, dv, lse) in float64, N x N at once."""
     s = (q @ k.T) * scale
+    if causal:
+        s = np.where(np.triu(np.ones(s.shape, dtype=bool), 1), -np.inf, s)
     m = s.max(axis=1, keepdims=True)
     e = np.exp(s - m)
     lse = m[:, 0] + np.log(e.sum(axis=1))
@@ -49,7 +53,7 @@ def _dense_head(q, k, v, do, scale):
     return scale * (ds @ k), scale * (ds.T @ q), dv, lse
 
 
-def attention_backward_fp64(q, k, v, do, dtype="f32", scale=None):
+def attention_backward_fp64(q, k, v, do, dtype="f32", scale=None, causal=False):
     """(dQ, dK, dV) [N, H, d] float64 of exact attention for upstream gradient dO.
 
     q, k, v, do: [N, H, d] float32 arrays or bf16 bit patterns (uint16), widened
@@ -62,7 +66,7 @@ def attention_backward_fp64(q, k, v, do, dtype="f32", scale=None):
     out = [np.zeros((n, h_count, d)) for _ in range(3)]
     for h in range(h_count):
         qh, kh, vh, doh = (to_f64(x[:, h, :], dtype) for x in (q, k, v, do))
-        dq, dk, dv, _ = _dense_head(qh, kh, vh, doh, scale)
+        dq, dk, dv, _ = _dense_head(qh, kh, vh, doh, scale, causal)
         out[0][:, h], out[1][:, h], out[2][:, h] = dq, dk, dv
     return tuple(out)
 
@@ -92,7 +96,7 @@ def task_backward_fp64(q, k, v, do, lse, delta, plan: Plan, task, dtype="f32", s
         if qi.size == 0:
             continue
         for b, pb in enumerate(task.units):
-            if not task.admitted(a, b):
+            if not task.admitted(a, b) or (plan.causal and b > a):
                 continue
             kj = _unit_rows(plan, pb)
             if kj.size == 0:
@@ -101,6 +105,8 @@ def task_backward_fp64(q, k, v, do, lse, delta, plan: Plan, task, dtype="f32", s
                 qh, doh = to_f64(q[qi, h], dtype), to_f64(do[qi, h], dtype)
                 kh, vh = to_f64(k[kj, h], dtype), to_f64(v[kj, h], dtype)
                 p_ = np.exp((qh @ kh.T) * scale - lse[h, qi][:, None])
+                if plan.causal:
+                    p_ = np.where(kj[None, :] > qi[:, None], 0.0, p_)
                 dp = doh @ vh.T
                 ds = p_ * (dp - delta[h, qi][:, None])
                 dq_t[pa][:, h] += scale * (ds @ kh)
@@ -109,7 +115,7 @@ def task_backward_fp64(q, k, v, do, lse, delta, plan: Plan, task, dtype="f32", s
     return dq_t, dk_t, dv_t
 
 
-def recompose_backward_fp64(q, k, v, do, plan: Plan, dtype="f32", scale=None):
+def recompose_backward_fp64(q, k, v, do, plan: Plan, dtype="f32", scale=None):  # noqa: C901
     """Sum every task's gradient terms in ascending task id: (dQ, dK, dV) [N, H, d].
 
     The final LSE and Delta come from the dense definition (they are inputs of a
@@ -123,6 +129,8 @@ def recompose_backward_fp64(q, k, v, do, plan: Plan, dtype="f32", scale=None):
     for h in range(h_count):
         qh, kh, vh, doh = (to_f64(x[:, h, :], dtype) for x in (q, k, v, do))
         s = (qh @ kh.T) * scale
+        if plan.causal:
+            s = np.where(np.triu(np.ones(s.shape, dtype=bool), 1), -np.inf, s)
         m = s.max(axis=1, keepdims=True)
         lse[h] = m[:, 0] + np.log(np.exp(s - m).sum(axis=1))
         o = np.exp(s - lse[h][:, None]) @ vh

@@ -34,6 +34,10 @@ R5  Recursion: R2-R4 are applied to each task's token list with the next
     level's l; admission is the AND of all levels' masks; the task id is
     mixed-radix, outer level most significant; tasks run in ascending id.
 R6  Unit = N / prod(c_k) tokens; every ownership boundary is unit aligned.
+R16 Causal variant (optional): row i attends keys j <= i.  The division and the
+    owners are unchanged; inside a task (whose token list is in ascending global
+    order, R3) an admitted unit pair (a, b) is kept only if b <= a: b < a is fully
+    visible, b == a is the diagonal block, masked element by element (j <= i).
 R12 Padding (optional): an N >= prod(c_k) that is not a multiple of prod(c_k) is
     divided as N_pad = ceil(N / prod(c_k)) * prod(c_k) tokens; positions >= N are padding.
     They belong to no segment, no key run and no query block, so every real
@@ -124,11 +128,12 @@ class Task:
                 return False
         return True
 
-    def key_runs(self, a: int) -> list:
-        """Admitted key units of local query unit a as (local start, count) runs."""
+    def key_runs(self, a: int, causal: bool = False) -> list:
+        """Admitted key units of local query unit a as (local start, count) runs
+        (with causal, only units b <= a: reading R16)."""
         runs = []
         for b in range(len(self.units)):
-            if not self.admitted(a, b):
+            if not self.admitted(a, b) or (causal and b > a):
                 continue
             if runs and runs[-1][0] + runs[-1][1] == b:
                 runs[-1][1] += 1
@@ -163,6 +168,7 @@ class Plan:
     n_units: int
     tasks: list
     n_pad: int = 0   # tokens the division covers (n_pad >= n; == n unless padded)
+    causal: bool = False
 
     def coverage(self) -> np.ndarray:
         """[U, U] int32: entry [p][q] is the id of the task owning (query unit p, key unit q).
@@ -175,7 +181,7 @@ class Plan:
         for task in self.tasks:
             for a, p in enumerate(task.units):
                 for b, q in enumerate(task.units):
-                    if task.admitted(a, b):
+                    if task.admitted(a, b) and not (self.causal and q > p):
                         cov[p, q] = task.tid if cov[p, q] == -1 else -2
         return cov
 
@@ -201,15 +207,16 @@ class Plan:
                 out += list(s)
             out.append(len(task.units))
             for a, g in enumerate(task.units):
-                runs = task.key_runs(a)
+                runs = task.key_runs(a, self.causal)
                 out += [g, len(runs)]
                 for r in runs:
                     out += list(r)
         return np.asarray(out, dtype=np.int64)
 
 
-def make_plan(n: int, ls: list, pad: bool = False) -> Plan:
-    """Build the plan for N tokens and per-level l values (readings R1-R6; R12 if pad)."""
+def make_plan(n: int, ls: list, pad: bool = False, causal: bool = False) -> Plan:
+    """Build the plan for N tokens and per-level l values (readings R1-R6; R12 if pad,
+    R16 if causal)."""
     if n <= 0 or not ls:
         raise ValueError("need n > 0 and at least one level")
     sets = [difference_set(l) for l in ls]
@@ -245,4 +252,4 @@ def make_plan(n: int, ls: list, pad: bool = False) -> Plan:
         tasks.append(Task(tid=tid, ids=ids, units=units, chunk=chunks))
     tasks.sort(key=lambda t: t.tid)
     return Plan(n=n, ls=list(ls), cs=cs, sets=sets, unit_tokens=unit,
-                n_units=prod_c, tasks=tasks, n_pad=n_pad)
+                n_units=prod_c, tasks=tasks, n_pad=n_pad, causal=causal)

@@ -12,7 +12,8 @@ calculation for softmax" (cited by title on the same page).
 
 Statistics of one task for one query row (natural-log units):
     m = max_j s_ij,  l = sum_j exp(s_ij - m),  n = sum_j exp(s_ij - m) v_j
-over the keys the task admits (readings R4/R5 of ``oracle.plan``).  A row with
+over the keys the task admits (readings R4/R5 of ``oracle.plan``; R16 for causal
+plans, where a row also drops the keys after it).  A row with
 no admitted key has m = -inf, l = 0, n = 0 and is the identity of the merge.
 
 Merge of two triples (a, b):  m = max(m_a, m_b),
@@ -34,7 +35,7 @@ def _key_tokens(plan: Plan, task, a: int) -> np.ndarray:
     (padding positions >= N excluded, reading R12 of oracle.plan)."""
     u = plan.unit_tokens
     parts = []
-    for b0, cnt in task.key_runs(a):
+    for b0, cnt in task.key_runs(a, plan.causal):
         for b in range(b0, b0 + cnt):
             g = task.units[b]
             parts.append(np.arange(g * u, min((g + 1) * u, plan.n), dtype=np.int64))
@@ -71,8 +72,10 @@ def task_partials_fp64(q, k, v, plan: Plan, task, dtype="f32", scale=None,
                 kh = to_f64(k[keys, h, :], dtype)
                 vh = to_f64(v[keys, h, :], dtype)
                 s = (qh @ kh.T) * scale
+                if plan.causal:  # the diagonal block: key j is seen by row i only if j <= i
+                    s = np.where(keys[None, :] > rows[:, None], -np.inf, s)
                 mh = s.max(axis=1)
-                pexp = np.exp(s - mh[:, None])
+                pexp = np.exp(s - np.where(np.isfinite(mh), mh, 0.0)[:, None])
                 m[:, h] = mh
                 lsum[:, h] = pexp.sum(axis=1)
                 num[:, h, :] = pexp @ vh

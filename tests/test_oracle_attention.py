@@ -139,3 +139,22 @@ def test_input_generator_rounding_and_determinism():
     for x1, x2 in zip(a, b):
         np.testing.assert_array_equal(x1, x2)
     assert not np.array_equal(a[0], a[1])
+
+
+def test_causal_matches_masked_scipy_softmax_and_prefix_attention():
+    rng = np.random.default_rng(12)
+    n, h_count, d = 40, 2, 8
+    q, k, v = (rng.standard_normal((n, h_count, d)).astype(np.float32) for _ in range(3))
+    o, lse = attention_fp64(q, k, v, dtype="f32", causal=True, key_block=7, row_block=3)
+    for h in range(h_count):
+        s = q[:, h].astype(np.float64) @ k[:, h].astype(np.float64).T / math.sqrt(d)
+        s[np.triu_indices(n, 1)] = -np.inf
+        np.testing.assert_allclose(o[:, h], softmax(s, axis=1) @ v[:, h].astype(np.float64), rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(lse[h], logsumexp(s, axis=1), rtol=1e-13)
+    # row i of causal attention is ordinary attention of query i over the prefix 0..i
+    for i in (0, 1, 17, n - 1):
+        oi, li = attention_fp64(q[:i + 1], k[:i + 1], v[:i + 1], rows=[i], dtype="f32")
+        np.testing.assert_allclose(o[i], oi[0], rtol=1e-12, atol=1e-14)
+    np.testing.assert_array_equal(o[0], v[0].astype(np.float64))  # the first row sees only itself
+    full, _ = attention_fp64(q, k, v, rows=[n - 1], dtype="f32")
+    np.testing.assert_allclose(o[n - 1], full[0], rtol=1e-13, atol=1e-15)  # the last row sees every key

@@ -133,3 +133,27 @@ def test_dq_rows_equal_dense_rows(dtype):
     rows = np.array([0, 3, 31, 69])
     np.testing.assert_allclose(dq_rows_fp64(q, k, v, do, rows, dtype=dtype, key_block=16), dq[rows],
                                rtol=1e-11, atol=1e-13)
+
+
+@pytest.mark.parametrize("n,h,d", [(9, 1, 4), (40, 2, 8)])
+def test_causal_gradients_match_torch_autograd(n, h, d):
+    torch = pytest.importorskip("torch")
+    q, k, v, do = _inputs(7 * n, n, h, d)
+    dq, dk, dv = attention_backward_fp64(q, k, v, do, dtype="f32", causal=True)
+    tq, tk, tv = (torch.tensor(x.astype(np.float64).transpose(1, 0, 2), requires_grad=True) for x in (q, k, v))
+    s = tq @ tk.transpose(1, 2) / np.sqrt(d)
+    s = s.masked_fill(torch.triu(torch.ones(n, n, dtype=torch.bool), 1), float("-inf"))
+    (torch.softmax(s, dim=-1) @ tv).backward(torch.tensor(do.astype(np.float64).transpose(1, 0, 2)))
+    for mine, t in ((dq, tq), (dk, tk), (dv, tv)):
+        np.testing.assert_allclose(mine, t.grad.numpy().transpose(1, 0, 2), rtol=1e-10, atol=1e-13)
+
+
+@pytest.mark.parametrize("ls,n", [([3], 21), ([2, 2], 18), ([3], 50), ([4], 13)])
+def test_causal_task_decomposition_equals_dense(ls, n):
+    prod_c = int(np.prod([l * (l - 1) + 1 for l in ls]))
+    plan = make_plan(n, ls, pad=n % prod_c != 0, causal=True)
+    q, k, v, do = _inputs(60 + n, n, 2, 6)
+    dense = attention_backward_fp64(q, k, v, do, dtype="f32", causal=True)
+    split = recompose_backward_fp64(q, k, v, do, plan, dtype="f32")
+    for a, b in zip(split, dense):
+        np.testing.assert_allclose(a, b, rtol=1e-11, atol=1e-13)

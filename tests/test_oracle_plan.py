@@ -176,3 +176,19 @@ def test_serialization_round_trip(ls):
             nr = rec[pos]; pos += 1
             pos += 2 * nr
     assert pos == len(rec)
+
+
+@pytest.mark.parametrize("ls,unit", [([3], 2), ([4], 1), ([2, 2], 1), ([3, 2], 1), ([1], 5)])
+def test_causal_coverage_is_the_lower_triangle_once(ls, unit):
+    from oracle.plan import make_plan as mk
+    n = int(np.prod([l * (l - 1) + 1 for l in ls])) * unit
+    plan = mk(n, ls, causal=True)
+    full = mk(n, ls).coverage()
+    cov = plan.coverage()
+    u = plan.n_units
+    lower = np.tril(np.ones((u, u), dtype=bool))
+    assert (cov[lower] >= 0).all() and (cov[~lower] == -1).all()
+    np.testing.assert_array_equal(cov[lower], full[lower])  # same owners as the non-causal plan
+    for task in plan.tasks:
+        for a in range(len(task.units)):
+            assert all(b0 + c - 1 <= a for b0, c in task.key_runs(a, True))

@@ -128,3 +128,14 @@ def test_padded_segments_stop_at_n():
         make_plan(50, [3])
     with pytest.raises(Exception):  # fewer tokens than units
         make_plan(5, [3], pad=True)
+
+
+@pytest.mark.parametrize("ls,n", [([3], 21), ([4], 13 * 3), ([2, 2], 18), ([3, 2], 42), ([1], 9), ([3], 50)])
+def test_causal_recompose_equals_dense_causal_attention(ls, n):
+    prod_c = int(np.prod([l * (l - 1) + 1 for l in ls]))
+    plan = make_plan(n, ls, pad=n % prod_c != 0, causal=True)
+    q, k, v = gen_qkv(500 + n, n, 2, 8, dtype="f32")
+    o_ref, lse_ref = attention_fp64(q, k, v, dtype="f32", causal=True)
+    o, lse = recompose_fp64(q, k, v, plan, dtype="f32")
+    np.testing.assert_allclose(o, o_ref, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, lse_ref, rtol=1e-12)
