@@ -67,6 +67,11 @@ typedef enum {
  * positions >= N are padding that no query block, key run or copy touches, so the result
  * is attention over the N real tokens.  Without this flag an N off the unit grid is EDIVIDE. */
 #define CQSA_FLAG_PAD 0x4u
+/* Causal attention: row i attends keys j <= i.  The division and owners are unchanged;
+ * inside a task (its tokens in ascending order) a unit pair is kept only when the key
+ * unit does not come after the query unit, and the diagonal unit block is masked
+ * element by element.  useful_flop becomes 2 N (N+1) d H. */
+#define CQSA_FLAG_CAUSAL 0x8u
 
 #define CQSA_MAX_LEVELS 12
 #define CQSA_MAX_L 10

@@ -18,7 +18,7 @@ import numpy as np
 
 __all__ = [
     "CqsaError", "load", "CQSA_BF16", "CQSA_F32", "CQSA_RES_DEVICE", "CQSA_RES_HOST_PINNED",
-    "CQSA_FLAG_HOST_ACC", "CQSA_FLAG_KV_SINGLE", "CQSA_FLAG_PAD", "MODE_NAMES",
+    "CQSA_FLAG_HOST_ACC", "CQSA_FLAG_KV_SINGLE", "CQSA_FLAG_PAD", "CQSA_FLAG_CAUSAL", "MODE_NAMES",
     "cqsa_version", "cqsa_difference_set", "cqsa_plan_create", "cqsa_plan_info_get", "cqsa_plan_schedule",
     "cqsa_plan_coverage", "cqsa_plan_destroy", "cqsa_workspace_size", "cqsa_partials", "cqsa_merge",
     "cqsa_forward", "cqsa_backward_workspace_size", "cqsa_backward", "cqsa_plan_estimate", "cqsa_status_string", "cqsa_last_error", "Plan",
@@ -26,7 +26,7 @@ __all__ = [
 
 CQSA_BF16, CQSA_F32 = 0, 1
 CQSA_RES_DEVICE, CQSA_RES_HOST_PINNED = 0, 1
-CQSA_FLAG_HOST_ACC, CQSA_FLAG_KV_SINGLE, CQSA_FLAG_PAD = 0x1, 0x2, 0x4
+CQSA_FLAG_HOST_ACC, CQSA_FLAG_KV_SINGLE, CQSA_FLAG_PAD, CQSA_FLAG_CAUSAL = 0x1, 0x2, 0x4, 0x8
 MODE_NAMES = {1: "device_acc_kv2", 2: "host_acc_kv2", 3: "device_acc_kv1", 4: "host_acc_kv1"}
 MAX_LEVELS = 12
 

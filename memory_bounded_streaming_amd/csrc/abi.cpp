@@ -121,7 +121,7 @@ cqsa_status cqsa_plan_info_get(const cqsa_plan* plan, cqsa_plan_info* out) {
     out->stream_workspace_bytes = p.stream_fp.bytes;
     out->device_workspace_bytes = p.device_ws;
     out->host_acc_bytes = p.host_acc_bytes;
-    out->useful_flop = 4.0 * double(p.n) * double(p.n) * p.d * p.heads;
+    out->useful_flop = p.useful_flop();
     out->padded_tokens = p.n_pad;
     return ok();
   });

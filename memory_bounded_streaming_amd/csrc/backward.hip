@@ -196,7 +196,7 @@ __device__ __forceinline__ uint4 load_tr_chunk(const u16* row, int64_t t0, int f
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-template <int D>
+template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512) void attn_bwd_dkdv_bf16(BwdParams P) {
   using T = BwdKTile<D>;
   constexpr int NKK = D / 16;
@@ -318,13 +318,14 @@ __global__ __launch_bounds__(512) void attn_bwd_dkdv_bf16(BwdParams P) {
   const float c2 = P.scale_log2;
   const int prow = (col & ~12) | ((col & 4) << 1) | ((col & 8) >> 1);
 
-  TileCursor cur = cursor_begin(runs, nrun);
+  constexpr int kNoCut = 0x3FFFFFFF;  // query runs are never cut (causal masking is below)
+  TileCursor cur = cursor_begin(runs, nrun, kNoCut);
   TileCursor nxt = cur;
   int stage = 0;
   if (cur.run < nrun) {
     fetch(cur);
     stash(0);
-    cursor_next(nxt, runs, nrun, T::QT);
+    cursor_next(nxt, runs, nrun, T::QT, kNoCut);
     if (nxt.run < nrun) fetch(nxt);
   }
   __syncthreads();
@@ -350,6 +351,14 @@ __global__ __launch_bounds__(512) void attn_bwd_dkdv_bf16(BwdParams P) {
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(*reinterpret_cast<const uint4*>(gp + 16 * kk)),
                                                       as_bf16x8(*reinterpret_cast<const uint4*>(vrow + 16 * kk)), dp, 0, 0, 0);
       }
+    }
+    // causal diagonal run: query k0 + q of the run sees this lane's key kj only if
+    // k0 + q >= diag + kj
+    if (CAUSAL && cur.diag >= 0 && cur.k0 < cur.diag + (tile + 1) * T::KB) {
+      const int lim = cur.diag + kj - cur.k0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (16 * (i >> 3) + 8 * hl + (i & 7) < lim) s[i] = -INFINITY;
     }
     // value i holds query 16*(i/8) + 8*hl + i%8 of the tile (and key col); each half m
     // of the values is turned into P and dS and consumed by
@@ -382,7 +391,7 @@ __global__ __launch_bounds__(512) void attn_bwd_dkdv_bf16(BwdParams P) {
     cur = nxt;
     if (cur.run < nrun) {
       stash(stage ^ 1);
-      cursor_next(nxt, runs, nrun, T::QT);
+      cursor_next(nxt, runs, nrun, T::QT, kNoCut);
       if (nxt.run < nrun) fetch(nxt);
     }
     stage ^= 1;
@@ -532,13 +541,14 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_bf16(BwdParams P) {
   const float c2 = P.scale_log2;
   const int prow = (col & ~12) | ((col & 4) << 1) | ((col & 8) >> 1);
 
-  TileCursor cur = cursor_begin(runs, nrun);
+  const int qhi = min(it.q_len, (tile + 1) * T::QB);
+  TileCursor cur = cursor_begin(runs, nrun, qhi);
   TileCursor nxt = cur;
   int stage = 0;
   if (cur.run < nrun) {
     fetch(cur);
     stash(0);
-    cursor_next(nxt, runs, nrun, T::KT);
+    cursor_next(nxt, runs, nrun, T::KT, qhi);
     if (nxt.run < nrun) fetch(nxt);
   }
   __syncthreads();
@@ -570,6 +580,13 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_bf16(BwdParams P) {
       for (int i = 0; i < 16; ++i)
         if (16 * (i >> 3) + 8 * hl + (i & 7) >= nv) s[i] = -INFINITY;
     }
+    // causal diagonal run: this lane's query qi sees key k0 + j only if k0 + j <= diag + qi
+    if (cur.diag >= 0 && cur.k0 + T::KT - 1 > cur.diag + tile * T::QB) {
+      const int lim = cur.diag + qi - cur.k0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (16 * (i >> 3) + 8 * hl + (i & 7) > lim) s[i] = -INFINITY;
+    }
     bf16x8 db[2];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -589,7 +606,7 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_bf16(BwdParams P) {
     cur = nxt;
     if (cur.run < nrun) {
       stash(stage ^ 1);
-      cursor_next(nxt, runs, nrun, T::KT);
+      cursor_next(nxt, runs, nrun, T::KT, qhi);
       if (nxt.run < nrun) fetch(nxt);
     }
     stage ^= 1;
@@ -650,10 +667,13 @@ __global__ __launch_bounds__(64) void attn_bwd_dq_f32(BwdParams P) {
   float dq[D];
 #pragma unroll
   for (int t = 0; t < D; ++t) dq[t] = 0.f;
+  const int qhi = min(it.q_len, (tile + 1) * QT);
   for (int ri = 0; ri < it.nrun; ++ri) {
     const KeyRun run = P.runs[it.run0 + ri];
-    for (int k0 = 0; k0 < run.len; k0 += KT) {
-      const int nv = min(KT, run.len - k0);
+    const int rlen = run.diag >= 0 ? min(run.len, run.diag + qhi) : run.len;
+    const int lim = run.diag >= 0 ? run.diag + qi : 0x7FFFFFFF;  // causal: keys <= lim
+    for (int k0 = 0; k0 < rlen; k0 += KT) {
+      const int nv = min(KT, rlen - k0);
       __syncthreads();
       for (int c = lane; c < KT * D; c += 64) {
         const int kr = c / D, kc = c % D;
@@ -663,12 +683,12 @@ __global__ __launch_bounds__(64) void attn_bwd_dq_f32(BwdParams P) {
       __syncthreads();
       for (int j = 0; j < nv; ++j) {
         float s = 0.f, dp = 0.f;
-#pragma unroll
+#pragma unroll 8
         for (int t = 0; t < D; ++t) {
           s = fmaf(qs[lane * RS + t], ks[j * D + t], s);
           dp = fmaf(gs[lane * RS + t], vs[j * D + t], dp);
         }
-        const float p = __builtin_amdgcn_exp2f(fmaf(s, c2, -lq));
+        const float p = k0 + j <= lim ? __builtin_amdgcn_exp2f(fmaf(s, c2, -lq)) : 0.f;
         const float ds = p * (dp - dl);
 #pragma unroll
         for (int t = 0; t < D; ++t) dq[t] = fmaf(ds, ks[j * D + t], dq[t]);
@@ -731,12 +751,14 @@ __global__ __launch_bounds__(128) void attn_bwd_dkdv_f32(BwdParams P) {
       __syncthreads();
       for (int i = 0; i < nv; ++i) {
         float s = 0.f, dp = 0.f;
-#pragma unroll
+#pragma unroll 8
         for (int t = 0; t < D; ++t) {
           s = fmaf(ks[lane * RS + t], qs[i * D + t], s);
           dp = fmaf(vs[lane * RS + t], gs[i * D + t], dp);
         }
-        const float p = __builtin_amdgcn_exp2f(fmaf(s, c2, -ls[i]));
+        // causal diagonal run: query q0 + i sees this lane's key kj only if q0 + i >= diag + kj
+        const bool vis = run.diag < 0 || q0 + i >= run.diag + kj;
+        const float p = vis ? __builtin_amdgcn_exp2f(fmaf(s, c2, -ls[i])) : 0.f;
         if (wave == 0) {
 #pragma unroll
           for (int t = 0; t < D; ++t) acc[t] = fmaf(p, gs[i * D + t], acc[t]);
@@ -847,20 +869,26 @@ BwdParams bwd_params(const BwdLaunch& a) {
 }  // namespace
 
 hipError_t launch_bwd_dkdv(const BwdLaunch& a, hipStream_t stream) {
-  if (a.n_items <= 0 || a.q_len <= 0) return hipSuccess;
+  if (a.n_kitems <= 0 || a.q_len <= 0) return hipSuccess;
   BwdParams p = bwd_params(a);
   p.g0 = a.dk_out;
   p.g1 = a.dv_out;
+  p.items = a.kitems;
+  p.runs = a.kruns;
   const int kb = bwd_key_tile(a.dtype);
   p.tiles_per_item = (a.q_len + kb - 1) / kb;
-  const int64_t blocks = int64_t(a.n_items) * p.tiles_per_item * a.heads;
+  const int64_t blocks = int64_t(a.n_kitems) * p.tiles_per_item * a.heads;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const dim3 grid(static_cast<unsigned>(blocks));
   if (a.dtype == CQSA_BF16) {
-    if (a.d == 128)
-      hipLaunchKernelGGL(attn_bwd_dkdv_bf16<128>, grid, dim3(BwdKTile<128>::NT), 0, stream, p);
+    if (a.d == 128 && a.causal)
+      hipLaunchKernelGGL((attn_bwd_dkdv_bf16<128, true>), grid, dim3(BwdKTile<128>::NT), 0, stream, p);
+    else if (a.d == 128)
+      hipLaunchKernelGGL((attn_bwd_dkdv_bf16<128, false>), grid, dim3(BwdKTile<128>::NT), 0, stream, p);
+    else if (a.d == 64 && a.causal)
+      hipLaunchKernelGGL((attn_bwd_dkdv_bf16<64, true>), grid, dim3(BwdKTile<64>::NT), 0, stream, p);
     else if (a.d == 64)
-      hipLaunchKernelGGL(attn_bwd_dkdv_bf16<64>, grid, dim3(BwdKTile<64>::NT), 0, stream, p);
+      hipLaunchKernelGGL((attn_bwd_dkdv_bf16<64, false>), grid, dim3(BwdKTile<64>::NT), 0, stream, p);
     else
       return hipErrorInvalidValue;
   } else {

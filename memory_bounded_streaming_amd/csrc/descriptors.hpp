@@ -10,7 +10,11 @@ namespace cqsa {
 struct KeyRun {
   int64_t start;  // first key row
   int32_t len;    // number of keys (may be any positive count)
-  int32_t pad;
+  int32_t diag;   // -1: every row of the run pairs with every row of the item.  >= 0:
+                  // the causal diagonal run.  In the tables whose items are query
+                  // blocks (forward, dQ), key j of the run is visible to query i of the
+                  // item only if j <= diag + i; in the key-block table of a causal dK/dV
+                  // pass, query j of the run sees key i of the item only if j >= diag + i
 };
 
 // One query block and its admitted keys.

@@ -27,39 +27,46 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast
 
 // Cursor over the tiles of an item's key runs.  The current run's start and length
 // are kept in (scalar) registers and reloaded only when the cursor enters a new run.
+// On a causal diagonal run (diag >= 0) the run is cut after the last key any query
+// of the workgroup can see: key j is visible to query i only if j <= diag + i, and the
+// workgroup's queries end before qhi.
 struct TileCursor {
   int run;        // index of the current run (nrun when exhausted)
   int k0;         // first key of the tile within the run
-  int len;        // length of the current run
+  int len;        // length of the current run (cut as above on a diagonal run)
+  int diag;       // the run's diagonal offset, -1 if every key is visible
   int64_t start;  // first key row of the current run
 };
 
-__device__ __forceinline__ void cursor_settle(TileCursor& c, const KeyRun* runs, int nrun) {
+__device__ __forceinline__ void cursor_settle(TileCursor& c, const KeyRun* runs, int nrun, int qhi) {
   while (c.run < nrun) {
     const KeyRun r = runs[c.run];
-    if (r.len > 0) {
+    const int len = r.diag >= 0 ? min(r.len, r.diag + qhi) : r.len;
+    if (len > 0) {
       c.start = r.start;
-      c.len = r.len;
+      c.len = len;
+      c.diag = r.diag;
       return;
     }
     ++c.run;
   }
   c.len = 0;
+  c.diag = -1;
   c.start = 0;
 }
 
-__device__ __forceinline__ TileCursor cursor_begin(const KeyRun* runs, int nrun) {
-  TileCursor c{0, 0, 0, 0};
-  cursor_settle(c, runs, nrun);
+__device__ __forceinline__ TileCursor cursor_begin(const KeyRun* runs, int nrun, int qhi) {
+  TileCursor c{0, 0, 0, -1, 0};
+  cursor_settle(c, runs, nrun, qhi);
   return c;
 }
 
-__device__ __forceinline__ void cursor_next(TileCursor& c, const KeyRun* runs, int nrun, int kt) {
+__device__ __forceinline__ void cursor_next(TileCursor& c, const KeyRun* runs, int nrun, int kt, int qhi) {
   c.k0 += kt;
   if (c.k0 >= c.len) {
     ++c.run;
     c.k0 = 0;
-    cursor_settle(c, runs, nrun);
+    cursor_settle(c, runs, nrun, qhi);
   }
 }
 

@@ -94,16 +94,20 @@ cqsa_status device_tables(const Plan& p, DeviceTables& out, std::string& why) {
   const int64_t b1 = align_up(int64_t(p.dev_runs.size()) * sizeof(KeyRun));
   const int64_t b2 = align_up(int64_t(p.stream_items.size()) * sizeof(WorkItem));
   const int64_t b3 = align_up(int64_t(p.stream_runs.size()) * sizeof(KeyRun));
+  const int64_t b4 = align_up(int64_t(p.dev_kitems.size()) * sizeof(WorkItem));
+  const int64_t b5 = align_up(int64_t(p.dev_kruns.size()) * sizeof(KeyRun));
   std::lock_guard<std::mutex> lock(p.dev_mu);
   char* base = nullptr;
   for (auto& e : p.dev_tables)
     if (e.first == dev) base = static_cast<char*>(e.second);
   if (base == nullptr) {
-    std::vector<char> host(b0 + b1 + b2 + b3, 0);
+    std::vector<char> host(b0 + b1 + b2 + b3 + b4 + b5, 0);
     std::memcpy(host.data(), p.dev_items.data(), p.dev_items.size() * sizeof(WorkItem));
     std::memcpy(host.data() + b0, p.dev_runs.data(), p.dev_runs.size() * sizeof(KeyRun));
     std::memcpy(host.data() + b0 + b1, p.stream_items.data(), p.stream_items.size() * sizeof(WorkItem));
     std::memcpy(host.data() + b0 + b1 + b2, p.stream_runs.data(), p.stream_runs.size() * sizeof(KeyRun));
+    std::memcpy(host.data() + b0 + b1 + b2 + b3, p.dev_kitems.data(), p.dev_kitems.size() * sizeof(WorkItem));
+    std::memcpy(host.data() + b0 + b1 + b2 + b3 + b4, p.dev_kruns.data(), p.dev_kruns.size() * sizeof(KeyRun));
     void* mem = nullptr;
     HIP_TRY(hipMalloc(&mem, host.size()));
     hipError_t e = hipMemcpy(mem, host.data(), host.size(), hipMemcpyHostToDevice);
@@ -119,7 +123,9 @@ cqsa_status device_tables(const Plan& p, DeviceTables& out, std::string& why) {
   out.dev_runs = reinterpret_cast<const KeyRun*>(base + b0);
   out.stream_items = reinterpret_cast<const WorkItem*>(base + b0 + b1);
   out.stream_runs = reinterpret_cast<const KeyRun*>(base + b0 + b1 + b2);
-  out.bytes = b0 + b1 + b2 + b3;
+  out.dev_kitems = reinterpret_cast<const WorkItem*>(base + b0 + b1 + b2 + b3);
+  out.dev_kruns = reinterpret_cast<const KeyRun*>(base + b0 + b1 + b2 + b3 + b4);
+  out.bytes = b0 + b1 + b2 + b3 + b4 + b5;
   return CQSA_OK;
 }
 
@@ -239,7 +245,7 @@ cqsa_status forward_device(const Plan& p, const void* q, const void* k, const vo
     stats->peak_device_bytes = p.device_ws + t.bytes;
     stats->n_attn_launches = 1;
     stats->n_merge_launches = 1;
-    stats->useful_flop = 4.0 * double(p.n) * double(p.n) * p.d * p.heads;
+    stats->useful_flop = p.useful_flop();
   }
   return CQSA_OK;
 }
@@ -534,7 +540,7 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
     stats->n_merge_launches = n_merge;
     stats->n_h2d_copies = n_h2d;
     stats->n_d2h_copies = n_d2h;
-    stats->useful_flop = 4.0 * double(p.n) * double(p.n) * p.d * p.heads;
+    stats->useful_flop = p.useful_flop();
     stats->t_total_ms = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
   }
   return CQSA_OK;
@@ -636,6 +642,11 @@ cqsa_status run_backward(const Plan& p, const void* q, const void* k, const void
   b.items = t.dev_items;
   b.runs = t.dev_runs;
   b.n_items = static_cast<int>(p.dev_items.size());
+  const bool causal = (p.flags & CQSA_FLAG_CAUSAL) != 0;
+  b.kitems = causal ? t.dev_kitems : t.dev_items;
+  b.kruns = causal ? t.dev_kruns : t.dev_runs;
+  b.n_kitems = static_cast<int>(causal ? p.dev_kitems.size() : p.dev_items.size());
+  b.causal = causal;
   b.q_len = static_cast<int>(p.unit);
   b.scale = static_cast<float>(1.0 / std::sqrt(double(p.d)));
   HIP_TRY(tm.begin(PH_ATTN, stream, ev));
@@ -668,7 +679,7 @@ cqsa_status run_backward(const Plan& p, const void* q, const void* k, const void
     stats->peak_device_bytes = L.total + t.bytes;
     stats->n_attn_launches = 2;
     stats->n_merge_launches = 4;
-    stats->useful_flop = 10.0 * double(p.n) * double(p.n) * p.d * p.heads;
+    stats->useful_flop = 2.5 * p.useful_flop();
   }
   return CQSA_OK;
 }

@@ -15,6 +15,8 @@ struct DeviceTables {
   const KeyRun* dev_runs;
   const WorkItem* stream_items;
   const KeyRun* stream_runs;
+  const WorkItem* dev_kitems;  // causal dK/dV tables (empty without causality)
+  const KeyRun* dev_kruns;
   int64_t bytes;
 };
 

@@ -158,13 +158,15 @@ __global__ __launch_bounds__(512) void attn_partial_bf16(AttnParams P) {
   const int grp = lane >> 4, sl = lane & 15;
   const int tr_off = (8 * (grp >> 1) + (sl >> 2)) * T::VSTR + 16 * (grp & 1) + 4 * (sl & 3);
 
-  TileCursor cur = cursor_begin(runs, nrun);
+  // queries of this workgroup: [tile * QT, qhi) of the item
+  const int qhi = min(it.q_len, (tile + 1) * T::QT);
+  TileCursor cur = cursor_begin(runs, nrun, qhi);
   TileCursor nxt = cur;
   int stage = 0;
   if (cur.run < nrun) {
     fetch(cur);
     stash(0);
-    cursor_next(nxt, runs, nrun, T::KT);
+    cursor_next(nxt, runs, nrun, T::KT, qhi);
     if (nxt.run < nrun) fetch(nxt);
   }
   __syncthreads();
@@ -194,6 +196,15 @@ __global__ __launch_bounds__(512) void attn_partial_bf16(AttnParams P) {
 #pragma unroll
         for (int i = 0; i < 16; ++i)
           if (32 * st + 16 * (i >> 3) + 8 * hl + (i & 7) >= nv) s[st][i] = -INFINITY;
+    }
+    // causal diagonal: this lane's query qi sees key k0 + j only if k0 + j <= diag + qi
+    if (cur.diag >= 0 && cur.k0 + T::KT - 1 > cur.diag + tile * T::QT) {
+      const int lim = cur.diag + qi - cur.k0;
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (32 * st + 16 * (i >> 3) + 8 * hl + (i & 7) > lim) s[st][i] = -INFINITY;
     }
     float mx = s[0][0];
 #pragma unroll
@@ -246,7 +257,7 @@ __global__ __launch_bounds__(512) void attn_partial_bf16(AttnParams P) {
     cur = nxt;
     if (cur.run < nrun) {
       stash(stage ^ 1);
-      cursor_next(nxt, runs, nrun, T::KT);
+      cursor_next(nxt, runs, nrun, T::KT, qhi);
       if (nxt.run < nrun) fetch(nxt);
     }
     stage ^= 1;
@@ -308,10 +319,14 @@ __global__ __launch_bounds__(64) void attn_partial_f32(AttnParams P) {
   }
   float m_run = -INFINITY, l_run = 0.f;
   const float c2 = P.scale_log2;
+  const int qhi = min(it.q_len, (tile + 1) * QT);
   for (int ri = 0; ri < it.nrun; ++ri) {
     const KeyRun run = P.runs[it.run0 + ri];
-    for (int k0 = 0; k0 < run.len; k0 += KT) {
-      const int nv = min(KT, run.len - k0);
+    const int rlen = run.diag >= 0 ? min(run.len, run.diag + qhi) : run.len;
+    // causal diagonal run: key k0 + j is visible to this row only if k0 + j <= lim
+    const int lim = run.diag >= 0 ? run.diag + qi : 0x7FFFFFFF;
+    for (int k0 = 0; k0 < rlen; k0 += KT) {
+      const int nv = min(KT, rlen - k0);
       const int64_t kbase = (run.start + k0) * rs + head * D;
       __syncthreads();
       for (int c = lane; c < KT * D / 4; c += 64) {
@@ -332,7 +347,7 @@ __global__ __launch_bounds__(64) void attn_partial_f32(AttnParams P) {
         float acc = 0.f;
 #pragma unroll
         for (int t = 0; t < D; ++t) acc = fmaf(q[t], kf[j * D + t], acc);
-        sc[j] = j < nv ? acc * c2 : -INFINITY;
+        sc[j] = j < nv && k0 + j <= lim ? acc * c2 : -INFINITY;
         mx = fmaxf(mx, sc[j]);
       }
       const float m_new = fmaxf(m_run, mx);

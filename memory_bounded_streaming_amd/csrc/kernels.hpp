@@ -88,9 +88,13 @@ struct BwdLaunch {
   float* dq_out;
   float* dk_out;
   float* dv_out;
-  const WorkItem* items;
+  const WorkItem* items;   // query blocks and their key runs (dQ)
   const KeyRun* runs;
   int n_items;
+  const WorkItem* kitems;  // key blocks and their query runs (dK/dV)
+  const KeyRun* kruns;
+  int n_kitems;
+  bool causal;         // runs may carry a causal diagonal (KeyRun::diag >= 0)
   int q_len;           // rows of every item in this launch (upper bound)
   float scale;
 };

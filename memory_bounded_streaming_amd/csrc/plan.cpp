@@ -103,6 +103,7 @@ namespace {
 // (its keys all belong to other tasks); its partial is then the empty triple.
 cqsa_status build_tasks(Plan& p, std::string& why) {
   (void)why;
+  const bool causal = (p.flags & CQSA_FLAG_CAUSAL) != 0;
   const int levels = static_cast<int>(p.ls.size());
   std::vector<int64_t> parent_len(levels + 1), chunk_len(levels);
   parent_len[0] = p.n_units;
@@ -155,7 +156,7 @@ cqsa_status build_tasks(Plan& p, std::string& why) {
           const int cb = chunk_of[static_cast<size_t>(k) * tu + b];
           ok = (ca != cb) || (ca == task.ids[k]);
         }
-        if (!ok) continue;
+        if (!ok || (causal && b > a)) continue;
         ++task.admitted_units;
         if (!runs.empty() && runs.back().start + runs.back().count == b)
           ++runs.back().count;
@@ -214,10 +215,22 @@ void build_schedule(Plan& p) {
   }
 }
 
+// Does task t admit local units (a, b) (in either role; the CQS Mask is symmetric)?
+bool admitted_pair(const Plan& p, const Task& t, int64_t a, int64_t b) {
+  for (const UnitRun& r : t.runs[a])
+    if (b >= r.start && b < r.start + r.count) return true;
+  // causal runs of a stop at a: look at b's runs for a (b > a)
+  for (const UnitRun& r : t.runs[b])
+    if (a >= r.start && a < r.start + r.count) return true;
+  (void)p;
+  return false;
+}
+
 // Kernel descriptor tables.  Key runs are split wherever the task's local order is not
 // globally contiguous, in both tables, so device-resident and streamed execution walk
 // identical key tiles and give identical bits.
 void build_descriptors(Plan& p) {
+  const bool causal = (p.flags & CQSA_FLAG_CAUSAL) != 0;
   p.dev_items.clear();
   p.dev_runs.clear();
   p.stream_items.clear();
@@ -239,9 +252,11 @@ void build_descriptors(Plan& p) {
           while (e < end && t.units[e] == t.units[e - 1] + 1) ++e;
           // keys at or past N are padding: clip the run there (units are ascending in it)
           const int64_t len = std::min((e - b) * p.unit, p.n - t.units[b] * p.unit);
+          // causal: the piece that ends with the query unit itself holds the diagonal
+          const int32_t diag = causal && e == static_cast<int64_t>(a) + 1 ? static_cast<int32_t>((static_cast<int64_t>(a) - b) * p.unit) : -1;
           if (len > 0) {
-            p.dev_runs.push_back({t.units[b] * p.unit, static_cast<int32_t>(len), 0});
-            p.stream_runs.push_back({b * p.unit, static_cast<int32_t>(len), 0});
+            p.dev_runs.push_back({t.units[b] * p.unit, static_cast<int32_t>(len), diag});
+            p.stream_runs.push_back({b * p.unit, static_cast<int32_t>(len), diag});
             keys += len;
           }
           b = e;
@@ -256,11 +271,49 @@ void build_descriptors(Plan& p) {
   // heaviest query blocks first in the one-launch device path (load balance only)
   std::stable_sort(p.dev_items.begin(), p.dev_items.end(),
                    [](const WorkItem& x, const WorkItem& y) { return x.keys > y.keys; });
+
+  p.dev_kitems.clear();
+  p.dev_kruns.clear();
+  if (!causal) return;
+  for (const Task& t : p.tasks) {
+    const int64_t tu = static_cast<int64_t>(t.units.size());
+    for (int64_t a = 0; a < tu; ++a) {
+      WorkItem ki{};
+      ki.q_row0 = t.units[a] * p.unit;
+      ki.out_row0 = int64_t(t.slot[a]) * p.n + t.units[a] * p.unit;
+      ki.q_len = static_cast<int32_t>(p.unit_rows(t.units[a]));
+      ki.run0 = static_cast<int32_t>(p.dev_kruns.size());
+      int64_t rows = 0;
+      // query units b >= a that the task admits with a (the mask is symmetric in a, b)
+      int64_t b = a;
+      while (b < tu) {
+        if (!admitted_pair(p, t, a, b)) {
+          ++b;
+          continue;
+        }
+        int64_t e = b + 1;
+        while (e < tu && t.units[e] == t.units[e - 1] + 1 && admitted_pair(p, t, a, e)) ++e;
+        const int64_t len = std::min((e - b) * p.unit, p.n - t.units[b] * p.unit);
+        if (len > 0) {
+          p.dev_kruns.push_back({t.units[b] * p.unit, static_cast<int32_t>(len), b == a ? 0 : -1});
+          rows += len;
+        }
+        b = e;
+      }
+      ki.nrun = static_cast<int32_t>(p.dev_kruns.size()) - ki.run0;
+      ki.keys = static_cast<int32_t>(std::min<int64_t>(rows, INT32_MAX));
+      if (ki.q_len > 0) p.dev_kitems.push_back(ki);
+    }
+  }
+  std::stable_sort(p.dev_kitems.begin(), p.dev_kitems.end(),
+                   [](const WorkItem& x, const WorkItem& y) { return x.keys > y.keys; });
 }
 
 int64_t descriptor_bytes(const Plan& p) {
   return align_up(int64_t(p.dev_items.size()) * sizeof(WorkItem)) +
          align_up(int64_t(p.dev_runs.size()) * sizeof(KeyRun)) +
+         align_up(int64_t(p.dev_kitems.size()) * sizeof(WorkItem)) +
+         align_up(int64_t(p.dev_kruns.size()) * sizeof(KeyRun)) +
          align_up(int64_t(p.stream_items.size()) * sizeof(WorkItem)) +
          align_up(int64_t(p.stream_runs.size()) * sizeof(KeyRun));
 }
@@ -367,7 +420,7 @@ cqsa_status build_plan(int64_t n, int heads, int d, cqsa_dtype dtype, const int3
                        int64_t budget, uint32_t flags, Plan& out, std::string& why) {
   if (n < 1 || heads < 1 || (d != 64 && d != 128) || ls == nullptr || n_levels < 0 ||
       n_levels > CQSA_MAX_LEVELS || budget < 0 || (dtype != CQSA_BF16 && dtype != CQSA_F32) ||
-      (flags & ~(CQSA_FLAG_HOST_ACC | CQSA_FLAG_KV_SINGLE | CQSA_FLAG_PAD)) != 0) {
+      (flags & ~(CQSA_FLAG_HOST_ACC | CQSA_FLAG_KV_SINGLE | CQSA_FLAG_PAD | CQSA_FLAG_CAUSAL)) != 0) {
     why = "invalid argument (need n>=1, heads>=1, head_dim 64 or 128, 0<=n_levels<=8, budget>=0, known dtype/flags)";
     return CQSA_EINVAL;
   }
@@ -453,7 +506,7 @@ cqsa_status estimate_plan(int64_t n, int heads, int d, cqsa_dtype dtype, const i
                           std::string& why) {
   if (n < 1 || heads < 1 || (d != 64 && d != 128) || ls == nullptr || n_levels < 0 ||
       n_levels > CQSA_MAX_LEVELS || budget < 0 || (dtype != CQSA_BF16 && dtype != CQSA_F32) ||
-      (flags & ~(CQSA_FLAG_HOST_ACC | CQSA_FLAG_KV_SINGLE | CQSA_FLAG_PAD)) != 0 || !(r.attn_tflops > 0) ||
+      (flags & ~(CQSA_FLAG_HOST_ACC | CQSA_FLAG_KV_SINGLE | CQSA_FLAG_PAD | CQSA_FLAG_CAUSAL)) != 0 || !(r.attn_tflops > 0) ||
       !(r.merge_gbs > 0) || !(r.h2d_gbs > 0) || !(r.d2h_gbs > 0)) {
     why = "invalid argument (see cqsa_plan_create; every rate must be positive)";
     return CQSA_EINVAL;
@@ -529,7 +582,7 @@ cqsa_status estimate_plan(int64_t n, int heads, int d, cqsa_dtype dtype, const i
   // accumulator (or, at the last visit, O and LSE); a single visit reads its partial
   const int64_t part = heads * int64_t(d + 2) * 4, fin = heads * (int64_t(d) * p.elem_bytes() + 4);
   out.merge_bytes = p.visits == 1 ? p.n * (part + fin) : p.n * ((p.visits - 2) * 3 * part + 2 * part + fin);
-  out.useful_flop = 4.0 * N * N * D * H;
+  out.useful_flop = (flags & CQSA_FLAG_CAUSAL) ? 2.0 * N * (N + 1) * D * H : 4.0 * N * N * D * H;
   out.t_attn_s = out.useful_flop / (r.attn_tflops * 1e12);
   out.t_merge_s = double(out.merge_bytes) / (r.merge_gbs * 1e9);
   out.t_h2d_s = double(out.bytes_h2d) / (r.h2d_gbs * 1e9);

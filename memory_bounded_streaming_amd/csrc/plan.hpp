@@ -66,6 +66,10 @@ struct Plan {
   std::vector<KeyRun> dev_runs;
   std::vector<WorkItem> stream_items;   // item (t, a) at index t*task_units + a, block coordinates
   std::vector<KeyRun> stream_runs;
+  // causal dK/dV: (task, key unit) items whose runs are the admitted query units at or
+  // after the key unit (without causality the mask is symmetric: dev_items serve)
+  std::vector<WorkItem> dev_kitems;
+  std::vector<KeyRun> dev_kruns;
 
   Footprint stream_fp{};
   int64_t device_ws = 0;                // slots bytes of the device-resident path
@@ -82,6 +86,11 @@ struct Plan {
   int64_t row_part_bytes() const { return int64_t(heads) * (d + 2) * 4; }
   int64_t row_out_bytes() const { return int64_t(heads) * (d * elem_bytes() + 4); }
   int64_t task_tokens() const { return task_units * unit; }
+  // useful attention FLOP: 4 d H per (query, key) pair attended
+  double useful_flop() const {
+    const double nn = (flags & CQSA_FLAG_CAUSAL) ? 0.5 * double(n) * double(n + 1) : double(n) * double(n);
+    return 4.0 * nn * d * heads;
+  }
   // real query rows of global unit u (0 for a unit that is all padding)
   int64_t unit_rows(int64_t u) const { return std::max<int64_t>(0, std::min(unit, n - u * unit)); }
 };

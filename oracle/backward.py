@@ -34,7 +34,8 @@ import numpy as np
 from .attention import default_scale, to_f64
 from .plan import Plan
 
-__all__ = ["attention_backward_fp64", "task_backward_fp64", "recompose_backward_fp64", "dq_rows_fp64"]
+__all__ = ["attention_backward_fp64", "attention_backward_given_fp64", "task_backward_fp64",
+           "recompose_backward_fp64", "dq_rows_fp64"]
 
 
 def _dense_head(q, k, v, do, scale, causal=False):
@@ -68,6 +69,33 @@ def attention_backward_fp64(q, k, v, do, dtype="f32", scale=None, causal=False):
         qh, kh, vh, doh = (to_f64(x[:, h, :], dtype) for x in (q, k, v, do))
         dq, dk, dv, _ = _dense_head(qh, kh, vh, doh, scale, causal)
         out[0][:, h], out[1][:, h], out[2][:, h] = dq, dk, dv
+    return tuple(out)
+
+
+def attention_backward_given_fp64(q, k, v, o, lse, do, dtype="f32", scale=None, causal=False):
+    """(dQ, dK, dV) of the backward as an operation on its inputs, in float64.
+
+    A backward pass receives the forward's saved O and LSE (rounded to their storage
+    precision) and uses them as given: P_ij = exp(s_ij - LSE_i), Delta_i = <dO_i, O_i>,
+    then the formulas above.  With the exact O and LSE this is attention_backward_fp64;
+    with rounded ones it is what an exact implementation of the operation returns for
+    those inputs.  o: [N, H, d] in dtype (float32 or bf16 bits) or float64; lse: [H, N].
+    """
+    n, h_count, d = q.shape
+    if scale is None:
+        scale = default_scale(d)
+    o64 = np.asarray(o, dtype=np.float64) if np.asarray(o).dtype == np.float64 else to_f64(o, dtype)
+    lse64 = np.asarray(lse, dtype=np.float64)
+    out = [np.zeros((n, h_count, d)) for _ in range(3)]
+    for h in range(h_count):
+        qh, kh, vh, doh = (to_f64(x[:, h, :], dtype) for x in (q, k, v, do))
+        s = (qh @ kh.T) * scale
+        p = np.exp(s - lse64[h][:, None])
+        if causal:
+            p = np.where(np.triu(np.ones(p.shape, dtype=bool), 1), 0.0, p)
+        delta = (doh * o64[:, h, :]).sum(axis=1)
+        ds = p * (doh @ vh.T - delta[:, None])
+        out[0][:, h], out[1][:, h], out[2][:, h] = scale * (ds @ kh), scale * (ds.T @ qh), p.T @ doh
     return tuple(out)
 
 

@@ -290,3 +290,23 @@ def test_estimate_of_a_billion_tokens_needs_no_plan():
     with pytest.raises(cqsa.CqsaError) as e:
         cqsa.cqsa_plan_estimate(n, 1, 128, cqsa.CQSA_BF16, [3], rates={**RATES, "h2d_gbs": 0.0})
     assert e.value.status == -1
+
+
+CAUSAL_PLANS = [([3], 21), ([3], 7 * 100), ([4], 13 * 3), ([2, 2], 18), ([3, 2], 42), ([1], 9), ([2, 3], 42),
+                ([3], 50), ([5], 21 * 4 + 3), ([3, 3], 12845056)]
+
+
+@pytest.mark.parametrize("levels,n", CAUSAL_PLANS)
+def test_causal_schedule_and_coverage_bit_exact(levels, n):
+    prod_c = int(np.prod([l * (l - 1) + 1 for l in levels]))
+    pad = n % prod_c != 0
+    ref = make_plan(n, levels, pad=pad, causal=True)
+    flags = cqsa.CQSA_FLAG_CAUSAL | (cqsa.CQSA_FLAG_PAD if pad else 0)
+    with cqsa.Plan(n, 2, 64, cqsa.CQSA_BF16, levels, flags=flags) as p:
+        assert p.schedule().tobytes() == ref.serialize().tobytes()
+        cov = p.coverage()
+        assert cov.tobytes() == ref.coverage().tobytes()
+        u = p.info["n_units"]
+        lower = np.tril(np.ones((u, u), dtype=bool))
+        assert (cov[lower] >= 0).all() and (cov[~lower] == -1).all()
+        assert p.info["useful_flop"] == pytest.approx(2.0 * n * (n + 1) * 64 * 2)

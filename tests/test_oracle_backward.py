@@ -11,7 +11,8 @@ import pytest
 from scipy.special import softmax
 
 from memory_bounded_streaming_amd.inputs import gen_qkv, gen_tensor
-from oracle.backward import attention_backward_fp64, dq_rows_fp64, recompose_backward_fp64
+from oracle.backward import (attention_backward_fp64, attention_backward_given_fp64, dq_rows_fp64,
+                             recompose_backward_fp64)
 from oracle.plan import make_plan
 
 
@@ -157,3 +158,32 @@ def test_causal_task_decomposition_equals_dense(ls, n):
     split = recompose_backward_fp64(q, k, v, do, plan, dtype="f32")
     for a, b in zip(split, dense):
         np.testing.assert_allclose(a, b, rtol=1e-11, atol=1e-13)
+
+
+def test_grad_metric_floors_rows_that_vanish():
+    from oracle.tolerance import GRAD_ROW_FLOOR, grad_rel_err, rowwise_rel_err
+    ref = np.array([[[0.0, 0.0]], [[1.0, -2.0]]])
+    got = ref + np.array([[[1e-4, 0.0]], [[0.0, 1e-3]]])
+    assert rowwise_rel_err(got, ref) > 1e100          # the zero row breaks a pure row-wise ratio
+    assert grad_rel_err(got, ref) == pytest.approx(max(1e-4 / (GRAD_ROW_FLOOR * 2.0), 1e-3 / 2.0))
+    # causal dQ: the first query attends only itself, so its gradient row is exactly zero
+    q, k, v, do = _inputs(3, 6, 1, 4)
+    dq, _, _ = attention_backward_fp64(q, k, v, do, dtype="f32", causal=True)
+    assert np.abs(dq[0]).max() < 1e-15 and np.abs(dq[1:]).max() > 1e-3
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_given_exact_statistics_is_the_gradient(causal):
+    from oracle.attention import attention_fp64
+    n, h, d = 30, 2, 8
+    q, k, v, do = _inputs(21, n, h, d)
+    o, lse = attention_fp64(q, k, v, dtype="f32", causal=causal)
+    want = attention_backward_fp64(q, k, v, do, dtype="f32", causal=causal)
+    got = attention_backward_given_fp64(q, k, v, o, lse, do, dtype="f32", causal=causal)
+    for a, b in zip(got, want):
+        np.testing.assert_allclose(a, b, rtol=1e-11, atol=1e-13)
+    # a rounded O moves Delta and so dQ, dK (not dV, which does not involve O)
+    o_r = o.astype(np.float32)
+    got_r = attention_backward_given_fp64(q, k, v, o_r, lse, do, dtype="f32", causal=causal)
+    np.testing.assert_allclose(got_r[2], want[2], rtol=1e-11, atol=1e-13)
+    assert np.abs(got_r[0] - want[0]).max() > 0
