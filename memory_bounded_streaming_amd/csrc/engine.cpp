@@ -11,8 +11,8 @@
 // cannot hold the accumulator).  Tasks run in ascending id.  For each task the K/V
 // segments are gathered into a staging buffer on the K/V copy stream; query units are
 // streamed through a two-slot ring (Q block, partial block, accumulator block, output
-// block) on the Q copy stream; the compute stream runs the partial kernel and the merge;
-// the D2H stream returns accumulator or output blocks.  Events order every reuse of a
+// block) on the Q copy stream; the caller's stream runs the partial kernel and the
+// merge; the D2H stream returns accumulator or output blocks.  Events order every reuse of a
 // staging buffer or ring slot.
 #include "engine.hpp"
 
@@ -251,13 +251,18 @@ cqsa_status forward_device(const Plan& p, const void* q, const void* k, const vo
 }
 
 // RAII holder of the stream engine's HIP objects.
+// The engine adds three streams (K/V copies, Q copies, D2H) to the caller's stream,
+// which runs the kernels: with four hardware queues per process (the runtime's
+// default), a fifth stream would share a queue with another and serialize behind it.
 struct StreamRes {
-  hipStream_t s[4] = {nullptr, nullptr, nullptr, nullptr};  // kv, q, compute, d2h
+  hipStream_t s[3] = {nullptr, nullptr, nullptr};  // kv, q, d2h
+  hipStream_t caller = nullptr;
   std::vector<hipEvent_t> events;
   void* ws = nullptr;
   bool own_ws = false;
   float* host_acc = nullptr;
   ~StreamRes() {
+    (void)hipStreamSynchronize(caller);
     for (hipStream_t x : s)
       if (x) (void)hipStreamSynchronize(x);
     for (hipEvent_t e : events) (void)hipEventDestroy(e);
@@ -339,8 +344,9 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
     host_n = R.host_acc;
     host_ml = R.host_acc + N * nrow_f;
   }
+  R.caller = caller;
   for (auto& s : R.s) HIP_TRY(hipStreamCreateWithFlags(&s, hipStreamNonBlocking));
-  hipStream_t s_kv = R.s[0], s_q = R.s[1], s_c = R.s[2], s_d = R.s[3];
+  hipStream_t s_kv = R.s[0], s_q = R.s[1], s_c = caller, s_d = R.s[2];
   hipEvent_t start, kv_ready[2], kv_free[2], q_ready[2], c_done[2], slot_free[2], task_done[3];
   HIP_TRY(R.event(start));
   for (int i = 0; i < 3; ++i) HIP_TRY(R.event(task_done[i]));
@@ -523,6 +529,7 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
     HIP_TRY(hipEventRecord(kv_free[b], s_c));  // after the task's last launch on s_c
     HIP_TRY(hipEventRecord(task_done[ti % 3], s_c));
   }
+  HIP_TRY(hipStreamSynchronize(s_c));
   for (hipStream_t s : R.s) HIP_TRY(hipStreamSynchronize(s));
   if (progress)
     for (int64_t t = std::max<int64_t>(0, n_tasks - 2); t < n_tasks; ++t) report(t);
