@@ -53,6 +53,7 @@ struct BwdParams {
   float* g1;           // dkdv: dV slots
   const WorkItem* items;
   const KeyRun* runs;
+  int64_t n_items;
   int64_t n, np;
   int tiles_per_item;
   int heads;
@@ -206,11 +207,11 @@ __global__ __launch_bounds__(512) void attn_bwd_dkdv_bf16(BwdParams P) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, col = lane & 31;
-  const int64_t b = xcd_remap(blockIdx.x, gridDim.x);
-  const int tile = static_cast<int>(b % P.tiles_per_item);
-  const int64_t rest = b / P.tiles_per_item;
-  const int head = static_cast<int>(rest % P.heads);
-  const WorkItem it = P.items[rest / P.heads];
+  GroupCoord gc;
+  if (!group_coord(blockIdx.x, P.tiles_per_item, P.heads, P.n_items, gc)) return;
+  const int tile = gc.tile;
+  const int head = gc.head;
+  const WorkItem it = P.items[gc.item];
   const KeyRun* runs = P.runs + it.run0;
   const int nrun = it.nrun;
   const int64_t rs = static_cast<int64_t>(P.heads) * D;
@@ -453,11 +454,11 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_bf16(BwdParams P) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, col = lane & 31;
-  const int64_t b = xcd_remap(blockIdx.x, gridDim.x);
-  const int tile = static_cast<int>(b % P.tiles_per_item);
-  const int64_t rest = b / P.tiles_per_item;
-  const int head = static_cast<int>(rest % P.heads);
-  const WorkItem it = P.items[rest / P.heads];
+  GroupCoord gc;
+  if (!group_coord(blockIdx.x, P.tiles_per_item, P.heads, P.n_items, gc)) return;
+  const int tile = gc.tile;
+  const int head = gc.head;
+  const WorkItem it = P.items[gc.item];
   const KeyRun* runs = P.runs + it.run0;
   const int nrun = it.nrun;
   const int64_t rs = static_cast<int64_t>(P.heads) * D;
@@ -640,11 +641,11 @@ __global__ __launch_bounds__(64) void attn_bwd_dq_f32(BwdParams P) {
   __shared__ __attribute__((aligned(16))) float ks[KT * D];
   __shared__ __attribute__((aligned(16))) float vs[KT * D];
   const int lane = threadIdx.x;
-  const int64_t b = xcd_remap(blockIdx.x, gridDim.x);
-  const int tile = static_cast<int>(b % P.tiles_per_item);
-  const int64_t rest = b / P.tiles_per_item;
-  const int head = static_cast<int>(rest % P.heads);
-  const WorkItem it = P.items[rest / P.heads];
+  GroupCoord gc;
+  if (!group_coord(blockIdx.x, P.tiles_per_item, P.heads, P.n_items, gc)) return;
+  const int tile = gc.tile;
+  const int head = gc.head;
+  const WorkItem it = P.items[gc.item];
   const int64_t rs = static_cast<int64_t>(P.heads) * D;
   const float* Q = static_cast<const float*>(P.q) + head * D;
   const float* G = static_cast<const float*>(P.d_o) + head * D;
@@ -712,11 +713,11 @@ __global__ __launch_bounds__(128) void attn_bwd_dkdv_f32(BwdParams P) {
   __shared__ float ls[QT], dls[QT];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int64_t b = xcd_remap(blockIdx.x, gridDim.x);
-  const int tile = static_cast<int>(b % P.tiles_per_item);
-  const int64_t rest = b / P.tiles_per_item;
-  const int head = static_cast<int>(rest % P.heads);
-  const WorkItem it = P.items[rest / P.heads];
+  GroupCoord gc;
+  if (!group_coord(blockIdx.x, P.tiles_per_item, P.heads, P.n_items, gc)) return;
+  const int tile = gc.tile;
+  const int head = gc.head;
+  const WorkItem it = P.items[gc.item];
   const int64_t rs = static_cast<int64_t>(P.heads) * D;
   const float* Q = static_cast<const float*>(P.q) + head * D;
   const float* G = static_cast<const float*>(P.d_o) + head * D;
@@ -862,6 +863,7 @@ BwdParams bwd_params(const BwdLaunch& a) {
   p.scale_log2 = a.scale * kLog2e;
   p.g0 = nullptr;
   p.g1 = nullptr;
+  p.n_items = 0;
   p.tiles_per_item = 0;
   return p;
 }
@@ -875,9 +877,10 @@ hipError_t launch_bwd_dkdv(const BwdLaunch& a, hipStream_t stream) {
   p.g1 = a.dv_out;
   p.items = a.kitems;
   p.runs = a.kruns;
+  p.n_items = a.n_kitems;
   const int kb = bwd_key_tile(a.dtype);
   p.tiles_per_item = (a.q_len + kb - 1) / kb;
-  const int64_t blocks = int64_t(a.n_kitems) * p.tiles_per_item * a.heads;
+  const int64_t blocks = group_grid(int64_t(a.n_kitems) * a.heads, p.tiles_per_item);
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const dim3 grid(static_cast<unsigned>(blocks));
   if (a.dtype == CQSA_BF16) {
@@ -906,9 +909,10 @@ hipError_t launch_bwd_dq(const BwdLaunch& a, hipStream_t stream) {
   if (a.n_items <= 0 || a.q_len <= 0) return hipSuccess;
   BwdParams p = bwd_params(a);
   p.g0 = a.dq_out;
+  p.n_items = a.n_items;
   const int qb = bwd_query_tile(a.dtype);
   p.tiles_per_item = (a.q_len + qb - 1) / qb;
-  const int64_t blocks = int64_t(a.n_items) * p.tiles_per_item * a.heads;
+  const int64_t blocks = group_grid(int64_t(a.n_items) * a.heads, p.tiles_per_item);
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const dim3 grid(static_cast<unsigned>(blocks));
   if (a.dtype == CQSA_BF16) {

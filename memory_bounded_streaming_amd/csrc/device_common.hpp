@@ -14,13 +14,29 @@ typedef unsigned short u16;
 typedef unsigned int u32;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// Workgroups are dealt round-robin to the 8 XCDs; renumber them so that each XCD
-// receives one contiguous range of tiles (tiles of one query block and head share
-// their K/V stream, which then stays in that XCD's L2).
-__device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t grid) {
-  const int64_t q = grid / 8, r = grid % 8;
-  const int64_t x = b % 8, k = b / 8;
-  return x * q + (x < r ? x : r) + k;
+// Work of one launch: groups (item, head) of `tiles` workgroups each, item-major.
+// Workgroups are dealt round-robin to the 8 XCDs in launch order (block b runs on XCD
+// b % 8).  Group g goes whole to XCD g % 8, as that XCD's (g / 8)-th group, so the
+// tiles of a group share their K/V stream in one L2 and consecutive groups -- items
+// are ordered heaviest first -- are spread over the XCDs, which balances their work.
+// The grid is 8 * tiles * ceil(groups / 8); the few workgroups past the last group
+// return at once.
+inline int64_t group_grid(int64_t groups, int tiles) { return 8 * int64_t(tiles) * ((groups + 7) / 8); }
+
+struct GroupCoord {
+  int64_t item;
+  int head;
+  int tile;
+};
+
+__device__ __forceinline__ bool group_coord(int64_t b, int tiles, int heads, int64_t n_items, GroupCoord& c) {
+  const int64_t i = b >> 3;
+  const int64_t g = ((i / tiles) << 3) + (b & 7);
+  if (g >= n_items * heads) return false;
+  c.tile = static_cast<int>(i % tiles);
+  c.head = static_cast<int>(g % heads);
+  c.item = g / heads;
+  return true;
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }

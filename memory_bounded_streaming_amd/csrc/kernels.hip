@@ -32,6 +32,7 @@ struct AttnParams {
   float* ml_out;
   const WorkItem* items;
   const KeyRun* runs;
+  int64_t n_items;
   int tiles_per_item;
   int heads;
   float scale_log2;
@@ -90,11 +91,11 @@ __global__ __launch_bounds__(512) void attn_partial_bf16(AttnParams P) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, col = lane & 31;
-  const int64_t b = xcd_remap(blockIdx.x, gridDim.x);
-  const int tile = static_cast<int>(b % P.tiles_per_item);
-  const int64_t rest = b / P.tiles_per_item;
-  const int head = static_cast<int>(rest % P.heads);
-  const WorkItem it = P.items[rest / P.heads];
+  GroupCoord gc;
+  if (!group_coord(blockIdx.x, P.tiles_per_item, P.heads, P.n_items, gc)) return;
+  const int tile = gc.tile;
+  const int head = gc.head;
+  const WorkItem it = P.items[gc.item];
   const KeyRun* runs = P.runs + it.run0;
   const int nrun = it.nrun;
   const int64_t rs = static_cast<int64_t>(P.heads) * D;
@@ -291,11 +292,11 @@ __global__ __launch_bounds__(64) void attn_partial_f32(AttnParams P) {
   __shared__ __attribute__((aligned(16))) float kf[KT * D];
   __shared__ __attribute__((aligned(16))) float vf[KT * D];
   const int lane = threadIdx.x;
-  const int64_t b = xcd_remap(blockIdx.x, gridDim.x);
-  const int tile = static_cast<int>(b % P.tiles_per_item);
-  const int64_t rest = b / P.tiles_per_item;
-  const int head = static_cast<int>(rest % P.heads);
-  const WorkItem it = P.items[rest / P.heads];
+  GroupCoord gc;
+  if (!group_coord(blockIdx.x, P.tiles_per_item, P.heads, P.n_items, gc)) return;
+  const int tile = gc.tile;
+  const int head = gc.head;
+  const WorkItem it = P.items[gc.item];
   const int64_t rs = static_cast<int64_t>(P.heads) * D;
   const float* __restrict__ Q = static_cast<const float*>(P.q);
   const float* __restrict__ K = static_cast<const float*>(P.k);
@@ -454,7 +455,8 @@ hipError_t launch_attn(const AttnLaunch& a, hipStream_t stream) {
   p.scale_log2 = a.scale_log2;
   const int qt = attn_query_tile(a.dtype);
   p.tiles_per_item = (a.q_len + qt - 1) / qt;
-  const int64_t blocks = int64_t(a.n_items) * p.tiles_per_item * a.heads;
+  p.n_items = a.n_items;
+  const int64_t blocks = group_grid(int64_t(a.n_items) * a.heads, p.tiles_per_item);
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const dim3 grid(static_cast<unsigned>(blocks));
   if (a.dtype == CQSA_BF16) {
