@@ -41,9 +41,12 @@ def log(msg):
 
 
 def kernel_source_hash():
-    path = os.path.join(ROOT, "memory_bounded_streaming_amd", "csrc", "kernels.hip")
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256 (first 16 hex) of the partial kernel's sources: kernels.hip then device_common.hpp."""
+    h = hashlib.sha256()
+    for name in ("kernels.hip", "device_common.hpp"):
+        with open(os.path.join(ROOT, "memory_bounded_streaming_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel_hash, units_per_launch):
