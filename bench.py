@@ -235,6 +235,7 @@ def run_streamed(args, torch, cqsa):
             "attn_ms": st["t_attn_ms"],
             "bytes_h2d": st["bytes_h2d"],
             "bytes_d2h": st["bytes_d2h"],
+            "bytes_d2d_chunk_reuse": st["bytes_d2d"],
             "peak_device_bytes": st["peak_device_bytes"],
             "budget_bytes": budget,
         }
@@ -285,6 +286,21 @@ def main():
         log("bench: host-pinned streamed workload")
         stream_res = run_streamed(args, torch, cqsa)
         log(f"bench: streamed {stream_res['tflops_pcie_inclusive']:.1f} TFLOP/s PCIe-inclusive")
+    dry = None
+    if stream_res is not None:
+        # the billion-token case priced with this run's measured rates (plan-only, no data)
+        rates = {"attn_tflops": dres["attn_tflops"], "merge_gbs": dres["merge_gbs"],
+                 "h2d_gbs": stream_res["h2d_achievable_gbs"], "d2h_gbs": stream_res["d2h_achievable_gbs"]}
+        dry = []
+        for budget in (16 * GiB, 2 * GiB):
+            e = cqsa.cqsa_plan_estimate(1 << 30, 1, 128, cqsa.CQSA_BF16, [3], n_levels=0, budget_bytes=budget,
+                                        flags=cqsa.CQSA_FLAG_PAD, rates=rates)
+            dry.append({"n_tokens": 1 << 30, "heads": 1, "head_dim": 128, "budget_bytes": budget,
+                        "levels": e["l"], "task_tokens": e["task_tokens"],
+                        "mode": cqsa.MODE_NAMES[e["stream_mode"]], "stream_workspace_bytes": e["stream_workspace_bytes"],
+                        "host_pinned_bytes": e["host_pinned_bytes"], "bytes_h2d": e["bytes_h2d"],
+                        "bytes_d2h": e["bytes_d2h"], "est_hours": round(e["t_est_s"] / 3600, 2),
+                        "attn_hours": round(e["t_attn_s"] / 3600, 2), "h2d_hours": round(e["t_h2d_s"] / 3600, 2)})
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: oracle cpu baseline")
@@ -327,6 +343,7 @@ def main():
                   "avg_launch_ms": round(dres["merge_ms"], 4)},
         "streamed": stream_res,
         "backward": bwd,
+        "dry_run_1b_tokens": dry,
         "cpu_baseline": cpu,
         "kernel_source_sha256_16": khash,
     }

@@ -106,6 +106,7 @@ typedef struct {
   int64_t peak_device_bytes;    /* workspace bytes used by the call */
   int64_t n_attn_launches, n_merge_launches, n_h2d_copies, n_d2h_copies;
   double useful_flop;
+  int64_t bytes_d2d;            /* K/V rows reused from the previous task's staging buffer */
 } cqsa_stats;
 
 /* Measured rates a dry run prices a plan with (all > 0). */
@@ -131,7 +132,10 @@ typedef struct {
   int64_t stream_workspace_bytes; /* device bytes of that mode (excluding descriptor tables) */
   int64_t per_task_descriptor_bytes; /* upper bound of one task's work items + key runs */
   int64_t host_pinned_bytes;    /* Q, K, V, O, LSE in pinned memory + the host accumulator */
-  int64_t bytes_h2d, bytes_d2h; /* exactly what the stream engine copies (LSE included) */
+  int64_t bytes_h2d, bytes_d2h; /* what the stream engine copies (LSE included); exact for
+                                   plans without padding, else bytes_h2d is a lower bound
+                                   and bytes_h2d + bytes_d2d is exact */
+  int64_t bytes_d2d;            /* K/V rows of shared chunks copied device to device */
   int64_t merge_bytes;          /* HBM bytes of all merge launches */
   double useful_flop;           /* 4 N^2 d H */
   double t_attn_s, t_merge_s, t_h2d_s, t_d2h_s;

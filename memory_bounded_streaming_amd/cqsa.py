@@ -62,6 +62,7 @@ class Stats(ctypes.Structure):
         ("bytes_h2d", ctypes.c_int64), ("bytes_d2h", ctypes.c_int64), ("peak_device_bytes", ctypes.c_int64),
         ("n_attn_launches", ctypes.c_int64), ("n_merge_launches", ctypes.c_int64),
         ("n_h2d_copies", ctypes.c_int64), ("n_d2h_copies", ctypes.c_int64), ("useful_flop", ctypes.c_double),
+        ("bytes_d2d", ctypes.c_int64),
     ]
 
 
@@ -79,6 +80,7 @@ class Estimate(ctypes.Structure):
         ("task_tokens", ctypes.c_int64), ("stream_mode", ctypes.c_int32), ("kv_buffers", ctypes.c_int32),
         ("stream_workspace_bytes", ctypes.c_int64), ("per_task_descriptor_bytes", ctypes.c_int64),
         ("host_pinned_bytes", ctypes.c_int64), ("bytes_h2d", ctypes.c_int64), ("bytes_d2h", ctypes.c_int64),
+        ("bytes_d2d", ctypes.c_int64),
         ("merge_bytes", ctypes.c_int64), ("useful_flop", ctypes.c_double),
         ("t_attn_s", ctypes.c_double), ("t_merge_s", ctypes.c_double), ("t_h2d_s", ctypes.c_double),
         ("t_d2h_s", ctypes.c_double), ("t_est_s", ctypes.c_double), ("materializable", ctypes.c_int32),

@@ -363,7 +363,7 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
   PhaseTimer tm;
   tm.on = stats != nullptr;
   hipEvent_t tev;
-  int64_t bytes_h2d = 0, bytes_d2h = 0, n_attn = 0, n_merge = 0, n_h2d = 0, n_d2h = 0;
+  int64_t bytes_h2d = 0, bytes_d2h = 0, bytes_d2d = 0, n_attn = 0, n_merge = 0, n_h2d = 0, n_d2h = 0;
   const int64_t tu = p.task_units;
   const float c2 = scale_log2(p);
   const int64_t e = p.elem_bytes();
@@ -388,13 +388,47 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
     }
     if (static_cast<int64_t>(ti) >= fp.kv_buffers) HIP_TRY(hipStreamWaitEvent(s_kv, kv_free[b], 0));
     HIP_TRY(tm.begin(PH_H2D, s_kv, tev));
+    // Chunk reuse: consecutive tasks of one outer task share exactly one inner chunk
+    // (a perfect difference set meets its own shift in one residue).  With two staging
+    // buffers the previous task's copy of it is still resident, so those rows are copied
+    // on the device; every other row comes from the host.  Token lists are in ascending
+    // global order, so one sweep over both segment lists finds the shared rows.  The
+    // copies stay ordered on the K/V stream: the previous buffer is refilled only after.
+    const Task* prev = nullptr;
+    if (fp.kv_buffers == 2 && ti > 0 &&
+        std::equal(task.ids.begin(), task.ids.end() - 1, p.tasks[ti - 1].ids.begin()))
+      prev = &p.tasks[ti - 1];
+    size_t ps = 0;
     for (const Segment& g : task.segments) {
-      HIP_TRY(hipMemcpyAsync(kst[b] + g.local_offset * row_in, k + g.global_start * row_in, g.length * row_in,
-                             hipMemcpyHostToDevice, s_kv));
-      HIP_TRY(hipMemcpyAsync(vst[b] + g.local_offset * row_in, v + g.global_start * row_in, g.length * row_in,
-                             hipMemcpyHostToDevice, s_kv));
-      bytes_h2d += 2 * g.length * row_in;
-      n_h2d += 2;
+      int64_t pos = g.global_start;
+      const int64_t end = g.global_start + g.length;
+      while (pos < end) {
+        while (prev && ps < prev->segments.size() &&
+               prev->segments[ps].global_start + prev->segments[ps].length <= pos)
+          ++ps;
+        const Segment* hit = nullptr;
+        int64_t stop = end;
+        if (prev && ps < prev->segments.size()) {
+          const Segment& s = prev->segments[ps];
+          if (s.global_start <= pos)
+            hit = &s, stop = std::min(end, s.global_start + s.length);
+          else
+            stop = std::min(end, s.global_start);
+        }
+        const int64_t rows = stop - pos, dst = (g.local_offset + pos - g.global_start) * row_in;
+        if (hit != nullptr) {
+          const int64_t src = (hit->local_offset + pos - hit->global_start) * row_in;
+          HIP_TRY(hipMemcpyAsync(kst[b] + dst, kst[b ^ 1] + src, rows * row_in, hipMemcpyDeviceToDevice, s_kv));
+          HIP_TRY(hipMemcpyAsync(vst[b] + dst, vst[b ^ 1] + src, rows * row_in, hipMemcpyDeviceToDevice, s_kv));
+          bytes_d2d += 2 * rows * row_in;
+        } else {
+          HIP_TRY(hipMemcpyAsync(kst[b] + dst, k + pos * row_in, rows * row_in, hipMemcpyHostToDevice, s_kv));
+          HIP_TRY(hipMemcpyAsync(vst[b] + dst, v + pos * row_in, rows * row_in, hipMemcpyHostToDevice, s_kv));
+          bytes_h2d += 2 * rows * row_in;
+          n_h2d += 2;
+        }
+        pos = stop;
+      }
     }
     HIP_TRY(tm.end(PH_H2D, s_kv));
     HIP_TRY(hipEventRecord(kv_ready[b], s_kv));
@@ -542,6 +576,7 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
     stats->t_d2h_ms = tm.total(PH_D2H);
     stats->bytes_h2d = bytes_h2d;
     stats->bytes_d2h = bytes_d2h;
+    stats->bytes_d2d = bytes_d2d;
     stats->peak_device_bytes = L.total + tabs.bytes;
     stats->n_attn_launches = n_attn;
     stats->n_merge_launches = n_merge;

@@ -576,6 +576,13 @@ cqsa_status estimate_plan(int64_t n, int heads, int d, cqsa_dtype dtype, const i
   const bool host_acc = !fp.acc_on_device;
   out.host_pinned_bytes = 4 * p.n * row_in + p.n * heads * 4 + (host_acc ? p.n * rowp : 0);
   out.bytes_h2d = 3 * p.visits * p.n * row_in + (host_acc ? (p.visits - 1) * p.n * rowp : 0);
+  if (fp.kv_buffers == 2 && !p.cs.empty()) {
+    // K/V reuse between consecutive tasks of one outer task: one inner chunk each
+    const int64_t c_in = p.cs.back(), l_in = p.ls.back();
+    const int64_t transitions = p.n_units / c_in * (c_in - 1);
+    out.bytes_d2d = c_in > 1 ? transitions * (p.task_tokens() / l_in) * row_in * 2 : 0;
+    out.bytes_h2d -= out.bytes_d2d;
+  }
   out.bytes_d2h = p.n * heads * int64_t(d) * p.elem_bytes() + p.n * heads * 4 +
                   (host_acc ? (p.visits - 1) * p.n * rowp : 0);
   // merge launches: a non-first visit reads accumulator + partial and writes the

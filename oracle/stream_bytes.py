@@ -16,6 +16,9 @@ reading R12):
   later visit reads the accumulator and the partial and writes the accumulator, or
   O and LSE at the last visit.  A first visit of several writes its partial straight
   into the accumulator (no merge).
+* chunk reuse (two K/V staging buffers): a task that follows a task of the same outer
+  task copies the K/V rows both hold from the previous staging buffer instead of the
+  host (device to device).
 """
 from __future__ import annotations
 
@@ -24,19 +27,27 @@ from .plan import Plan
 __all__ = ["stream_traffic"]
 
 
-def stream_traffic(plan: Plan, heads: int, d: int, elem_bytes: int, host_acc: bool) -> dict:
+def stream_traffic(plan: Plan, heads: int, d: int, elem_bytes: int, host_acc: bool, kv_buffers: int = 1) -> dict:
     row = heads * d * elem_bytes          # one token of Q, K, V or O
     part = heads * (d + 2) * 4            # one token's (n, m, l) statistics, fp32
     fin = heads * (d * elem_bytes + 4)    # one token's O and LSE
     visits = 1
     for l in plan.ls:
         visits *= l
-    h2d = d2h = merge = 0
+    h2d = d2h = merge = d2d = 0
     seen: dict[int, int] = {}
     u = plan.unit_tokens
+    prev = None
     for task in plan.tasks:
-        for _, length, _ in task.segments(u, plan.n):
-            h2d += 2 * length * row
+        tokens = set()
+        for g, length, _ in task.segments(u, plan.n):
+            tokens.update(range(g, g + length))
+        shared = 0
+        if kv_buffers == 2 and prev is not None and prev[0] == task.ids[:-1]:
+            shared = len(tokens & prev[1])
+        d2d += 2 * shared * row
+        h2d += 2 * (len(tokens) - shared) * row
+        prev = (task.ids[:-1], tokens)
         for p in task.units:
             r = max(0, min(u, plan.n - p * u))
             if r == 0:
@@ -55,4 +66,4 @@ def stream_traffic(plan: Plan, heads: int, d: int, elem_bytes: int, host_acc: bo
                 merge += r * (part + fin)
             elif not first:
                 merge += r * (2 * part + (fin if last else part))
-    return {"bytes_h2d": h2d, "bytes_d2h": d2h, "merge_bytes": merge}
+    return {"bytes_h2d": h2d, "bytes_d2h": d2h, "merge_bytes": merge, "bytes_d2d": d2d}

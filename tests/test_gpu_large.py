@@ -58,13 +58,13 @@ def test_streamed_workload_sampled_rows(name):
     assert abs(free1 - free0) < (256 << 20)
     e = 2
     visits = info["visits"]
-    assert st["bytes_h2d"] >= 3 * visits * n * h * d * e
+    assert st["bytes_h2d"] + st["bytes_d2d"] >= 3 * visits * n * h * d * e
     # the dry run predicts the copies exactly; its time uses this run's measured rates
     rates = {"attn_tflops": info["useful_flop"] / (st["t_attn_ms"] / 1e3) / 1e12,
              "merge_gbs": 5000.0, "h2d_gbs": st["bytes_h2d"] / (st["t_h2d_ms"] / 1e3) / 1e9,
              "d2h_gbs": st["bytes_d2h"] / (st["t_d2h_ms"] / 1e3) / 1e9}
     est = cqsa.cqsa_plan_estimate(n, h, d, cqsa.CQSA_BF16, levels, budget_bytes=budget, rates=rates)
-    assert est["bytes_h2d"] == st["bytes_h2d"] and est["bytes_d2h"] == st["bytes_d2h"]
+    assert (est["bytes_h2d"], est["bytes_d2h"], est["bytes_d2d"]) == (st["bytes_h2d"], st["bytes_d2h"], st["bytes_d2d"])
     log(f"  dry run: {est['t_est_s']:.2f} s estimated vs {wall:.2f} s measured")
     rows = sample_rows(n, r_count, 0, unit_tokens=info["unit_tokens"])
     log(f"  oracle on {rows.size} rows")

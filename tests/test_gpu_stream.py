@@ -57,10 +57,11 @@ def test_stream_modes_equal_device_path(case, flags):
         assert st["peak_device_bytes"] >= p.info["stream_workspace_bytes"]
         e = 2 if dtype == "bf16" else 4
         visits = int(np.prod(levels))
-        assert st["bytes_h2d"] >= 3 * visits * n * h * d * e
+        assert st["bytes_h2d"] + st["bytes_d2d"] >= 3 * visits * n * h * d * e
         est = cqsa.cqsa_plan_estimate(n, h, d, DT[dtype], levels, flags=flags,
                                       rates={"attn_tflops": 1.0, "merge_gbs": 1.0, "h2d_gbs": 1.0, "d2h_gbs": 1.0})
-        assert (est["bytes_h2d"], est["bytes_d2h"]) == (st["bytes_h2d"], st["bytes_d2h"]), "dry run bytes exact"
+        assert (est["bytes_h2d"], est["bytes_d2h"], est["bytes_d2d"]) == (st["bytes_h2d"], st["bytes_d2h"], st["bytes_d2d"]), \
+            "dry run bytes exact"
         assert np.array_equal(oa, o_dev), "streamed output equals the device-resident output bit for bit"
         assert np.array_equal(tl.numpy(), lse_dev)
     o_ref, _ = attention_fp64(q, k, v, dtype=dtype)
