@@ -14,14 +14,27 @@ typedef unsigned short u16;
 typedef unsigned int u32;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// Work of one launch: groups (item, head) of `tiles` workgroups each, item-major.
-// Workgroups are dealt round-robin to the 8 XCDs in launch order (block b runs on XCD
-// b % 8).  Group g goes whole to XCD g % 8, as that XCD's (g / 8)-th group, so the
-// tiles of a group share their K/V stream in one L2 and consecutive groups -- items
-// are ordered heaviest first -- are spread over the XCDs, which balances their work.
-// The grid is 8 * tiles * ceil(groups / 8); the few workgroups past the last group
-// return at once.
-inline int64_t group_grid(int64_t groups, int tiles) { return 8 * int64_t(tiles) * ((groups + 7) / 8); }
+// Work of one launch: (item, head) groups of `tiles` workgroups each, item-major, cut
+// into equal chunks of at most kChunk tiles (one round of an XCD's 32 CUs).  Workgroups
+// are dealt round-robin to the 8 XCDs in launch order (block b runs on XCD b % 8).
+// Chunk g goes whole to XCD g % 8, as that XCD's (g / 8)-th chunk: the tiles of a chunk
+// share their K/V stream in one L2, and consecutive chunks -- of one large group, or of
+// consecutive groups, whose items are ordered heaviest first -- are spread over the
+// XCDs, which balances their work.  The grid is 8 * chunk_tiles * ceil(chunks / 8); the
+// workgroups past the last chunk, or past the last tile of a shorter final chunk of a
+// group, return at once.
+constexpr int kChunk = 32;
+
+__host__ __device__ inline int chunks_per_group(int tiles) { return (tiles + kChunk - 1) / kChunk; }
+__host__ __device__ inline int chunk_tiles(int tiles) {
+  const int per = chunks_per_group(tiles);
+  return (tiles + per - 1) / per;
+}
+
+inline int64_t group_grid(int64_t groups, int tiles) {
+  const int64_t chunks = groups * chunks_per_group(tiles);
+  return 8 * int64_t(chunk_tiles(tiles)) * ((chunks + 7) / 8);
+}
 
 struct GroupCoord {
   int64_t item;
@@ -30,12 +43,16 @@ struct GroupCoord {
 };
 
 __device__ __forceinline__ bool group_coord(int64_t b, int tiles, int heads, int64_t n_items, GroupCoord& c) {
+  const int per_group = chunks_per_group(tiles), ct = chunk_tiles(tiles);
   const int64_t i = b >> 3;
-  const int64_t g = ((i / tiles) << 3) + (b & 7);
-  if (g >= n_items * heads) return false;
-  c.tile = static_cast<int>(i % tiles);
-  c.head = static_cast<int>(g % heads);
-  c.item = g / heads;
+  const int64_t g = ((i / ct) << 3) + (b & 7);  // chunk index
+  if (g >= n_items * heads * per_group) return false;
+  const int tile = static_cast<int>(g % per_group) * ct + static_cast<int>(i % ct);
+  if (tile >= tiles) return false;
+  const int64_t gh = g / per_group;
+  c.tile = tile;
+  c.head = static_cast<int>(gh % heads);
+  c.item = gh / heads;
   return true;
 }
 
