@@ -260,10 +260,14 @@ cqsa_status cqsa_forward(const cqsa_plan* plan, const void* q, const void* k, co
                          int64_t workspace_bytes, void* stream, cqsa_stats* stats);
 
 /*
- * Device workspace bytes cqsa_backward needs for res (CQSA_RES_DEVICE only): Delta
- * [H][N] fp32, for bf16 three transposed copies (Q, K, dO) [H][d][round_up(N, 64)], and
- * the visit slots of dQ, dK, dV [V][N][H][d] fp32 (V = prod(l_k)).
- * Errors: EINVAL (NULL, or a residency the backward does not run on).
+ * Device workspace bytes cqsa_backward needs for res.  CQSA_RES_DEVICE: Delta [H][N]
+ * fp32, for bf16 three transposed copies (Q, K, dO) [H][d][round_up(N, 64)], and the
+ * visit slots of dQ, dK, dV [V][N][H][d] fp32 (V = prod(l_k)).  CQSA_RES_HOST_PINNED:
+ * L and Delta [H][N]; one task's Q, K, V, dO and their transposes; the task's L and
+ * Delta rows; a two-slot ring of unit blocks (terms, output, and host-accumulator
+ * blocks); fp32 accumulators [N][H][d] for dQ, dK, dV when they fit the plan's budget
+ * (else they live in pinned host memory and are not counted).
+ * Errors: EINVAL (NULL or unknown residency), EBUDGET (no streamed layout fits).
  */
 cqsa_status cqsa_backward_workspace_size(const cqsa_plan* plan, cqsa_residency res, int64_t* bytes);
 
@@ -277,12 +281,19 @@ cqsa_status cqsa_backward_workspace_size(const cqsa_plan* plan, cqsa_residency r
  * and the CQS Mask gives each pair to exactly one task, so each task's terms go to
  * the rows' visit slots and the slots are summed in ascending task order
  * (deterministic; no rescaling across tasks).
- *   q, k, v, o, d_o: device [N, H, d] in the plan's dtype (read only); o and lse are
- *     the forward's outputs (lse: device float32 [H, N], natural log).
- *   dq, dk, dv: device [N, H, d] in the plan's dtype (written; round to nearest even).
- *   res: CQSA_RES_DEVICE (CQSA_RES_HOST_PINNED is rejected with EINVAL).
- *   workspace: device buffer >= cqsa_backward_workspace_size bytes, or NULL (the
- *     library allocates and frees it).  Stream-ordered like cqsa_forward.
+ *   q, k, v, o, d_o: [N, H, d] in the plan's dtype (read only); o and lse are the
+ *     forward's outputs (lse: float32 [H, N], natural log).
+ *   dq, dk, dv: [N, H, d] in the plan's dtype (written; round to nearest even).
+ *   res: CQSA_RES_DEVICE (device pointers; stream-ordered like cqsa_forward) or
+ *     CQSA_RES_HOST_PINNED (pinned host pointers; synchronous): Delta of every row is
+ *     formed first from O and dO streamed in unit blocks; then per task in ascending id
+ *     its Q, K, V, dO rows are staged and transposed on the device, its L and Delta
+ *     rows gathered, and for each of its units the dQ and dK/dV terms are added into
+ *     the unit's accumulators (device, or pinned host memory with round trips) in the
+ *     device path's order, so both residencies give the same bits.  Device memory used
+ *     is the workspace (<= the plan's budget).  Not built for causal plans (EINVAL).
+ *   workspace: device buffer >= cqsa_backward_workspace_size(res) bytes, or NULL (the
+ *     library allocates and frees it).
  *   stats: optional; t_attn_ms = the two gradient kernels, t_merge_ms = the Delta /
  *     transpose pass and the slot sums, useful_flop = 10 N^2 d H.
  * Errors: EINVAL, ESMALL, EBUDGET (workspace over the plan's budget), EHIP, ENOMEM.

@@ -222,7 +222,12 @@ cqsa_status cqsa_forward(const cqsa_plan* plan, const void* q, const void* k, co
 cqsa_status cqsa_backward_workspace_size(const cqsa_plan* plan, cqsa_residency res, int64_t* bytes) {
   return guarded([&]() -> cqsa_status {
     if (plan == nullptr || bytes == nullptr) return fail(CQSA_EINVAL, "NULL argument");
-    if (res != CQSA_RES_DEVICE) return fail(CQSA_EINVAL, "the backward pass runs on device-resident tensors only");
+    if (res == CQSA_RES_HOST_PINNED) {
+      if (plan->p.bwd_stream_fp.bytes < 0) return fail(CQSA_EBUDGET, "no streamed backward layout fits the budget");
+      *bytes = plan->p.bwd_stream_fp.bytes;
+      return ok();
+    }
+    if (res != CQSA_RES_DEVICE) return fail(CQSA_EINVAL, "unknown residency");
     *bytes = plan->p.bwd_device_ws;
     return ok();
   });

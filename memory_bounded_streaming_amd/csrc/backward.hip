@@ -72,11 +72,11 @@ struct PrepParams {
   const void* k;
   const void* o;
   const void* d_o;
-  float* delta;
-  u16* qt;
+  float* delta;         // [H][dpitch], or null: no Delta
+  u16* qt;              // null: no transposed copies
   u16* kt;
   u16* dot;
-  int64_t n, np;
+  int64_t n, np, dpitch;
   int heads;
 };
 
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(256) void bwd_prep(PrepParams P) {
   const int64_t tok0 = static_cast<int64_t>(blockIdx.x) * TOK;
   const int64_t rs = static_cast<int64_t>(P.heads) * D;
   // Delta: 4 threads per token, D/4 elements each
-  {
+  if (P.delta != nullptr) {
     const int t = tid >> 2, part = tid & 3;
     const int64_t row = tok0 + t;
     float acc = 0.f;
@@ -115,9 +115,10 @@ __global__ __launch_bounds__(256) void bwd_prep(PrepParams P) {
     }
     acc += __shfl_xor(acc, 1);
     acc += __shfl_xor(acc, 2);
-    if (part == 0 && row < P.n) P.delta[head * P.n + row] = acc;
+    if (part == 0 && row < P.n) P.delta[head * P.dpitch + row] = acc;
   }
   if constexpr (sizeof(T) == 2) {
+    if (P.qt == nullptr) return;
     const u16* srcs[3] = {static_cast<const u16*>(P.q), static_cast<const u16*>(P.k), static_cast<const u16*>(P.d_o)};
     u16* dsts[3] = {P.qt, P.kt, P.dot};
     constexpr int DCH = D / 8;
@@ -800,7 +801,46 @@ __global__ __launch_bounds__(256) void sum_slots(const float* __restrict__ in, i
   }
 }
 
+// ---------------------------------------------------------------------------------
+// Accumulation of one visit's gradient terms (stream engine): a = term on a row's first
+// visit, else a = acc + term -- the order of the device path's slot sum; the result goes
+// back to acc, or, at the last visit, to out in the output dtype.
+// ---------------------------------------------------------------------------------
+template <typename OutT>
+__global__ __launch_bounds__(256) void accumulate_terms(float* __restrict__ acc, const float* __restrict__ term,
+                                                        int64_t count4, int first, OutT* __restrict__ out) {
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < count4;
+       e += static_cast<int64_t>(gridDim.x) * 256) {
+    float4 a = *reinterpret_cast<const float4*>(term + 4 * e);
+    if (!first) {
+      const float4 c = *reinterpret_cast<const float4*>(acc + 4 * e);
+      a = make_float4(c.x + a.x, c.y + a.y, c.z + a.z, c.w + a.w);
+    }
+    if (out != nullptr)
+      store_out(out + 4 * e, a);
+    else
+      *reinterpret_cast<float4*>(acc + 4 * e) = a;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_accumulate(const AccLaunch& a, hipStream_t stream) {
+  if (a.count <= 0) return hipSuccess;
+  if (a.count % 4 != 0) return hipErrorInvalidValue;
+  const int64_t count4 = a.count / 4;
+  const dim3 grid(static_cast<unsigned>(std::min<int64_t>((count4 + 255) / 256, 65536)));
+  if (a.out == nullptr)
+    hipLaunchKernelGGL((accumulate_terms<float>), grid, dim3(256), 0, stream, a.acc, a.term, count4, a.first ? 1 : 0,
+                       static_cast<float*>(nullptr));
+  else if (a.dtype == CQSA_BF16)
+    hipLaunchKernelGGL((accumulate_terms<u16>), grid, dim3(256), 0, stream, a.acc, a.term, count4, a.first ? 1 : 0,
+                       static_cast<u16*>(a.out));
+  else
+    hipLaunchKernelGGL((accumulate_terms<float>), grid, dim3(256), 0, stream, a.acc, a.term, count4, a.first ? 1 : 0,
+                       static_cast<float*>(a.out));
+  return hipGetLastError();
+}
 
 int bwd_key_tile(cqsa_dtype dtype) { return dtype == CQSA_BF16 ? BwdKTile<128>::KB : 64; }
 int bwd_query_tile(cqsa_dtype dtype) { return dtype == CQSA_BF16 ? BwdQTile<128>::QB : 64; }
@@ -818,10 +858,11 @@ hipError_t launch_bwd_prep(const PrepLaunch& a, hipStream_t stream) {
   p.dot = static_cast<u16*>(a.dot);
   p.n = a.n;
   p.np = a.np;
+  p.dpitch = a.dpitch > 0 ? a.dpitch : a.n;
   p.heads = a.heads;
   const int64_t tiles = (a.n + 63) / 64;
   if (tiles > 0x7FFFFFFF || a.heads > 65535) return hipErrorInvalidConfiguration;
-  if (a.dtype == CQSA_BF16 && (a.np < tiles * 64 || (a.np & 7) != 0)) return hipErrorInvalidValue;
+  if (a.dtype == CQSA_BF16 && a.qt != nullptr && (a.np < tiles * 64 || (a.np & 7) != 0)) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(a.heads));
   if (a.dtype == CQSA_BF16) {
     if (a.d == 128)

@@ -96,18 +96,21 @@ cqsa_status device_tables(const Plan& p, DeviceTables& out, std::string& why) {
   const int64_t b3 = align_up(int64_t(p.stream_runs.size()) * sizeof(KeyRun));
   const int64_t b4 = align_up(int64_t(p.dev_kitems.size()) * sizeof(WorkItem));
   const int64_t b5 = align_up(int64_t(p.dev_kruns.size()) * sizeof(KeyRun));
+  const int64_t b6 = align_up(int64_t(p.bstream_items.size()) * sizeof(WorkItem));
   std::lock_guard<std::mutex> lock(p.dev_mu);
   char* base = nullptr;
   for (auto& e : p.dev_tables)
     if (e.first == dev) base = static_cast<char*>(e.second);
   if (base == nullptr) {
-    std::vector<char> host(b0 + b1 + b2 + b3 + b4 + b5, 0);
+    std::vector<char> host(b0 + b1 + b2 + b3 + b4 + b5 + b6, 0);
     std::memcpy(host.data(), p.dev_items.data(), p.dev_items.size() * sizeof(WorkItem));
     std::memcpy(host.data() + b0, p.dev_runs.data(), p.dev_runs.size() * sizeof(KeyRun));
     std::memcpy(host.data() + b0 + b1, p.stream_items.data(), p.stream_items.size() * sizeof(WorkItem));
     std::memcpy(host.data() + b0 + b1 + b2, p.stream_runs.data(), p.stream_runs.size() * sizeof(KeyRun));
     std::memcpy(host.data() + b0 + b1 + b2 + b3, p.dev_kitems.data(), p.dev_kitems.size() * sizeof(WorkItem));
     std::memcpy(host.data() + b0 + b1 + b2 + b3 + b4, p.dev_kruns.data(), p.dev_kruns.size() * sizeof(KeyRun));
+    std::memcpy(host.data() + b0 + b1 + b2 + b3 + b4 + b5, p.bstream_items.data(),
+                p.bstream_items.size() * sizeof(WorkItem));
     void* mem = nullptr;
     HIP_TRY(hipMalloc(&mem, host.size()));
     hipError_t e = hipMemcpy(mem, host.data(), host.size(), hipMemcpyHostToDevice);
@@ -125,7 +128,8 @@ cqsa_status device_tables(const Plan& p, DeviceTables& out, std::string& why) {
   out.stream_runs = reinterpret_cast<const KeyRun*>(base + b0 + b1 + b2);
   out.dev_kitems = reinterpret_cast<const WorkItem*>(base + b0 + b1 + b2 + b3);
   out.dev_kruns = reinterpret_cast<const KeyRun*>(base + b0 + b1 + b2 + b3 + b4);
-  out.bytes = b0 + b1 + b2 + b3 + b4 + b5;
+  out.bstream_items = reinterpret_cast<const WorkItem*>(base + b0 + b1 + b2 + b3 + b4 + b5);
+  out.bytes = b0 + b1 + b2 + b3 + b4 + b5 + b6;
   return CQSA_OK;
 }
 
@@ -590,6 +594,315 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
 
 }  // namespace
 
+
+// ----------------------------------------------------------------------------------
+// backward, host-pinned: Delta of every row first (O and dO streamed through in unit
+// blocks), then per task in ascending id: stage Q, K, V, dO of the task's tokens,
+// transpose them on the device, gather the task's L and Delta rows, and for each of its
+// units run the dQ and dK/dV kernels into a unit block of terms and add the terms into
+// the unit's accumulators (device, or pinned host memory with H2D/D2H round trips).  A
+// row's first visit stores its terms and later visits add to them -- the order of the
+// device path's slot sum -- and its last visit writes the gradient in the input dtype.
+// The task staging is single-buffered; unit blocks go through a two-slot ring.
+// ----------------------------------------------------------------------------------
+namespace {
+
+struct BwdStreamRes {
+  hipStream_t s[2] = {nullptr, nullptr};  // h2d, d2h
+  hipStream_t caller = nullptr;
+  std::vector<hipEvent_t> events;
+  void* ws = nullptr;
+  bool own_ws = false;
+  float* host_acc = nullptr;
+  ~BwdStreamRes() {
+    (void)hipStreamSynchronize(caller);
+    for (hipStream_t x : s)
+      if (x) (void)hipStreamSynchronize(x);
+    for (hipEvent_t e : events) (void)hipEventDestroy(e);
+    for (hipStream_t x : s)
+      if (x) (void)hipStreamDestroy(x);
+    if (own_ws && ws) (void)hipFree(ws);
+    if (host_acc) (void)hipHostFree(host_acc);
+  }
+  hipError_t event(hipEvent_t& e) {
+    hipError_t r = hipEventCreateWithFlags(&e, hipEventDisableTiming);
+    if (r == hipSuccess) events.push_back(e);
+    return r;
+  }
+};
+
+cqsa_status backward_stream(const Plan& p, const char* q, const char* k, const char* v, const char* o,
+                            const float* lse, const char* d_o, char* dq, char* dk, char* dv, void* ws,
+                            int64_t ws_bytes, hipStream_t caller, cqsa_stats* stats, std::string& why) {
+  if (p.flags & CQSA_FLAG_CAUSAL) {
+    why = "the host-pinned backward of a causal plan is not built (the device-resident one is)";
+    return CQSA_EINVAL;
+  }
+  if (p.bwd_stream_fp.bytes < 0) {
+    why = "no streamed backward layout fits the budget of " + std::to_string(p.budget) + " bytes";
+    return CQSA_EBUDGET;
+  }
+  const auto t0 = std::chrono::steady_clock::now();
+  const bool dev_acc = p.bwd_stream_fp.acc_on_device;
+  const BwdStreamLayout L = bwd_stream_layout(p, dev_acc);
+  DeviceTables tabs{};
+  cqsa_status st = device_tables(p, tabs, why);
+  if (st != CQSA_OK) return st;
+  BwdStreamRes R;
+  R.caller = caller;
+  if (ws == nullptr) {
+    HIP_TRY(hipMalloc(&R.ws, L.total));
+    R.own_ws = true;
+  } else {
+    if (ws_bytes < L.total) {
+      why = "workspace of " + std::to_string(ws_bytes) + " bytes, need " + std::to_string(L.total);
+      return CQSA_ESMALL;
+    }
+    R.ws = ws;
+  }
+  char* cur = static_cast<char*>(R.ws);
+  auto take = [&](int64_t bytes) {
+    char* r = cur;
+    cur += bytes;
+    return r;
+  };
+  const int64_t H = p.heads, D = p.d, U = p.unit, N = p.n, T = p.task_tokens(), e = p.elem_bytes();
+  const int64_t row_in = p.row_in_bytes(), hd = H * D;
+  float* lse_d = reinterpret_cast<float*>(take(L.lse));
+  float* delta_d = reinterpret_cast<float*>(take(L.delta));
+  char* stg[4];  // Q, K, V, dO of the task
+  for (auto& x : stg) x = take(L.stage);
+  char* trs[3] = {nullptr, nullptr, nullptr};  // Q^T, K^T, dO^T
+  if (L.trans)
+    for (auto& x : trs) x = take(L.trans);
+  float* ls_t = reinterpret_cast<float*>(take(L.tstat));
+  float* ds_t = reinterpret_cast<float*>(take(L.tstat));
+  struct Slot {
+    float* term[3];
+    float* temp[3];
+    char* out[3];
+  } slot[2];
+  for (auto& s : slot) {
+    for (int g = 0; g < 3; ++g) s.term[g] = reinterpret_cast<float*>(take(L.term));
+    for (int g = 0; g < 3; ++g) s.temp[g] = L.temp ? reinterpret_cast<float*>(take(L.temp)) : nullptr;
+    for (int g = 0; g < 3; ++g) s.out[g] = take(L.out);
+  }
+  float* acc[3] = {nullptr, nullptr, nullptr};
+  if (dev_acc)
+    for (auto& x : acc) x = reinterpret_cast<float*>(take(L.acc));
+  float* host_acc[3] = {nullptr, nullptr, nullptr};
+  if (!dev_acc) {
+    HIP_TRY(hipHostMalloc(reinterpret_cast<void**>(&R.host_acc), 3 * N * hd * sizeof(float), hipHostMallocDefault));
+    for (int g = 0; g < 3; ++g) host_acc[g] = R.host_acc + g * N * hd;
+  }
+  char* outs[3] = {dq, dk, dv};
+
+  for (auto& s : R.s) HIP_TRY(hipStreamCreateWithFlags(&s, hipStreamNonBlocking));
+  hipStream_t s_h = R.s[0], s_d = R.s[1], s_c = caller;
+  hipEvent_t start, staged, stage_free, acc_ready[2], c_done[2], slot_free[2];
+  HIP_TRY(R.event(start));
+  HIP_TRY(R.event(staged));
+  HIP_TRY(R.event(stage_free));
+  for (int i = 0; i < 2; ++i) {
+    HIP_TRY(R.event(acc_ready[i]));
+    HIP_TRY(R.event(c_done[i]));
+    HIP_TRY(R.event(slot_free[i]));
+  }
+  HIP_TRY(hipEventRecord(start, caller));
+  for (hipStream_t s : R.s) HIP_TRY(hipStreamWaitEvent(s, start, 0));
+  PhaseTimer tm;
+  tm.on = stats != nullptr;
+  hipEvent_t tev;
+  int64_t bytes_h2d = 0, bytes_d2h = 0, n_attn = 0, n_merge = 0, n_h2d = 0, n_d2h = 0;
+
+  // phase 0: LSE to the device, Delta of every row from O and dO in unit blocks
+  HIP_TRY(tm.begin(PH_H2D, s_h, tev));
+  HIP_TRY(hipMemcpyAsync(lse_d, lse, H * N * sizeof(float), hipMemcpyHostToDevice, s_h));
+  HIP_TRY(tm.end(PH_H2D, s_h));
+  bytes_h2d += H * N * 4;
+  ++n_h2d;
+  for (int64_t r0 = 0; r0 < N; r0 += U) {
+    const int64_t rows = std::min(U, N - r0);
+    if (r0 > 0) HIP_TRY(hipStreamWaitEvent(s_h, stage_free, 0));
+    HIP_TRY(tm.begin(PH_H2D, s_h, tev));
+    HIP_TRY(hipMemcpyAsync(stg[0], o + r0 * row_in, rows * row_in, hipMemcpyHostToDevice, s_h));
+    HIP_TRY(hipMemcpyAsync(stg[3], d_o + r0 * row_in, rows * row_in, hipMemcpyHostToDevice, s_h));
+    HIP_TRY(tm.end(PH_H2D, s_h));
+    bytes_h2d += 2 * rows * row_in;
+    n_h2d += 2;
+    HIP_TRY(hipEventRecord(staged, s_h));
+    HIP_TRY(hipStreamWaitEvent(s_c, staged, 0));
+    PrepLaunch pr{};
+    pr.dtype = p.dtype;
+    pr.d = p.d;
+    pr.heads = p.heads;
+    pr.n = rows;
+    pr.o = stg[0];
+    pr.d_o = stg[3];
+    pr.delta = delta_d + r0;
+    pr.dpitch = N;
+    HIP_TRY(tm.begin(PH_MERGE, s_c, tev));
+    HIP_TRY(launch_bwd_prep(pr, s_c));
+    HIP_TRY(tm.end(PH_MERGE, s_c));
+    HIP_TRY(hipEventRecord(stage_free, s_c));
+  }
+
+  const int64_t tu = p.task_units;
+  const float scale = static_cast<float>(1.0 / std::sqrt(double(p.d)));
+  std::vector<int64_t> last_block(p.n_units, -4);
+  int64_t blk = 0;
+  for (size_t ti = 0; ti < p.tasks.size(); ++ti) {
+    const Task& task = p.tasks[ti];
+    // stage the task (single buffer: after the previous task's kernels)
+    HIP_TRY(hipStreamWaitEvent(s_h, stage_free, 0));
+    HIP_TRY(tm.begin(PH_H2D, s_h, tev));
+    const char* srcs[4] = {q, k, v, d_o};
+    for (const Segment& g : task.segments)
+      for (int x = 0; x < 4; ++x) {
+        HIP_TRY(hipMemcpyAsync(stg[x] + g.local_offset * row_in, srcs[x] + g.global_start * row_in, g.length * row_in,
+                               hipMemcpyHostToDevice, s_h));
+        bytes_h2d += g.length * row_in;
+        ++n_h2d;
+      }
+    HIP_TRY(tm.end(PH_H2D, s_h));
+    HIP_TRY(hipEventRecord(staged, s_h));
+    HIP_TRY(hipStreamWaitEvent(s_c, staged, 0));
+    // the task's L and Delta rows, [H][T]
+    HIP_TRY(tm.begin(PH_MERGE, s_c, tev));
+    for (const Segment& g : task.segments) {
+      HIP_TRY(hipMemcpy2DAsync(ls_t + g.local_offset, T * 4, lse_d + g.global_start, N * 4, g.length * 4, H,
+                               hipMemcpyDeviceToDevice, s_c));
+      HIP_TRY(hipMemcpy2DAsync(ds_t + g.local_offset, T * 4, delta_d + g.global_start, N * 4, g.length * 4, H,
+                               hipMemcpyDeviceToDevice, s_c));
+    }
+    if (L.trans) {
+      PrepLaunch pr{};
+      pr.dtype = p.dtype;
+      pr.d = p.d;
+      pr.heads = p.heads;
+      pr.n = T;
+      pr.np = L.tnp;
+      pr.q = stg[0];
+      pr.k = stg[1];
+      pr.d_o = stg[3];
+      pr.qt = trs[0];
+      pr.kt = trs[1];
+      pr.dot = trs[2];
+      HIP_TRY(launch_bwd_prep(pr, s_c));
+    }
+    HIP_TRY(tm.end(PH_MERGE, s_c));
+
+    for (int64_t a = 0; a < tu; ++a, ++blk) {
+      const int j = static_cast<int>(blk % 2);
+      Slot& S = slot[j];
+      const int64_t pu = task.units[a];
+      const int64_t rows = p.unit_rows(pu);
+      if (rows == 0) continue;
+      const int visit = task.slot[a];
+      const bool first = visit == 0, last = visit == p.visits - 1;
+      if (blk >= 2) HIP_TRY(hipStreamWaitEvent(s_c, slot_free[j], 0));
+      if (!dev_acc && !first) {
+        // the unit's accumulator blocks back from host memory
+        if (blk >= 2) HIP_TRY(hipStreamWaitEvent(s_h, slot_free[j], 0));
+        if (last_block[pu] == blk - 1) HIP_TRY(hipStreamWaitEvent(s_h, slot_free[(blk - 1) % 2], 0));
+        HIP_TRY(tm.begin(PH_H2D, s_h, tev));
+        for (int g = 0; g < 3; ++g)
+          HIP_TRY(hipMemcpyAsync(S.temp[g], host_acc[g] + pu * U * hd, rows * hd * 4, hipMemcpyHostToDevice, s_h));
+        HIP_TRY(tm.end(PH_H2D, s_h));
+        bytes_h2d += 3 * rows * hd * 4;
+        n_h2d += 3;
+        HIP_TRY(hipEventRecord(acc_ready[j], s_h));
+        HIP_TRY(hipStreamWaitEvent(s_c, acc_ready[j], 0));
+      }
+      BwdLaunch b{};
+      b.dtype = p.dtype;
+      b.d = p.d;
+      b.heads = p.heads;
+      b.n = T;
+      b.np = L.tnp;
+      b.q = stg[0];
+      b.k = stg[1];
+      b.v = stg[2];
+      b.d_o = stg[3];
+      b.qt = trs[0];
+      b.kt = trs[1];
+      b.dot = trs[2];
+      b.lse = ls_t;
+      b.delta = ds_t;
+      b.dq_out = S.term[0];
+      b.dk_out = S.term[1];
+      b.dv_out = S.term[2];
+      b.items = tabs.bstream_items + (int64_t(ti) * tu + a);
+      b.runs = tabs.stream_runs;
+      b.n_items = 1;
+      b.kitems = b.items;
+      b.kruns = b.runs;
+      b.n_kitems = 1;
+      b.causal = false;
+      b.q_len = static_cast<int>(U);
+      b.scale = scale;
+      HIP_TRY(tm.begin(PH_ATTN, s_c, tev));
+      HIP_TRY(launch_bwd_dq(b, s_c));
+      HIP_TRY(launch_bwd_dkdv(b, s_c));
+      HIP_TRY(tm.end(PH_ATTN, s_c));
+      n_attn += 2;
+      HIP_TRY(tm.begin(PH_MERGE, s_c, tev));
+      for (int g = 0; g < 3; ++g) {
+        AccLaunch ac{};
+        ac.dtype = p.dtype;
+        ac.acc = dev_acc ? acc[g] + pu * U * hd : S.temp[g];
+        ac.term = S.term[g];
+        ac.count = rows * hd;
+        ac.first = first;
+        ac.out = last ? S.out[g] : nullptr;
+        HIP_TRY(launch_accumulate(ac, s_c));
+        ++n_merge;
+      }
+      HIP_TRY(tm.end(PH_MERGE, s_c));
+      HIP_TRY(hipEventRecord(c_done[j], s_c));
+      HIP_TRY(hipStreamWaitEvent(s_d, c_done[j], 0));
+      HIP_TRY(tm.begin(PH_D2H, s_d, tev));
+      for (int g = 0; g < 3; ++g) {
+        if (last) {
+          HIP_TRY(hipMemcpyAsync(outs[g] + pu * U * hd * e, S.out[g], rows * hd * e, hipMemcpyDeviceToHost, s_d));
+          bytes_d2h += rows * hd * e;
+          ++n_d2h;
+        } else if (!dev_acc) {
+          HIP_TRY(hipMemcpyAsync(host_acc[g] + pu * U * hd, S.temp[g], rows * hd * 4, hipMemcpyDeviceToHost, s_d));
+          bytes_d2h += rows * hd * 4;
+          ++n_d2h;
+        }
+      }
+      if (!dev_acc && !last) last_block[pu] = blk;
+      HIP_TRY(tm.end(PH_D2H, s_d));
+      HIP_TRY(hipEventRecord(slot_free[j], s_d));
+    }
+    HIP_TRY(hipEventRecord(stage_free, s_c));
+  }
+  HIP_TRY(hipStreamSynchronize(s_c));
+  for (hipStream_t s : R.s) HIP_TRY(hipStreamSynchronize(s));
+  HIP_TRY(hipGetLastError());
+  if (stats) {
+    std::memset(stats, 0, sizeof(*stats));
+    stats->t_h2d_ms = tm.total(PH_H2D);
+    stats->t_attn_ms = tm.total(PH_ATTN);
+    stats->t_merge_ms = tm.total(PH_MERGE);
+    stats->t_d2h_ms = tm.total(PH_D2H);
+    stats->bytes_h2d = bytes_h2d;
+    stats->bytes_d2h = bytes_d2h;
+    stats->peak_device_bytes = L.total + tabs.bytes;
+    stats->n_attn_launches = n_attn;
+    stats->n_merge_launches = n_merge;
+    stats->n_h2d_copies = n_h2d;
+    stats->n_d2h_copies = n_d2h;
+    stats->useful_flop = 2.5 * p.useful_flop();
+    stats->t_total_ms = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+  }
+  return CQSA_OK;
+}
+
+}  // namespace
+
 // ----------------------------------------------------------------------------------
 // backward, device-resident: prep (Delta, transposed copies), dK/dV terms and dQ terms
 // of every (task, unit) into visit slots, then one slot sum per gradient
@@ -597,8 +910,12 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
 cqsa_status run_backward(const Plan& p, const void* q, const void* k, const void* v, const void* o,
                          const float* lse, const void* d_o, void* dq, void* dk, void* dv, cqsa_residency res,
                          void* ws, int64_t ws_bytes, hipStream_t stream, cqsa_stats* stats, std::string& why) {
+  if (res == CQSA_RES_HOST_PINNED)
+    return backward_stream(p, static_cast<const char*>(q), static_cast<const char*>(k), static_cast<const char*>(v),
+                           static_cast<const char*>(o), lse, static_cast<const char*>(d_o), static_cast<char*>(dq),
+                           static_cast<char*>(dk), static_cast<char*>(dv), ws, ws_bytes, stream, stats, why);
   if (res != CQSA_RES_DEVICE) {
-    why = "the backward pass runs on device-resident tensors only";
+    why = "unknown residency";
     return CQSA_EINVAL;
   }
   if (p.budget > 0 && p.bwd_device_ws > p.budget) {

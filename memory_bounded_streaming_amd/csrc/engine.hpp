@@ -17,6 +17,7 @@ struct DeviceTables {
   const KeyRun* stream_runs;
   const WorkItem* dev_kitems;  // causal dK/dV tables (empty without causality)
   const KeyRun* dev_kruns;
+  const WorkItem* bstream_items;  // streamed backward items (rows in the task staging)
   int64_t bytes;
 };
 

@@ -63,10 +63,11 @@ struct PrepLaunch {
   const void* k;
   const void* o;
   const void* d_o;
-  float* delta;        // [H][n]
-  void* qt;            // bf16 only
+  float* delta;        // [H][dpitch] (dpitch 0: n), or null: no Delta
+  void* qt;            // bf16 only; null: no transposed copies
   void* kt;
   void* dot;
+  int64_t dpitch;
 };
 
 // Gradient terms of the pairs the items admit, written to visit slots
@@ -110,7 +111,18 @@ struct SumLaunch {
   void* out;
 };
 
+// acc = term (first) or acc + term; written to acc, or to out (dtype) when out != null.
+struct AccLaunch {
+  cqsa_dtype dtype;
+  float* acc;
+  const float* term;
+  int64_t count;       // floats (a multiple of 4)
+  bool first;
+  void* out;
+};
+
 int bwd_key_tile(cqsa_dtype dtype);
+hipError_t launch_accumulate(const AccLaunch& a, hipStream_t stream);
 int bwd_query_tile(cqsa_dtype dtype);
 hipError_t launch_bwd_prep(const PrepLaunch& a, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdLaunch& a, hipStream_t stream);

@@ -96,6 +96,23 @@ BwdLayout bwd_layout(const Plan& p) {
   return b;
 }
 
+BwdStreamLayout bwd_stream_layout(const Plan& p, bool acc_on_device) {
+  BwdStreamLayout b{};
+  const int64_t h = p.heads, d = p.d, e = p.elem_bytes(), T = p.task_tokens(), U = p.unit;
+  b.tnp = (T + 63) / 64 * 64;
+  b.lse = align_up(h * p.n * 4);
+  b.delta = b.lse;
+  b.stage = align_up(T * h * d * e);
+  b.trans = p.dtype == CQSA_BF16 ? align_up(h * d * b.tnp * 2) : 0;
+  b.tstat = align_up(h * T * 4);
+  b.term = align_up(U * h * d * 4);
+  b.temp = acc_on_device ? 0 : b.term;
+  b.out = align_up(U * h * d * e);
+  b.acc = acc_on_device ? align_up(p.n * h * d * 4) : 0;
+  b.total = b.lse + b.delta + 4 * b.stage + 3 * b.trans + 2 * b.tstat + 2 * 3 * (b.term + b.temp + b.out) + 3 * b.acc;
+  return b;
+}
+
 namespace {
 
 // Every innermost task with its units, per-level chunk of each local unit, admitted
@@ -231,6 +248,7 @@ bool admitted_pair(const Plan& p, const Task& t, int64_t a, int64_t b) {
 // identical key tiles and give identical bits.
 void build_descriptors(Plan& p) {
   const bool causal = (p.flags & CQSA_FLAG_CAUSAL) != 0;
+  p.bstream_items.clear();
   p.dev_items.clear();
   p.dev_runs.clear();
   p.stream_items.clear();
@@ -266,6 +284,9 @@ void build_descriptors(Plan& p) {
       di.keys = si.keys = static_cast<int32_t>(std::min<int64_t>(keys, INT32_MAX));
       if (di.q_len > 0) p.dev_items.push_back(di);  // a unit of padding only has no rows
       p.stream_items.push_back(si);                 // indexed by (task, unit): kept, engine skips it
+      WorkItem bi = si;
+      bi.q_row0 = static_cast<int64_t>(a) * p.unit;
+      p.bstream_items.push_back(bi);
     }
   }
   // heaviest query blocks first in the one-launch device path (load balance only)
@@ -314,6 +335,7 @@ int64_t descriptor_bytes(const Plan& p) {
          align_up(int64_t(p.dev_runs.size()) * sizeof(KeyRun)) +
          align_up(int64_t(p.dev_kitems.size()) * sizeof(WorkItem)) +
          align_up(int64_t(p.dev_kruns.size()) * sizeof(KeyRun)) +
+         align_up(int64_t(p.bstream_items.size()) * sizeof(WorkItem)) +
          align_up(int64_t(p.stream_items.size()) * sizeof(WorkItem)) +
          align_up(int64_t(p.stream_runs.size()) * sizeof(KeyRun));
 }
@@ -411,6 +433,16 @@ cqsa_status build_fixed(int64_t n, int heads, int d, cqsa_dtype dtype, const std
   p.device_ws = align_up(p.visits * p.n * heads * int64_t(d) * 4) + align_up(p.visits * p.n * heads * int64_t(2) * 4);
   p.bwd_np = (n + 63) / 64 * 64;
   p.bwd_device_ws = bwd_layout(p).total;
+  // streamed backward: device accumulators if they fit the budget, else host ones
+  p.bwd_stream_fp = {false, 1, -1};
+  for (const bool dev : {true, false}) {
+    if ((flags & CQSA_FLAG_HOST_ACC) && dev) continue;
+    const int64_t bytes = bwd_stream_layout(p, dev).total;
+    if (budget == 0 || bytes + descriptor_bytes(p) <= budget) {
+      p.bwd_stream_fp = {dev, 1, bytes};
+      break;
+    }
+  }
   return choose_mode(p, why);
 }
 

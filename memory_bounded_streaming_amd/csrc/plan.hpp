@@ -70,11 +70,15 @@ struct Plan {
   // after the key unit (without causality the mask is symmetric: dev_items serve)
   std::vector<WorkItem> dev_kitems;
   std::vector<KeyRun> dev_kruns;
+  // streamed backward: item (t, a) at index t*task_units + a, rows in the task's staging
+  // (q_row0 = a * unit), outputs in a unit block (out_row0 = 0); runs are stream_runs
+  std::vector<WorkItem> bstream_items;
 
   Footprint stream_fp{};
   int64_t device_ws = 0;                // slots bytes of the device-resident path
   int64_t bwd_np = 0;                   // row pitch (tokens) of the backward's transposed copies
   int64_t bwd_device_ws = 0;            // workspace bytes of the device-resident backward
+  Footprint bwd_stream_fp{};            // streamed backward mode (bytes < 0: none fits the budget)
   int64_t host_acc_bytes = 0;
 
   // device copies of the descriptor tables, uploaded lazily per device
@@ -103,6 +107,21 @@ struct BwdLayout {
   int64_t total;        // delta + 3 trans + 3 slots
 };
 BwdLayout bwd_layout(const Plan& p);
+
+// Byte size of each piece of the streamed backward's workspace, in carve order.
+struct BwdStreamLayout {
+  int64_t lse, delta;     // [H][N] fp32 each, resident for the call
+  int64_t stage;          // one staged tensor of a task (Q, K, V or dO): task_tokens rows
+  int64_t trans;          // one transposed staged tensor [H][d][tnp] bf16 (0 for fp32)
+  int64_t tstat;          // the task's L or Delta rows [H][task_tokens] fp32
+  int64_t term;           // one gradient's terms of a unit [U][H][d] fp32 (per ring slot)
+  int64_t temp;           // host accumulator block [U][H][d] fp32 (per ring slot; 0 on device)
+  int64_t out;            // one output block [U][H][d] dtype (per ring slot)
+  int64_t acc;            // one device accumulator [N][H][d] fp32 (0 with the host one)
+  int64_t tnp;            // row pitch of the transposed staging (tokens)
+  int64_t total;
+};
+BwdStreamLayout bwd_stream_layout(const Plan& p, bool acc_on_device);
 
 // Byte size of each piece of the streamed path's workspace, in the order it is carved.
 struct StreamLayout {

@@ -147,5 +147,64 @@ def test_backward_errors():
             p.backward(t[0], t[1], t[2], t[3], lse, t[4], t[5], t[6], t[7], workspace=small)
         assert e.value.status == -7
         with pytest.raises(cqsa.CqsaError) as e:
+            p.backward(t[0], t[1], t[2], t[3], lse, t[4], t[5], t[6], t[7], residency=7)
+        assert e.value.status == -1
+
+
+STREAM_CASES = [  # levels, N, heads, head_dim, dtype, flags
+    ([3], 7 * 300, 2, 128, "bf16", 0),
+    ([3], 7 * 300, 2, 128, "bf16", cqsa.CQSA_FLAG_HOST_ACC),
+    ([4], 13 * 100 + 9, 1, 64, "bf16", cqsa.CQSA_FLAG_PAD),
+    ([2, 2], 9 * 40, 2, 128, "bf16", cqsa.CQSA_FLAG_HOST_ACC),
+    ([3, 2], 21 * 16, 1, 64, "bf16", 0),
+    ([3], 7 * 64, 1, 64, "f32", cqsa.CQSA_FLAG_HOST_ACC),
+    ([2, 3], 21 * 9 + 2, 1, 128, "f32", cqsa.CQSA_FLAG_PAD),
+]
+
+
+@pytest.mark.parametrize("case", STREAM_CASES,
+                         ids=lambda c: f"l{'x'.join(map(str, c[0]))}-n{c[1]}-h{c[2]}-d{c[3]}-{c[4]}-f{c[5]}")
+def test_streamed_backward_equals_device_backward(case):
+    """Host-pinned backward (tasks staged through the device under the plan's layout) gives
+    the device-resident backward's gradients bit for bit."""
+    from gpu_util import pinned
+    torch = pytest.importorskip("torch")
+    levels, n, h, d, dtype, flags = case
+    log(f"streamed backward {case}")
+    q, k, v = gen_qkv(151 + n, n, h, d, dtype)
+    do = gen_tensor(151 + n, 3, n, h, d, dtype)
+    with cqsa.Plan(n, h, d, DT[dtype], levels, flags=flags) as p:
+        qd, kd, vd, dod = (to_device(x, dtype) for x in (q, k, v, do))
+        o = empty_device((n, h, d), dtype)
+        lse = torch.empty((h, n), device="cuda")
+        p.forward(qd, kd, vd, o, lse)
+        want = _run_backward(p, [qd, kd, vd, o, lse, dod], dtype, n, h, d)
+        hosts = []
+        for x in (q, k, v, to_numpy(o, dtype), do):
+            t, a = pinned((n, h, d), dtype)
+            a[...] = x
+            hosts.append(t)
+        lse_h = lse.cpu().pin_memory()
+        outs = [pinned((n, h, d), dtype) for _ in range(3)]
+        st = p.backward(*hosts[:4], lse_h, hosts[4], *(t for t, _ in outs), residency=cqsa.CQSA_RES_HOST_PINNED,
+                        stats=True)
+        assert st["peak_device_bytes"] >= p.backward_workspace_size(cqsa.CQSA_RES_HOST_PINNED)
+        got = [as_f64(a, dtype) for _, a in outs]
+    for name, g, w in zip(("dQ", "dK", "dV"), got, want):
+        assert np.array_equal(g, w), f"{name} differs from the device path"
+
+
+def test_streamed_backward_respects_budget_and_rejects_causal():
+    torch = pytest.importorskip("torch")
+    n, h, d = 13 * 512, 4, 128
+    with cqsa.Plan(n, h, d, cqsa.CQSA_BF16, [4]) as probe:
+        need_dev = probe.backward_workspace_size(cqsa.CQSA_RES_HOST_PINNED)
+    with cqsa.Plan(n, h, d, cqsa.CQSA_BF16, [4], budget_bytes=need_dev // 2) as p:
+        ws = p.backward_workspace_size(cqsa.CQSA_RES_HOST_PINNED)
+        assert ws <= need_dev // 2  # the accumulators moved to pinned host memory
+    with cqsa.Plan(7 * 64, 1, 64, cqsa.CQSA_BF16, [3], flags=cqsa.CQSA_FLAG_CAUSAL) as p:
+        t = [torch.zeros((7 * 64, 1, 64), dtype=torch.int16, pin_memory=True) for _ in range(8)]
+        lse = torch.zeros((1, 7 * 64), pin_memory=True)
+        with pytest.raises(cqsa.CqsaError) as e:
             p.backward(t[0], t[1], t[2], t[3], lse, t[4], t[5], t[6], t[7], residency=cqsa.CQSA_RES_HOST_PINNED)
         assert e.value.status == -1
