@@ -182,6 +182,42 @@ def run_backward(args, torch, cqsa):
     }
 
 
+def run_streamed_backward(args, torch, cqsa):
+    """Backward of the host-pinned N=212992, 16-head workload under 16 GiB: Q, K, V, O, dO
+    and LSE in pinned memory, gradients written to pinned memory (one warm call, one timed)."""
+    from memory_bounded_streaming_amd.inputs import gen_tensor
+    n, h, d, levels, budget, _ = WORKLOADS["c3"]
+    ts = []
+    for i in range(4):  # Q, K, V, dO
+        t = torch.empty((n, h, d), dtype=torch.int16, pin_memory=True)
+        gen_tensor(args.seed, i, n, h, d, "bf16", out=t.numpy().view(np.uint16))
+        ts.append(t)
+    o = torch.empty((n, h, d), dtype=torch.int16, pin_memory=True)
+    lse = torch.empty((h, n), dtype=torch.float32, pin_memory=True)
+    grads = [torch.empty((n, h, d), dtype=torch.int16, pin_memory=True) for _ in range(3)]
+    with cqsa.Plan(n, h, d, cqsa.CQSA_BF16, levels, budget_bytes=budget) as plan:
+        plan.forward(ts[0], ts[1], ts[2], o, lse, residency=cqsa.CQSA_RES_HOST_PINNED)
+        need = plan.backward_workspace_size(cqsa.CQSA_RES_HOST_PINNED)
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        call = (ts[0], ts[1], ts[2], o, lse, ts[3], *grads)
+        plan.backward(*call, residency=cqsa.CQSA_RES_HOST_PINNED, workspace=ws)  # warm-up
+        t0 = time.perf_counter()
+        st = plan.backward(*call, residency=cqsa.CQSA_RES_HOST_PINNED, workspace=ws, stats=True)
+        wall = time.perf_counter() - t0
+        useful = 2.5 * plan.info["useful_flop"]
+    return {
+        "workload": f"backward of N={n}, H={h}, d={d}, bf16, CQS l={levels[0]}, pinned host memory, "
+                    f"device budget {budget // GiB} GiB",
+        "wall_s": wall,
+        "tflops_pcie_inclusive": useful / wall / 1e12,
+        "grad_kernels_tflops_executed": 14.0 / 10.0 * useful / (st["t_attn_ms"] / 1e3) / 1e12,
+        "bytes_h2d": st["bytes_h2d"],
+        "bytes_d2h": st["bytes_d2h"],
+        "peak_device_bytes": st["peak_device_bytes"],
+        "budget_bytes": budget,
+    }
+
+
 def pcie_achievable(torch, nbytes=512 << 20, reps=5):
     """Plain pinned-memory copies of 512 MiB in each direction: the achievable PCIe rate."""
     h = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
@@ -250,6 +286,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-streamed", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-streamed-backward", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one plain device copy of 1 GiB first (reference for HBM traffic counters)")
@@ -286,6 +323,11 @@ def main():
         log("bench: host-pinned streamed workload")
         stream_res = run_streamed(args, torch, cqsa)
         log(f"bench: streamed {stream_res['tflops_pcie_inclusive']:.1f} TFLOP/s PCIe-inclusive")
+    sbwd = None
+    if not args.no_streamed and not args.no_streamed_backward:
+        log("bench: host-pinned streamed backward")
+        sbwd = run_streamed_backward(args, torch, cqsa)
+        log(f"bench: streamed backward {sbwd['tflops_pcie_inclusive']:.1f} useful TFLOP/s PCIe-inclusive")
     dry = None
     if stream_res is not None:
         # the billion-token case priced with this run's measured rates (plan-only, no data)
@@ -343,6 +385,7 @@ def main():
                   "avg_launch_ms": round(dres["merge_ms"], 4)},
         "streamed": stream_res,
         "backward": bwd,
+        "streamed_backward": sbwd,
         "dry_run_1b_tokens": dry,
         "cpu_baseline": cpu,
         "kernel_source_sha256_16": khash,
