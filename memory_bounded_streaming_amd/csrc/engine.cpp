@@ -603,7 +603,8 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
 // the unit's accumulators (device, or pinned host memory with H2D/D2H round trips).  A
 // row's first visit stores its terms and later visits add to them -- the order of the
 // device path's slot sum -- and its last visit writes the gradient in the input dtype.
-// The task staging is single-buffered; unit blocks go through a two-slot ring.
+// The task staging has one or two sets (the next task is staged while this one runs);
+// unit blocks go through a two-slot ring.
 // ----------------------------------------------------------------------------------
 namespace {
 
@@ -644,7 +645,8 @@ cqsa_status backward_stream(const Plan& p, const char* q, const char* k, const c
   }
   const auto t0 = std::chrono::steady_clock::now();
   const bool dev_acc = p.bwd_stream_fp.acc_on_device;
-  const BwdStreamLayout L = bwd_stream_layout(p, dev_acc);
+  const int nset = p.bwd_stream_fp.kv_buffers;
+  const BwdStreamLayout L = bwd_stream_layout(p, dev_acc, nset);
   DeviceTables tabs{};
   cqsa_status st = device_tables(p, tabs, why);
   if (st != CQSA_OK) return st;
@@ -670,13 +672,20 @@ cqsa_status backward_stream(const Plan& p, const char* q, const char* k, const c
   const int64_t row_in = p.row_in_bytes(), hd = H * D;
   float* lse_d = reinterpret_cast<float*>(take(L.lse));
   float* delta_d = reinterpret_cast<float*>(take(L.delta));
-  char* stg[4];  // Q, K, V, dO of the task
-  for (auto& x : stg) x = take(L.stage);
-  char* trs[3] = {nullptr, nullptr, nullptr};  // Q^T, K^T, dO^T
-  if (L.trans)
-    for (auto& x : trs) x = take(L.trans);
-  float* ls_t = reinterpret_cast<float*>(take(L.tstat));
-  float* ds_t = reinterpret_cast<float*>(take(L.tstat));
+  struct Stage {
+    char* t[4];      // Q, K, V, dO of the task
+    char* tr[3];     // Q^T, K^T, dO^T
+    float* ls;       // the task's L rows [H][T]
+    float* ds;       // the task's Delta rows
+  } set[2] = {};
+  for (int b = 0; b < nset; ++b) {
+    Stage& S = set[b];
+    for (auto& x : S.t) x = take(L.stage);
+    for (auto& x : S.tr) x = L.trans ? take(L.trans) : nullptr;
+    S.ls = reinterpret_cast<float*>(take(L.tstat));
+    S.ds = reinterpret_cast<float*>(take(L.tstat));
+  }
+  char** stg = set[0].t;  // phase 0 borrows the first set's Q and dO staging
   struct Slot {
     float* term[3];
     float* temp[3];
@@ -699,11 +708,11 @@ cqsa_status backward_stream(const Plan& p, const char* q, const char* k, const c
 
   for (auto& s : R.s) HIP_TRY(hipStreamCreateWithFlags(&s, hipStreamNonBlocking));
   hipStream_t s_h = R.s[0], s_d = R.s[1], s_c = caller;
-  hipEvent_t start, staged, stage_free, acc_ready[2], c_done[2], slot_free[2];
+  hipEvent_t start, staged, stage_free[2], acc_ready[2], c_done[2], slot_free[2];
   HIP_TRY(R.event(start));
   HIP_TRY(R.event(staged));
-  HIP_TRY(R.event(stage_free));
   for (int i = 0; i < 2; ++i) {
+    HIP_TRY(R.event(stage_free[i]));
     HIP_TRY(R.event(acc_ready[i]));
     HIP_TRY(R.event(c_done[i]));
     HIP_TRY(R.event(slot_free[i]));
@@ -723,7 +732,7 @@ cqsa_status backward_stream(const Plan& p, const char* q, const char* k, const c
   ++n_h2d;
   for (int64_t r0 = 0; r0 < N; r0 += U) {
     const int64_t rows = std::min(U, N - r0);
-    if (r0 > 0) HIP_TRY(hipStreamWaitEvent(s_h, stage_free, 0));
+    if (r0 > 0) HIP_TRY(hipStreamWaitEvent(s_h, stage_free[0], 0));
     HIP_TRY(tm.begin(PH_H2D, s_h, tev));
     HIP_TRY(hipMemcpyAsync(stg[0], o + r0 * row_in, rows * row_in, hipMemcpyHostToDevice, s_h));
     HIP_TRY(hipMemcpyAsync(stg[3], d_o + r0 * row_in, rows * row_in, hipMemcpyHostToDevice, s_h));
@@ -744,7 +753,7 @@ cqsa_status backward_stream(const Plan& p, const char* q, const char* k, const c
     HIP_TRY(tm.begin(PH_MERGE, s_c, tev));
     HIP_TRY(launch_bwd_prep(pr, s_c));
     HIP_TRY(tm.end(PH_MERGE, s_c));
-    HIP_TRY(hipEventRecord(stage_free, s_c));
+    HIP_TRY(hipEventRecord(stage_free[0], s_c));
   }
 
   const int64_t tu = p.task_units;
@@ -753,13 +762,15 @@ cqsa_status backward_stream(const Plan& p, const char* q, const char* k, const c
   int64_t blk = 0;
   for (size_t ti = 0; ti < p.tasks.size(); ++ti) {
     const Task& task = p.tasks[ti];
-    // stage the task (single buffer: after the previous task's kernels)
-    HIP_TRY(hipStreamWaitEvent(s_h, stage_free, 0));
+    // stage the task into its set, once the kernels of the set's previous task are done
+    const int sb = static_cast<int>(ti % nset);
+    Stage& G = set[sb];
+    HIP_TRY(hipStreamWaitEvent(s_h, stage_free[sb], 0));
     HIP_TRY(tm.begin(PH_H2D, s_h, tev));
     const char* srcs[4] = {q, k, v, d_o};
     for (const Segment& g : task.segments)
       for (int x = 0; x < 4; ++x) {
-        HIP_TRY(hipMemcpyAsync(stg[x] + g.local_offset * row_in, srcs[x] + g.global_start * row_in, g.length * row_in,
+        HIP_TRY(hipMemcpyAsync(G.t[x] + g.local_offset * row_in, srcs[x] + g.global_start * row_in, g.length * row_in,
                                hipMemcpyHostToDevice, s_h));
         bytes_h2d += g.length * row_in;
         ++n_h2d;
@@ -770,9 +781,9 @@ cqsa_status backward_stream(const Plan& p, const char* q, const char* k, const c
     // the task's L and Delta rows, [H][T]
     HIP_TRY(tm.begin(PH_MERGE, s_c, tev));
     for (const Segment& g : task.segments) {
-      HIP_TRY(hipMemcpy2DAsync(ls_t + g.local_offset, T * 4, lse_d + g.global_start, N * 4, g.length * 4, H,
+      HIP_TRY(hipMemcpy2DAsync(G.ls + g.local_offset, T * 4, lse_d + g.global_start, N * 4, g.length * 4, H,
                                hipMemcpyDeviceToDevice, s_c));
-      HIP_TRY(hipMemcpy2DAsync(ds_t + g.local_offset, T * 4, delta_d + g.global_start, N * 4, g.length * 4, H,
+      HIP_TRY(hipMemcpy2DAsync(G.ds + g.local_offset, T * 4, delta_d + g.global_start, N * 4, g.length * 4, H,
                                hipMemcpyDeviceToDevice, s_c));
     }
     if (L.trans) {
@@ -782,12 +793,12 @@ cqsa_status backward_stream(const Plan& p, const char* q, const char* k, const c
       pr.heads = p.heads;
       pr.n = T;
       pr.np = L.tnp;
-      pr.q = stg[0];
-      pr.k = stg[1];
-      pr.d_o = stg[3];
-      pr.qt = trs[0];
-      pr.kt = trs[1];
-      pr.dot = trs[2];
+      pr.q = G.t[0];
+      pr.k = G.t[1];
+      pr.d_o = G.t[3];
+      pr.qt = G.tr[0];
+      pr.kt = G.tr[1];
+      pr.dot = G.tr[2];
       HIP_TRY(launch_bwd_prep(pr, s_c));
     }
     HIP_TRY(tm.end(PH_MERGE, s_c));
@@ -820,15 +831,15 @@ cqsa_status backward_stream(const Plan& p, const char* q, const char* k, const c
       b.heads = p.heads;
       b.n = T;
       b.np = L.tnp;
-      b.q = stg[0];
-      b.k = stg[1];
-      b.v = stg[2];
-      b.d_o = stg[3];
-      b.qt = trs[0];
-      b.kt = trs[1];
-      b.dot = trs[2];
-      b.lse = ls_t;
-      b.delta = ds_t;
+      b.q = G.t[0];
+      b.k = G.t[1];
+      b.v = G.t[2];
+      b.d_o = G.t[3];
+      b.qt = G.tr[0];
+      b.kt = G.tr[1];
+      b.dot = G.tr[2];
+      b.lse = G.ls;
+      b.delta = G.ds;
       b.dq_out = S.term[0];
       b.dk_out = S.term[1];
       b.dv_out = S.term[2];
@@ -877,7 +888,7 @@ cqsa_status backward_stream(const Plan& p, const char* q, const char* k, const c
       HIP_TRY(tm.end(PH_D2H, s_d));
       HIP_TRY(hipEventRecord(slot_free[j], s_d));
     }
-    HIP_TRY(hipEventRecord(stage_free, s_c));
+    HIP_TRY(hipEventRecord(stage_free[sb], s_c));
   }
   HIP_TRY(hipStreamSynchronize(s_c));
   for (hipStream_t s : R.s) HIP_TRY(hipStreamSynchronize(s));

@@ -96,8 +96,9 @@ BwdLayout bwd_layout(const Plan& p) {
   return b;
 }
 
-BwdStreamLayout bwd_stream_layout(const Plan& p, bool acc_on_device) {
+BwdStreamLayout bwd_stream_layout(const Plan& p, bool acc_on_device, int stage_sets) {
   BwdStreamLayout b{};
+  b.sets = stage_sets;
   const int64_t h = p.heads, d = p.d, e = p.elem_bytes(), T = p.task_tokens(), U = p.unit;
   b.tnp = (T + 63) / 64 * 64;
   b.lse = align_up(h * p.n * 4);
@@ -109,7 +110,8 @@ BwdStreamLayout bwd_stream_layout(const Plan& p, bool acc_on_device) {
   b.temp = acc_on_device ? 0 : b.term;
   b.out = align_up(U * h * d * e);
   b.acc = acc_on_device ? align_up(p.n * h * d * 4) : 0;
-  b.total = b.lse + b.delta + 4 * b.stage + 3 * b.trans + 2 * b.tstat + 2 * 3 * (b.term + b.temp + b.out) + 3 * b.acc;
+  b.total = b.lse + b.delta + stage_sets * (4 * b.stage + 3 * b.trans + 2 * b.tstat) + 2 * 3 * (b.term + b.temp + b.out) +
+            3 * b.acc;
   return b;
 }
 
@@ -433,13 +435,16 @@ cqsa_status build_fixed(int64_t n, int heads, int d, cqsa_dtype dtype, const std
   p.device_ws = align_up(p.visits * p.n * heads * int64_t(d) * 4) + align_up(p.visits * p.n * heads * int64_t(2) * 4);
   p.bwd_np = (n + 63) / 64 * 64;
   p.bwd_device_ws = bwd_layout(p).total;
-  // streamed backward: device accumulators if they fit the budget, else host ones
+  // streamed backward: the forward's mode order (device accumulators and two staging
+  // sets first), restricted by the same flags
   p.bwd_stream_fp = {false, 1, -1};
-  for (const bool dev : {true, false}) {
-    if ((flags & CQSA_FLAG_HOST_ACC) && dev) continue;
-    const int64_t bytes = bwd_stream_layout(p, dev).total;
+  const std::pair<bool, int> bwd_order[4] = {{true, 2}, {false, 2}, {true, 1}, {false, 1}};
+  for (const auto& m : bwd_order) {
+    if ((flags & CQSA_FLAG_HOST_ACC) && m.first) continue;
+    if ((flags & CQSA_FLAG_KV_SINGLE) && m.second != 1) continue;
+    const int64_t bytes = bwd_stream_layout(p, m.first, m.second).total;
     if (budget == 0 || bytes + descriptor_bytes(p) <= budget) {
-      p.bwd_stream_fp = {dev, 1, bytes};
+      p.bwd_stream_fp = {m.first, m.second, bytes};
       break;
     }
   }

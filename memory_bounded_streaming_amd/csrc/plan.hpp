@@ -119,9 +119,10 @@ struct BwdStreamLayout {
   int64_t out;            // one output block [U][H][d] dtype (per ring slot)
   int64_t acc;            // one device accumulator [N][H][d] fp32 (0 with the host one)
   int64_t tnp;            // row pitch of the transposed staging (tokens)
+  int sets;               // task staging sets (2: the next task is staged during this one)
   int64_t total;
 };
-BwdStreamLayout bwd_stream_layout(const Plan& p, bool acc_on_device);
+BwdStreamLayout bwd_stream_layout(const Plan& p, bool acc_on_device, int stage_sets);
 
 // Byte size of each piece of the streamed path's workspace, in the order it is carved.
 struct StreamLayout {

@@ -237,7 +237,7 @@ def test_backward_workspace_size_and_argument_errors(lib):
         t = 3 * 100
         tnp = -(-t // 64) * 64
         ring = 2 * 3 * (al(100 * h * d * 4) + al(100 * h * d * 2))
-        want_s = 2 * al(h * n * 4) + 4 * al(t * h * d * 2) + 3 * al(h * d * tnp * 2) + 2 * al(h * t * 4) + ring \
+        want_s = 2 * al(h * n * 4) + 2 * (4 * al(t * h * d * 2) + 3 * al(h * d * tnp * 2) + 2 * al(h * t * 4)) + ring \
             + 3 * al(n * h * d * 4)
         assert p.backward_workspace_size(cqsa.CQSA_RES_HOST_PINNED) == want_s
     with cqsa.Plan(n, h, d, cqsa.CQSA_F32, [3]) as p:

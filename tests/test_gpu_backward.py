@@ -159,6 +159,8 @@ STREAM_CASES = [  # levels, N, heads, head_dim, dtype, flags
     ([3, 2], 21 * 16, 1, 64, "bf16", 0),
     ([3], 7 * 64, 1, 64, "f32", cqsa.CQSA_FLAG_HOST_ACC),
     ([2, 3], 21 * 9 + 2, 1, 128, "f32", cqsa.CQSA_FLAG_PAD),
+    ([3], 7 * 300, 2, 128, "bf16", cqsa.CQSA_FLAG_KV_SINGLE),  # one task staging set
+    ([4], 13 * 64, 2, 64, "bf16", cqsa.CQSA_FLAG_KV_SINGLE | cqsa.CQSA_FLAG_HOST_ACC),
 ]
 
 
