@@ -291,7 +291,7 @@ cqsa_status cqsa_backward_workspace_size(const cqsa_plan* plan, cqsa_residency r
  *     rows gathered, and for each of its units the dQ and dK/dV terms are added into
  *     the unit's accumulators (device, or pinned host memory with round trips) in the
  *     device path's order, so both residencies give the same bits.  Device memory used
- *     is the workspace (<= the plan's budget).  Not built for causal plans (EINVAL).
+ *     is the workspace (<= the plan's budget).
  *   workspace: device buffer >= cqsa_backward_workspace_size(res) bytes, or NULL (the
  *     library allocates and frees it).
  *   stats: optional; t_attn_ms = the two gradient kernels, t_merge_ms = the Delta /

@@ -97,12 +97,14 @@ cqsa_status device_tables(const Plan& p, DeviceTables& out, std::string& why) {
   const int64_t b4 = align_up(int64_t(p.dev_kitems.size()) * sizeof(WorkItem));
   const int64_t b5 = align_up(int64_t(p.dev_kruns.size()) * sizeof(KeyRun));
   const int64_t b6 = align_up(int64_t(p.bstream_items.size()) * sizeof(WorkItem));
+  const int64_t b7 = align_up(int64_t(p.bstream_kitems.size()) * sizeof(WorkItem));
+  const int64_t b8 = align_up(int64_t(p.bstream_kruns.size()) * sizeof(KeyRun));
   std::lock_guard<std::mutex> lock(p.dev_mu);
   char* base = nullptr;
   for (auto& e : p.dev_tables)
     if (e.first == dev) base = static_cast<char*>(e.second);
   if (base == nullptr) {
-    std::vector<char> host(b0 + b1 + b2 + b3 + b4 + b5 + b6, 0);
+    std::vector<char> host(b0 + b1 + b2 + b3 + b4 + b5 + b6 + b7 + b8, 0);
     std::memcpy(host.data(), p.dev_items.data(), p.dev_items.size() * sizeof(WorkItem));
     std::memcpy(host.data() + b0, p.dev_runs.data(), p.dev_runs.size() * sizeof(KeyRun));
     std::memcpy(host.data() + b0 + b1, p.stream_items.data(), p.stream_items.size() * sizeof(WorkItem));
@@ -111,6 +113,10 @@ cqsa_status device_tables(const Plan& p, DeviceTables& out, std::string& why) {
     std::memcpy(host.data() + b0 + b1 + b2 + b3 + b4, p.dev_kruns.data(), p.dev_kruns.size() * sizeof(KeyRun));
     std::memcpy(host.data() + b0 + b1 + b2 + b3 + b4 + b5, p.bstream_items.data(),
                 p.bstream_items.size() * sizeof(WorkItem));
+    std::memcpy(host.data() + b0 + b1 + b2 + b3 + b4 + b5 + b6, p.bstream_kitems.data(),
+                p.bstream_kitems.size() * sizeof(WorkItem));
+    std::memcpy(host.data() + b0 + b1 + b2 + b3 + b4 + b5 + b6 + b7, p.bstream_kruns.data(),
+                p.bstream_kruns.size() * sizeof(KeyRun));
     void* mem = nullptr;
     HIP_TRY(hipMalloc(&mem, host.size()));
     hipError_t e = hipMemcpy(mem, host.data(), host.size(), hipMemcpyHostToDevice);
@@ -129,7 +135,9 @@ cqsa_status device_tables(const Plan& p, DeviceTables& out, std::string& why) {
   out.dev_kitems = reinterpret_cast<const WorkItem*>(base + b0 + b1 + b2 + b3);
   out.dev_kruns = reinterpret_cast<const KeyRun*>(base + b0 + b1 + b2 + b3 + b4);
   out.bstream_items = reinterpret_cast<const WorkItem*>(base + b0 + b1 + b2 + b3 + b4 + b5);
-  out.bytes = b0 + b1 + b2 + b3 + b4 + b5 + b6;
+  out.bstream_kitems = reinterpret_cast<const WorkItem*>(base + b0 + b1 + b2 + b3 + b4 + b5 + b6);
+  out.bstream_kruns = reinterpret_cast<const KeyRun*>(base + b0 + b1 + b2 + b3 + b4 + b5 + b6 + b7);
+  out.bytes = b0 + b1 + b2 + b3 + b4 + b5 + b6 + b7 + b8;
   return CQSA_OK;
 }
 
@@ -635,10 +643,7 @@ struct BwdStreamRes {
 cqsa_status backward_stream(const Plan& p, const char* q, const char* k, const char* v, const char* o,
                             const float* lse, const char* d_o, char* dq, char* dk, char* dv, void* ws,
                             int64_t ws_bytes, hipStream_t caller, cqsa_stats* stats, std::string& why) {
-  if (p.flags & CQSA_FLAG_CAUSAL) {
-    why = "the host-pinned backward of a causal plan is not built (the device-resident one is)";
-    return CQSA_EINVAL;
-  }
+  const bool causal = (p.flags & CQSA_FLAG_CAUSAL) != 0;
   if (p.bwd_stream_fp.bytes < 0) {
     why = "no streamed backward layout fits the budget of " + std::to_string(p.budget) + " bytes";
     return CQSA_EBUDGET;
@@ -846,10 +851,10 @@ cqsa_status backward_stream(const Plan& p, const char* q, const char* k, const c
       b.items = tabs.bstream_items + (int64_t(ti) * tu + a);
       b.runs = tabs.stream_runs;
       b.n_items = 1;
-      b.kitems = b.items;
-      b.kruns = b.runs;
+      b.kitems = causal ? tabs.bstream_kitems + (int64_t(ti) * tu + a) : b.items;
+      b.kruns = causal ? tabs.bstream_kruns : b.runs;
       b.n_kitems = 1;
-      b.causal = false;
+      b.causal = causal;
       b.q_len = static_cast<int>(U);
       b.scale = scale;
       HIP_TRY(tm.begin(PH_ATTN, s_c, tev));

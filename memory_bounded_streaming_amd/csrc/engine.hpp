@@ -18,6 +18,8 @@ struct DeviceTables {
   const WorkItem* dev_kitems;  // causal dK/dV tables (empty without causality)
   const KeyRun* dev_kruns;
   const WorkItem* bstream_items;  // streamed backward items (rows in the task staging)
+  const WorkItem* bstream_kitems; // causal streamed dK/dV items and runs (task staging rows)
+  const KeyRun* bstream_kruns;
   int64_t bytes;
 };
 

@@ -297,6 +297,8 @@ void build_descriptors(Plan& p) {
 
   p.dev_kitems.clear();
   p.dev_kruns.clear();
+  p.bstream_kitems.clear();
+  p.bstream_kruns.clear();
   if (!causal) return;
   for (const Task& t : p.tasks) {
     const int64_t tu = static_cast<int64_t>(t.units.size());
@@ -306,6 +308,10 @@ void build_descriptors(Plan& p) {
       ki.out_row0 = int64_t(t.slot[a]) * p.n + t.units[a] * p.unit;
       ki.q_len = static_cast<int32_t>(p.unit_rows(t.units[a]));
       ki.run0 = static_cast<int32_t>(p.dev_kruns.size());
+      WorkItem ks{};
+      ks.q_row0 = a * p.unit;
+      ks.q_len = ki.q_len;
+      ks.run0 = static_cast<int32_t>(p.bstream_kruns.size());
       int64_t rows = 0;
       // query units b >= a that the task admits with a (the mask is symmetric in a, b)
       int64_t b = a;
@@ -319,13 +325,17 @@ void build_descriptors(Plan& p) {
         const int64_t len = std::min((e - b) * p.unit, p.n - t.units[b] * p.unit);
         if (len > 0) {
           p.dev_kruns.push_back({t.units[b] * p.unit, static_cast<int32_t>(len), b == a ? 0 : -1});
+          p.bstream_kruns.push_back({b * p.unit, static_cast<int32_t>(len), b == a ? 0 : -1});
           rows += len;
         }
         b = e;
       }
       ki.nrun = static_cast<int32_t>(p.dev_kruns.size()) - ki.run0;
       ki.keys = static_cast<int32_t>(std::min<int64_t>(rows, INT32_MAX));
+      ks.nrun = ki.nrun;
+      ks.keys = ki.keys;
       if (ki.q_len > 0) p.dev_kitems.push_back(ki);
+      p.bstream_kitems.push_back(ks);  // indexed by (task, unit)
     }
   }
   std::stable_sort(p.dev_kitems.begin(), p.dev_kitems.end(),
@@ -338,6 +348,8 @@ int64_t descriptor_bytes(const Plan& p) {
          align_up(int64_t(p.dev_kitems.size()) * sizeof(WorkItem)) +
          align_up(int64_t(p.dev_kruns.size()) * sizeof(KeyRun)) +
          align_up(int64_t(p.bstream_items.size()) * sizeof(WorkItem)) +
+         align_up(int64_t(p.bstream_kitems.size()) * sizeof(WorkItem)) +
+         align_up(int64_t(p.bstream_kruns.size()) * sizeof(KeyRun)) +
          align_up(int64_t(p.stream_items.size()) * sizeof(WorkItem)) +
          align_up(int64_t(p.stream_runs.size()) * sizeof(KeyRun));
 }

@@ -73,6 +73,9 @@ struct Plan {
   // streamed backward: item (t, a) at index t*task_units + a, rows in the task's staging
   // (q_row0 = a * unit), outputs in a unit block (out_row0 = 0); runs are stream_runs
   std::vector<WorkItem> bstream_items;
+  // causal streamed dK/dV: the key-block tables in the same task-local coordinates
+  std::vector<WorkItem> bstream_kitems;
+  std::vector<KeyRun> bstream_kruns;
 
   Footprint stream_fp{};
   int64_t device_ws = 0;                // slots bytes of the device-resident path

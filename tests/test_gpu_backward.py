@@ -161,6 +161,9 @@ STREAM_CASES = [  # levels, N, heads, head_dim, dtype, flags
     ([2, 3], 21 * 9 + 2, 1, 128, "f32", cqsa.CQSA_FLAG_PAD),
     ([3], 7 * 300, 2, 128, "bf16", cqsa.CQSA_FLAG_KV_SINGLE),  # one task staging set
     ([4], 13 * 64, 2, 64, "bf16", cqsa.CQSA_FLAG_KV_SINGLE | cqsa.CQSA_FLAG_HOST_ACC),
+    ([3], 7 * 300, 2, 128, "bf16", cqsa.CQSA_FLAG_CAUSAL),
+    ([2, 2], 9 * 40 + 5, 1, 64, "bf16", cqsa.CQSA_FLAG_CAUSAL | cqsa.CQSA_FLAG_PAD | cqsa.CQSA_FLAG_HOST_ACC),
+    ([3], 7 * 33, 1, 128, "f32", cqsa.CQSA_FLAG_CAUSAL | cqsa.CQSA_FLAG_KV_SINGLE),
 ]
 
 
@@ -196,7 +199,7 @@ def test_streamed_backward_equals_device_backward(case):
         assert np.array_equal(g, w), f"{name} differs from the device path"
 
 
-def test_streamed_backward_respects_budget_and_rejects_causal():
+def test_streamed_backward_respects_budget():
     torch = pytest.importorskip("torch")
     n, h, d = 13 * 512, 4, 128
     with cqsa.Plan(n, h, d, cqsa.CQSA_BF16, [4]) as probe:
@@ -204,9 +207,3 @@ def test_streamed_backward_respects_budget_and_rejects_causal():
     with cqsa.Plan(n, h, d, cqsa.CQSA_BF16, [4], budget_bytes=need_dev // 2) as p:
         ws = p.backward_workspace_size(cqsa.CQSA_RES_HOST_PINNED)
         assert ws <= need_dev // 2  # the accumulators moved to pinned host memory
-    with cqsa.Plan(7 * 64, 1, 64, cqsa.CQSA_BF16, [3], flags=cqsa.CQSA_FLAG_CAUSAL) as p:
-        t = [torch.zeros((7 * 64, 1, 64), dtype=torch.int16, pin_memory=True) for _ in range(8)]
-        lse = torch.zeros((1, 7 * 64), pin_memory=True)
-        with pytest.raises(cqsa.CqsaError) as e:
-            p.backward(t[0], t[1], t[2], t[3], lse, t[4], t[5], t[6], t[7], residency=cqsa.CQSA_RES_HOST_PINNED)
-        assert e.value.status == -1
