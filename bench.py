@@ -287,7 +287,7 @@ def main():
     ap.add_argument("--no-streamed", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-streamed-backward", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--cpu-rows", type=int, default=8192)
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one plain device copy of 1 GiB first (reference for HBM traffic counters)")
     args = ap.parse_args()
