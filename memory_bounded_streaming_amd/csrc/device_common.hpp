@@ -73,12 +73,20 @@ struct TileCursor {
 
 __device__ __forceinline__ void cursor_settle(TileCursor& c, const KeyRun* runs, int nrun, int qhi) {
   while (c.run < nrun) {
-    const KeyRun r = runs[c.run];
-    const int len = r.diag >= 0 ? min(r.len, r.diag + qhi) : r.len;
+    // The run table is read-only and the index wave-uniform: reading it through the
+    // constant address space at a lane-0 address makes these scalar loads, which keep
+    // the vector-memory counter free for the tile loads.
+    const uint64_t ra = reinterpret_cast<uint64_t>(runs + c.run);
+    const uint64_t ru = (uint64_t(__builtin_amdgcn_readfirstlane(unsigned(ra >> 32))) << 32) |
+                        unsigned(__builtin_amdgcn_readfirstlane(unsigned(ra)));
+    const __attribute__((address_space(4))) KeyRun* rp = (const __attribute__((address_space(4))) KeyRun*)(ru);
+    const int64_t rstart = rp->start;
+    const int rlen = rp->len, rdiag = rp->diag;
+    const int len = rdiag >= 0 ? min(rlen, rdiag + qhi) : rlen;
     if (len > 0) {
-      c.start = r.start;
+      c.start = rstart;
       c.len = len;
-      c.diag = r.diag;
+      c.diag = rdiag;
       return;
     }
     ++c.run;

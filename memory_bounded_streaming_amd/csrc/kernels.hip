@@ -55,14 +55,16 @@ struct AttnParams {
 //
 // Pipeline: the next tile is fetched from global memory into registers while the
 // current one is computed from LDS, then written to the other LDS stage; one barrier
-// per tile.  The running max is rescaled lazily: the reference max only moves when a
-// score exceeds it by more than 2^8, so every exponent stays <= 2^8 and the triple
-// (m, l, n) remains exact for whatever m it carries.
+// per tile.  The running max is a lazily moved reference: the weights of a tile are
+// formed against it first, and it moves (with a rescale of l and n and a recompute of
+// the weights) only when a lane's weights sum to more than 2^8 or to a non-finite
+// value.  Every weight therefore stays <= 2^8, the triple (m, l, n) remains exact for
+// whatever m it carries, and the common path needs no max over the tile.
 // ---------------------------------------------------------------------------------
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-constexpr float kLazyRescale = 8.0f;  // log2 units
+constexpr float kLazySum = 256.0f;  // largest row sum of a lane's weights kept without moving m
 
 template <int D>
 struct Bf16Tile {
@@ -116,22 +118,25 @@ __global__ __launch_bounds__(512) void attn_partial_bf16(AttnParams P) {
     }
   }
 
-  // global -> register fetch of one tile (rows past the run end read as zero)
-  uint4 kr[T::CPT], vr[T::CPT];
+  // global -> register fetch of one tile.  Each thread's chunks sit at fixed offsets
+  // from the tile's first row (computed once); on a run's ragged last tile the rows past
+  // the end repeat the run's last row, so no read leaves the run, and their scores are
+  // masked to -inf (weight exactly 0).
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 kr[T::CPT], vr[T::CPT];
+  const uint32_t fcol = (tid % T::DCH) * 8;
+  const uint32_t fbase = static_cast<uint32_t>(tid / T::DCH) * static_cast<uint32_t>(rs) + fcol;
+  const uint32_t fstep = static_cast<uint32_t>(T::NT / T::DCH) * static_cast<uint32_t>(rs);
   auto fetch = [&](const TileCursor& c) {
-    const int64_t start = c.start + c.k0;
-    const int nv = min(T::KT, c.len - c.k0);
+    const u16* kb = K + (c.start + c.k0) * rs;
+    const u16* vb = V + (c.start + c.k0) * rs;
+    const uint32_t last = static_cast<uint32_t>(min(T::KT, c.len - c.k0) - 1) * static_cast<uint32_t>(rs) + fcol;
 #pragma unroll
     for (int i = 0; i < T::CPT; ++i) {
-      const int ch = tid + i * T::NT;
-      const int row = ch / T::DCH, cc = ch % T::DCH;
-      kr[i] = make_uint4(0, 0, 0, 0);
-      vr[i] = make_uint4(0, 0, 0, 0);
-      if (row < nv) {
-        const int64_t off = (start + row) * rs + cc * 8;
-        kr[i] = *reinterpret_cast<const uint4*>(K + off);
-        vr[i] = *reinterpret_cast<const uint4*>(V + off);
-      }
+      const uint32_t o = fbase + i * fstep;
+      const uint32_t off = o < last ? o : last;
+      kr[i] = *reinterpret_cast<const u32x4*>(kb + off);
+      vr[i] = *reinterpret_cast<const u32x4*>(vb + off);
     }
   };
   auto stash = [&](int stage) {
@@ -141,8 +146,8 @@ __global__ __launch_bounds__(512) void attn_partial_bf16(AttnParams P) {
     for (int i = 0; i < T::CPT; ++i) {
       const int ch = tid + i * T::NT;
       const int row = ch / T::DCH, cc = ch % T::DCH;
-      *reinterpret_cast<uint4*>(ks + row * T::KSTR + cc * 8) = kr[i];
-      *reinterpret_cast<uint4*>(vs + row * T::VSTR + cc * 8) = vr[i];
+      *reinterpret_cast<u32x4*>(ks + row * T::KSTR + cc * 8) = kr[i];
+      *reinterpret_cast<u32x4*>(vs + row * T::VSTR + cc * 8) = vr[i];
     }
   };
 
@@ -180,15 +185,18 @@ __global__ __launch_bounds__(512) void attn_partial_bf16(AttnParams P) {
     // scores S^T for keys [0,32) and [32,64)
     f32x16 s[2];
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
+    for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[st][i] = 0.f;
-      const u16* kp = ks + (32 * st + prow) * T::KSTR + 8 * hl;
+    {
+      const u16* kp = ks + prow * T::KSTR + 8 * hl;
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(kp + 16 * kk));
-        s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[st], 0, 0, 0);
-      }
+      for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(kp + 32 * st * T::KSTR + 16 * kk));
+          s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[st], 0, 0, 0);
+        }
     }
     // accumulator element i of tile st holds key 32*st + 16*(i/8) + 8*hl + i%8
     if (nv < T::KT) {
@@ -207,37 +215,44 @@ __global__ __launch_bounds__(512) void attn_partial_bf16(AttnParams P) {
         for (int i = 0; i < 16; ++i)
           if (32 * st + 16 * (i >> 3) + 8 * hl + (i & 7) > lim) s[st][i] = -INFINITY;
     }
-    float mx = s[0][0];
+    // Weights against the current reference m, and their row sum over the bf16-rounded
+    // values (the same values the P V product uses).  The weights are non-negative, so a
+    // lane whose sum is <= 2^8 has every weight <= 2^8.  A larger or non-finite sum (a
+    // row's first tile meets m = -inf) sends the wave to the rare branch: m moves to the
+    // tile max (both half-waves), l and O are rescaled, and the weights are recomputed.
+    bf16x8 pf[4];
+    float ps0 = 0.f, ps1 = 0.f;
+    auto weights = [&]() {
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+      for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[st][i]);
-    // Each half-wave holds 32 of the 64 scores of a query.  The reference max is
-    // shared by both halves; it only moves (rare) when some half's local max passes
-    // it by more than 2^8, and only then do the halves exchange their maxima.
-    mx *= c2;
-    if (__any(mx > m_run + kLazyRescale)) {
+        for (int i = 0; i < 16; ++i)
+          pf[2 * st + (i >> 3)][i & 7] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(s[st][i], c2, -m_run)));
+      ps0 = 0.f;
+      ps1 = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[q], pf[q], 0, 1), ones, ps0, false);
+        ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[q], pf[q], 2, 3), ones, ps1, false);
+        ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[q], pf[q], 4, 5), ones, ps0, false);
+        ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[q], pf[q], 6, 7), ones, ps1, false);
+      }
+    };
+    weights();
+    if (__any(!(ps0 + ps1 <= kLazySum))) {
+      float mx = s[0][0];
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[st][i]);
+      mx *= c2;
       const float m_new = fmaxf(m_run, fmaxf(mx, __shfl_xor(mx, 32)));
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
       m_run = m_new;
-    }
-    bf16x8 pf[4];
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        pf[2 * st + (i >> 3)][i & 7] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(s[st][i], c2, -m_run)));
-    // the row sum adds the bf16-rounded weights, the same values the P V product uses
-    float ps0 = 0.f, ps1 = 0.f;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[q], pf[q], 0, 1), ones, ps0, false);
-      ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[q], pf[q], 2, 3), ones, ps1, false);
-      ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[q], pf[q], 4, 5), ones, ps0, false);
-      ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[q], pf[q], 6, 7), ones, ps1, false);
+      weights();
     }
     l_run += ps0 + ps1;
     // O^T (dims x queries) += V^T * P^T, 16 keys per step
