@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 from memory_bounded_streaming_amd import cqsa
-from memory_bounded_streaming_amd.inputs import gen_qkv, sample_rows
+from memory_bounded_streaming_amd.inputs import bf16_bits_to_f32, gen_qkv, round_to_bf16_bits, sample_rows
 from oracle.attention import attention_fp64
 from oracle.plan import make_plan
 from oracle.recompose import finalize_fp64, merge_fp64, task_partials_fp64
@@ -120,6 +120,57 @@ def test_forward_device_matches_dense_attention(case):
         out = as_f64(to_numpy(o, dtype), dtype)
         _check(out, o_ref, dtype, "O")
         assert np.abs(lse.cpu().numpy() - lse_ref).max() <= (F32_LSE_TOL if dtype == "f32" else BF16_LSE_TOL)
+
+
+@pytest.mark.parametrize("profile", ["ramp", "spikes"])
+def test_forward_reference_max_moves(profile):
+    """Scores that keep growing along the keys, so the running reference max of the bf16
+    kernel must move on many tiles ("ramp"), and isolated keys whose logits pass it by far
+    more than 2^7 in log2 units, so the weights formed against the old reference overflow
+    to inf before it moves ("spikes").  Device path and per-task partials against the
+    fp64 oracle."""
+    torch = pytest.importorskip("torch")
+    levels, u, h, d = [3], 300, 2, 128
+    n = 7 * u
+    log(f"reference max {profile} N={n}")
+    q, k, v = gen_qkv(71, n, h, d, "bf16")
+    kf = bf16_bits_to_f32(k)
+    if profile == "ramp":
+        factor = 1.0 + 6.0 * np.arange(n) / n
+    else:
+        factor = np.ones(n)
+        factor[37::211] = 40.0
+    k = round_to_bf16_bits((kf * factor[:, None, None]).astype(np.float32))
+    o_ref, lse_ref = attention_fp64(q, k, v, dtype="bf16")
+    plan = make_plan(n, levels)
+    with cqsa.Plan(n, h, d, cqsa.CQSA_BF16, levels) as p:
+        qd, kd, vd = (to_device(x, "bf16") for x in (q, k, v))
+        o = empty_device((n, h, d), "bf16")
+        lse = torch.empty((h, n), device="cuda")
+        p.forward(qd, kd, vd, o, lse)
+        nsl = torch.full((3, n, h, d), float("nan"), device="cuda")
+        mls = torch.full((3, n, h, 2), float("nan"), device="cuda")
+        p.partials(qd, kd, vd, nsl, mls)
+        torch.cuda.synchronize()
+        out = as_f64(to_numpy(o, "bf16"), "bf16")
+        nsl, mls = nsl.cpu().numpy().astype(np.float64), mls.cpu().numpy().astype(np.float64)
+        lse_k = lse.cpu().numpy()
+    _check(out, o_ref, "bf16", "O")
+    lse_err = np.abs(lse_k - lse_ref).max()
+    log(f"  LSE abs err {lse_err:.3e} (|LSE| up to {np.abs(lse_ref).max():.1f})")
+    assert lse_err <= BF16_LSE_TOL
+    slots = _visit_slots(plan)
+    for task in plan.tasks:
+        parts = task_partials_fp64(q, k, v, plan, task, dtype="bf16")
+        for a, pu in enumerate(task.units):
+            rows, m_ref, l_ref, n_ref = parts[pu]
+            if not task.key_runs(a):
+                continue
+            sl = slots[(task.tid, pu)]
+            m_k, l_k, n_k = mls[sl, rows, :, 0], mls[sl, rows, :, 1], nsl[sl, rows]
+            assert np.isfinite(m_k).all() and (l_k >= 1.0).all() and (l_k <= 2.0 ** 8 * 2 * n).all()
+            assert np.abs(m_k * LN2 + np.log(l_k) - (m_ref + np.log(l_ref))).max() <= BF16_LSE_TOL
+            assert rowwise_rel_err(n_k / l_k[..., None], n_ref / l_ref[..., None]) <= BF16_REL_TOL
 
 
 @pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128), ("bf16", 64)])
