@@ -31,8 +31,8 @@ GiB = 1 << 30
 
 WORKLOADS = {
     # name: (N, H, d, levels, budget, residency description)
-    "c2": (57344, 8, 128, [3], 0, "device"),
-    "c3": (212992, 16, 128, [4], 16 * GiB, "host_pinned"),
+    "device_n57344": (57344, 8, 128, [3], 0, "device"),
+    "pinned_n212992": (212992, 16, 128, [4], 16 * GiB, "host_pinned"),
 }
 
 
@@ -51,7 +51,7 @@ def kernel_source_hash():
 
 def measured_traffic(kernel_hash, units_per_launch):
     """HBM bytes per launch from the committed rocprofv3 PMC summary, if it matches this kernel."""
-    path = os.path.join(ROOT, "profiles", "attn_partial_c2_traffic.json")
+    path = os.path.join(ROOT, "profiles", "attn_partial_bf16_d128_n57344_h8_l3_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -62,7 +62,7 @@ def measured_traffic(kernel_hash, units_per_launch):
 
 
 def cpu_baseline(rows_wanted=1024):
-    """The fp64 oracle on a bounded sample of the C2 workload (all keys, sampled query rows)."""
+    """The fp64 oracle on a bounded sample of the N=57344, 8-head workload (all keys, sampled query rows)."""
     from memory_bounded_streaming_amd.inputs import gen_qkv, sample_rows
     from oracle.attention import attention_fp64
     try:
@@ -84,7 +84,7 @@ def cpu_baseline(rows_wanted=1024):
 
 def run_device(args, torch, cqsa):
     from memory_bounded_streaming_amd.inputs import gen_qkv
-    n, h, d, levels, _, _ = WORKLOADS["c2"]
+    n, h, d, levels, _, _ = WORKLOADS["device_n57344"]
     q, k, v = gen_qkv(args.seed, n, h, d, "bf16")
     dev = [torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda() for x in (q, k, v)]
     plan = cqsa.Plan(n, h, d, cqsa.CQSA_BF16, levels)
@@ -143,7 +143,7 @@ def run_backward(args, torch, cqsa):
     (Delta/transposes, dK/dV and dQ kernels, slot sums), timed with HIP events on its
     stream; O and LSE come from one forward beforehand."""
     from memory_bounded_streaming_amd.inputs import gen_qkv, gen_tensor
-    n, h, d, levels, _, _ = WORKLOADS["c2"]
+    n, h, d, levels, _, _ = WORKLOADS["device_n57344"]
     q, k, v = gen_qkv(args.seed, n, h, d, "bf16")
     do = gen_tensor(args.seed, 3, n, h, d, "bf16")
     dev = [torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda() for x in (q, k, v, do)]
@@ -186,7 +186,7 @@ def run_streamed_backward(args, torch, cqsa):
     """Backward of the host-pinned N=212992, 16-head workload under 16 GiB: Q, K, V, O, dO
     and LSE in pinned memory, gradients written to pinned memory (one warm call, one timed)."""
     from memory_bounded_streaming_amd.inputs import gen_tensor
-    n, h, d, levels, budget, _ = WORKLOADS["c3"]
+    n, h, d, levels, budget, _ = WORKLOADS["pinned_n212992"]
     ts = []
     for i in range(4):  # Q, K, V, dO
         t = torch.empty((n, h, d), dtype=torch.int16, pin_memory=True)
@@ -236,7 +236,7 @@ def pcie_achievable(torch, nbytes=512 << 20, reps=5):
 
 def run_streamed(args, torch, cqsa):
     from memory_bounded_streaming_amd.inputs import gen_tensor
-    n, h, d, levels, budget, _ = WORKLOADS["c3"]
+    n, h, d, levels, budget, _ = WORKLOADS["pinned_n212992"]
     ts = []
     for i in range(3):
         t = torch.empty((n, h, d), dtype=torch.int16, pin_memory=True)
@@ -348,7 +348,7 @@ def main():
         log("bench: oracle cpu baseline")
         cpu = cpu_baseline(args.cpu_rows)
 
-    n, h, d, levels, _, _ = WORKLOADS["c2"]
+    n, h, d, levels, _, _ = WORKLOADS["device_n57344"]
     flop = dres["plan"]["useful_flop"]
     khash = kernel_source_hash()
     traffic = measured_traffic(khash, 1)

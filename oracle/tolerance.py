@@ -38,7 +38,7 @@ BF16_LSE_TOL = 2.0 ** -8
 # so P = 1 and dS = dP - Delta = 0 and its dQ row vanishes, whereas the kernel forms
 # Delta from the bf16-rounded O.  The pages state no gradient metric (the abstract of
 # arXiv 2604.20819 only compares gradient error with FlashAttention-2's); the floor
-# judges such rows by their error against the tensor's scale instead.
+# measures such rows by their error against the tensor's scale instead.
 GRAD_ROW_FLOOR = 2.0 ** -8
 
 

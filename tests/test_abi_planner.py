@@ -15,11 +15,11 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 GiB = 1 << 30
 
 CONFIGS = {  # name: (N, H, d, dtype, levels, budget)
-    "C1": (3584, 1, 64, cqsa.CQSA_F32, [3], 0),
-    "C2": (57344, 8, 128, cqsa.CQSA_BF16, [3], 0),
-    "C3": (212992, 16, 128, cqsa.CQSA_BF16, [4], 16 * GiB),
-    "C4": (1376256, 8, 128, cqsa.CQSA_BF16, [5], 8 * GiB),
-    "C5": (12845056, 1, 128, cqsa.CQSA_BF16, [3, 3], 2 * GiB),
+    "n3584_f32_l3": (3584, 1, 64, cqsa.CQSA_F32, [3], 0),
+    "n57344_h8_l3": (57344, 8, 128, cqsa.CQSA_BF16, [3], 0),
+    "n212992_h16_l4_16GiB": (212992, 16, 128, cqsa.CQSA_BF16, [4], 16 * GiB),
+    "n1376256_h8_l5_8GiB": (1376256, 8, 128, cqsa.CQSA_BF16, [5], 8 * GiB),
+    "n12845056_h1_l3x3_2GiB": (12845056, 1, 128, cqsa.CQSA_BF16, [3, 3], 2 * GiB),
 }
 
 
@@ -87,11 +87,11 @@ def test_footprint_fits_budget(name):
         assert info["useful_flop"] == pytest.approx(4.0 * n * n * d * h)
         # the K/V staging alone: kv_buffers x (K + V) x task tokens
         assert info["stream_workspace_bytes"] >= info["kv_buffers"] * 2 * info["task_tokens"] * h * d * e
-    modes = {"C1": 1, "C2": 1, "C3": 1, "C4": 2, "C5": 4}
+    modes = {"n3584_f32_l3": 1, "n57344_h8_l3": 1, "n212992_h16_l4_16GiB": 1, "n1376256_h8_l5_8GiB": 2, "n12845056_h1_l3x3_2GiB": 4}
     assert info["stream_mode"] == modes[name]
 
 
-def test_c4_device_accumulator_does_not_fit_8gib():
+def test_n1376256_device_accumulator_does_not_fit_8gib():
     # a device accumulator for all N rows (5.33 GiB) + the K/V double buffer (2.5 GiB) + the
     # two-slot query ring exceeds 8 GiB, so the accumulator moves to pinned host memory
     n, h, d = 1376256, 8, 128

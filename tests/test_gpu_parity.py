@@ -213,11 +213,11 @@ def test_merge_kernel_matches_fp64_merge(dtype, d):
     assert np.abs(lse.cpu().numpy() - lse_ref).max() <= 1e-5
 
 
-def test_c1_full_fp32():
+def test_n3584_fp32_every_row():
     """N=3584, H=1, d=64, fp32, l=3 ({0,1,3} mod 7, chunks of 512): every row."""
     torch = pytest.importorskip("torch")
     n, h, d = 3584, 1, 64
-    log("C1 full")
+    log("N=3584 fp32, every row")
     q, k, v = gen_qkv(0, n, h, d, "f32")
     o_ref, lse_ref = attention_fp64(q, k, v, dtype="f32")
     with cqsa.Plan(n, h, d, cqsa.CQSA_F32, [3]) as p:
@@ -227,16 +227,16 @@ def test_c1_full_fp32():
         p.forward(to_device(q, "f32"), to_device(k, "f32"), to_device(v, "f32"), o, lse)
         torch.cuda.synchronize()
         rep = error_report(o.cpu().numpy(), o_ref)
-        log(f"  C1 {rep}")
+        log(f"  N=3584 {rep}")
         assert rep["max_abs"] <= F32_ABS_TOL
         assert np.abs(lse.cpu().numpy() - lse_ref).max() <= 1e-5
 
 
-def test_c2_bf16_sampled_rows_and_determinism():
+def test_n57344_bf16_sampled_rows_and_determinism():
     """N=57344, H=8, d=128, bf16, l=3, device-resident; 2048 sampled rows + unit edges."""
     torch = pytest.importorskip("torch")
     n, h, d = 57344, 8, 128
-    log("C2 device-resident")
+    log("N=57344 H=8 bf16 device-resident")
     q, k, v = gen_qkv(0, n, h, d, "bf16")
     rows = sample_rows(n, 2048, 0, unit_tokens=8192)
     with cqsa.Plan(n, h, d, cqsa.CQSA_BF16, [3]) as p:
@@ -254,7 +254,7 @@ def test_c2_bf16_sampled_rows_and_determinism():
     o_ref, lse_ref = attention_fp64(q, k, v, rows=rows, dtype="bf16")
     out = as_f64(outs[0][0][rows], "bf16")
     rep = error_report(out, o_ref)
-    log(f"  C2 {rep}")
+    log(f"  N=57344 {rep}")
     assert rep["rowwise_rel"] <= BF16_REL_TOL
     assert np.abs(outs[0][1][:, rows] - lse_ref).max() <= BF16_LSE_TOL
 

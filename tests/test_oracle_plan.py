@@ -4,7 +4,7 @@ Each check ties the planner to something other than itself: the closed
 difference-set invariant, brute-force enumeration, the Steiner property
 S(2,l,c) stated in "Stream-CQSA: Breaking the Billion-Token Barrier on a Single
 GPU" (section "The 'CQS Divide': Attention as a Steiner System"), and a coverage
-table derived by hand (tests/golden/c1_coverage.txt).
+table derived by hand (tests/golden/l3_coverage.txt).
 """
 import itertools
 import os
@@ -18,11 +18,11 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 # The five workload plans: (levels, N)
 CONFIG_PLANS = {
-    "C1": ([3], 3584),
-    "C2": ([3], 57344),
-    "C3": ([4], 212992),
-    "C4": ([5], 1376256),
-    "C5": ([3, 3], 12845056),
+    "n3584_l3": ([3], 3584),
+    "n57344_l3": ([3], 57344),
+    "n212992_l4": ([4], 212992),
+    "n1376256_l5": ([5], 1376256),
+    "n12845056_l3x3": ([3, 3], 12845056),
 }
 
 
@@ -75,8 +75,8 @@ def test_no_difference_set_for_l7_brute_force():
         difference_set(7)
 
 
-def test_c1_coverage_matches_hand_derived_table():
-    want = np.loadtxt(os.path.join(GOLDEN, "c1_coverage.txt"), dtype=np.int32, comments="#")
+def test_l3_coverage_matches_hand_derived_table():
+    want = np.loadtxt(os.path.join(GOLDEN, "l3_coverage.txt"), dtype=np.int32, comments="#")
     plan = make_plan(3584, [3])
     assert plan.unit_tokens == 512
     np.testing.assert_array_equal(plan.coverage(), want)
@@ -122,7 +122,7 @@ def test_single_level_load_balance(l):
         assert diag == [task.tid]
 
 
-def test_c5_recursive_plan_shape():
+def test_two_level_12m_token_plan_shape():
     plan = make_plan(12845056, [3, 3])
     assert plan.unit_tokens == 262144 and plan.n_units == 49 and len(plan.tasks) == 49
     work = [sum(t.admitted(a, b) for a in range(9) for b in range(9)) for t in plan.tasks]

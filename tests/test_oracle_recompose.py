@@ -31,7 +31,7 @@ def test_recompose_equals_dense_attention(ls, unit):
     np.testing.assert_allclose(lse, lse_ref, rtol=1e-12)
 
 
-def test_recompose_on_c1_shape_bf16():
+def test_recompose_on_n3584_shape_bf16():
     plan = make_plan(3584, [3])
     q, k, v = gen_qkv(0, 3584, 1, 64, dtype="bf16")
     rows = np.array([0, 1, 511, 512, 2047, 3583])
