@@ -489,29 +489,41 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_bf16(BwdParams P) {
   const float lq = qok ? P.lse[head * P.n + qrow] * kLog2e : INFINITY;
   const float dq_delta = qok ? P.delta[head * P.n + qrow] : 0.f;
 
-  uint4 rk[T::RPT], rv[T::RPT], rkt[T::TPT];
+  // K/V rows: each thread's chunk sits at a fixed offset from the tile's first row; on a
+  // run's ragged last tile rows past the end repeat the run's last row (their scores are
+  // masked, so they add nothing).  K^T: 8 consecutive keys of one dim, zero past the run.
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 rk[T::RPT], rv[T::RPT];
+  uint4 rkt[T::TPT];
+  const uint32_t fcol = (tid % T::DCH) * 8;
+  const uint32_t fbase = static_cast<uint32_t>(tid / T::DCH) * static_cast<uint32_t>(rs) + fcol;
+  const uint32_t fstep = static_cast<uint32_t>(T::NT / T::DCH) * static_cast<uint32_t>(rs);
+  const u16* ktrow[T::TPT];
+  int ktc8[T::TPT];
+#pragma unroll
+  for (int i = 0; i < T::TPT; ++i) {
+    const int ch = tid + i * T::NT;
+    ktrow[i] = Kt + (ch / (T::KT / 8)) * P.np;
+    ktc8[i] = 8 * (ch % (T::KT / 8));
+  }
   auto fetch = [&](const TileCursor& c) {
     const int64_t start = c.start + c.k0;
     const int nv = min(T::KT, c.len - c.k0);
+    const u16* kb = K + start * rs;
+    const u16* vb = V + start * rs;
+    const uint32_t last = static_cast<uint32_t>(nv - 1) * static_cast<uint32_t>(rs) + fcol;
 #pragma unroll
     for (int i = 0; i < T::RPT; ++i) {
-      const int ch = tid + i * T::NT;
-      const int r = ch / T::DCH, cc = ch % T::DCH;
-      rk[i] = make_uint4(0, 0, 0, 0);
-      rv[i] = make_uint4(0, 0, 0, 0);
-      if (ch < T::RCH && r < nv) {
-        const int64_t off = (start + r) * rs + cc * 8;
-        rk[i] = *reinterpret_cast<const uint4*>(K + off);
-        rv[i] = *reinterpret_cast<const uint4*>(V + off);
+      if (tid + i * T::NT < T::RCH) {
+        const uint32_t o = fbase + i * fstep;
+        const uint32_t off = o < last ? o : last;
+        rk[i] = *reinterpret_cast<const u32x4*>(kb + off);
+        rv[i] = *reinterpret_cast<const u32x4*>(vb + off);
       }
     }
 #pragma unroll
-    for (int i = 0; i < T::TPT; ++i) {
-      const int ch = tid + i * T::NT;
-      const int dd = ch / (T::KT / 8), c8 = ch % (T::KT / 8);
-      rkt[i] = make_uint4(0, 0, 0, 0);
-      if (ch < T::TCH) rkt[i] = load_tr_chunk(Kt + dd * P.np, start + 8 * c8, 8 * c8, nv);
-    }
+    for (int i = 0; i < T::TPT; ++i)
+      if (tid + i * T::NT < T::TCH) rkt[i] = load_tr_chunk(ktrow[i], start + ktc8[i], ktc8[i], nv);
   };
   auto stash = [&](int stage) {
     char* base = smem + stage * T::STAGE;
@@ -523,8 +535,8 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_bf16(BwdParams P) {
       const int ch = tid + i * T::NT;
       const int r = ch / T::DCH, cc = ch % T::DCH;
       if (ch < T::RCH) {
-        *reinterpret_cast<uint4*>(ks + r * T::RSTR + cc * 8) = rk[i];
-        *reinterpret_cast<uint4*>(vs + r * T::RSTR + cc * 8) = rv[i];
+        *reinterpret_cast<u32x4*>(ks + r * T::RSTR + cc * 8) = rk[i];
+        *reinterpret_cast<u32x4*>(vs + r * T::RSTR + cc * 8) = rv[i];
       }
     }
 #pragma unroll
@@ -562,9 +574,13 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_bf16(BwdParams P) {
     const u16* vs = reinterpret_cast<const u16*>(base + T::ROWB);
     const u16* kts = reinterpret_cast<const u16*>(base + 2 * T::ROWB);
 
+    // dP^T - Delta: the accumulator starts at -Delta (all 16 values of a lane are its query)
     f32x16 s, dp;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+    for (int i = 0; i < 16; ++i) {
+      s[i] = 0.f;
+      dp[i] = -dq_delta;
+    }
     {
       const u16* kp = ks + prow * T::RSTR + 8 * hl;
       const u16* vp = vs + prow * T::RSTR + 8 * hl;
@@ -593,7 +609,7 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_bf16(BwdParams P) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const float p = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -lq));
-      db[i >> 3][i & 7] = static_cast<__bf16>(p * (dp[i] - dq_delta));
+      db[i >> 3][i & 7] = static_cast<__bf16>(p * dp[i]);
     }
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
