@@ -158,3 +158,19 @@ def test_causal_matches_masked_scipy_softmax_and_prefix_attention():
     np.testing.assert_array_equal(o[0], v[0].astype(np.float64))  # the first row sees only itself
     full, _ = attention_fp64(q, k, v, rows=[n - 1], dtype="f32")
     np.testing.assert_allclose(o[n - 1], full[0], rtol=1e-13, atol=1e-15)  # the last row sees every key
+
+
+def test_bf16_lse_tolerance_covers_weight_rounding():
+    """The bf16 LSE bound against the arithmetic it is derived from: a softmax weight
+    rounded to bf16 (nearest even) moves ln of a row sum it dominates by at most
+    ln(1 + 2^-8).  Computed over a dense grid of weights in one binade (rounding is
+    scale-free), the worst case must equal that, exceed what a 2^-9 rounding error
+    would allow, and stay under the bound with room for float32 rounding."""
+    from oracle.tolerance import BF16_LSE_TOL
+    p = np.linspace(1.0, 2.0, 1 << 20, endpoint=False, dtype=np.float64).astype(np.float32)
+    bits = round_to_bf16_bits(p)
+    r = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    worst = np.abs(np.log(r) - np.log(p.astype(np.float64))).max()
+    assert worst == pytest.approx(math.log1p(2.0 ** -8), rel=1e-6)
+    assert 2.0 ** -9 < worst < BF16_LSE_TOL
+    assert BF16_LSE_TOL - worst > 2.0 ** -13
