@@ -470,8 +470,8 @@ cqsa_status build_plan(int64_t n, int heads, int d, cqsa_dtype dtype, const int3
   if (n < 1 || heads < 1 || (d != 64 && d != 128) || ls == nullptr || n_levels < 0 ||
       n_levels > CQSA_MAX_LEVELS || budget < 0 || (dtype != CQSA_BF16 && dtype != CQSA_F32) ||
       (flags & ~(CQSA_FLAG_HOST_ACC | CQSA_FLAG_KV_SINGLE | CQSA_FLAG_PAD | CQSA_FLAG_CAUSAL)) != 0) {
-    why = "invalid argument (need n>=1, heads>=1, head_dim 64 or 128, 0<=n_levels<=" + std::to_string(CQSA_MAX_LEVELS) +
-          ", budget>=0, known dtype/flags)";
+    why = "need n>=1, heads>=1, head_dim 64 or 128, 0<=n_levels<=" + std::to_string(CQSA_MAX_LEVELS) +
+          ", budget>=0, known dtype and flags";
     return CQSA_EINVAL;
   }
   if (n > (int64_t(1) << 40) || int64_t(heads) * d > (int64_t(1) << 20)) {
@@ -558,7 +558,7 @@ cqsa_status estimate_plan(int64_t n, int heads, int d, cqsa_dtype dtype, const i
       n_levels > CQSA_MAX_LEVELS || budget < 0 || (dtype != CQSA_BF16 && dtype != CQSA_F32) ||
       (flags & ~(CQSA_FLAG_HOST_ACC | CQSA_FLAG_KV_SINGLE | CQSA_FLAG_PAD | CQSA_FLAG_CAUSAL)) != 0 || !(r.attn_tflops > 0) ||
       !(r.merge_gbs > 0) || !(r.h2d_gbs > 0) || !(r.d2h_gbs > 0)) {
-    why = "invalid argument (see cqsa_plan_create; every rate must be positive)";
+    why = "the arguments of cqsa_plan_create, and every rate must be positive";
     return CQSA_EINVAL;
   }
   Plan p;
