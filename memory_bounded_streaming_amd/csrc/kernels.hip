@@ -9,8 +9,10 @@
 // "Online normalizer calculation for softmax" (cited by title on the arXiv page).
 //
 // Partial of one task for query row i:   (log2 units throughout)
-//   m = log2(e) * max_j s_ij,  l = sum_j 2^(log2(e) s_ij - m),  n = sum_j 2^(...) v_j
-// over the keys admitted for i.  The kernel design (tiles, LDS layout, MFMA shapes) is
+//   m = a reference at most 8 below log2(e) * max_j s_ij (the bf16 kernel moves it
+//       lazily; the fp32 kernel keeps the running max),
+//   l = sum_j 2^(log2(e) s_ij - m),  n = sum_j 2^(log2(e) s_ij - m) v_j
+// over the keys admitted for i; (m, l, n) is exact for whatever m it carries.  The kernel design (tiles, LDS layout, MFMA shapes) is
 // this library's own for CDNA4 wave64 hardware.
 #include <hip/hip_runtime.h>
 
