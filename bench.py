@@ -79,7 +79,10 @@ def cpu_baseline(rows_wanted=1024):
     flop = 4.0 * rows.size * n * d * h
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{rows.size} sampled query rows x {h} heads of the N={n}, d={d} workload against all "
-                      f"{n} keys, fp64 two-pass softmax; {dt:.1f} s wall; rate = 4*rows*N*d*H / time"}
+                      f"{n} keys, fp64 two-pass softmax; {dt:.1f} s wall; rate = 4*rows*N*d*H / time",
+            "sample_wall_s": round(dt, 2),
+            "extrapolated_full_n_s": round(dt * n / rows.size, 1),
+            "extrapolation": f"sample wall x N/rows = time for all {n} query rows (not measured)"}
 
 
 def run_device(args, torch, cqsa):
