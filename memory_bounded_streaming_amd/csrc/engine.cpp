@@ -299,19 +299,19 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
   cqsa_status st = device_tables(p, tabs, why);
   if (st != CQSA_OK) return st;
 
-  StreamRes R;
+  StreamRes res;
   if (ws == nullptr) {
-    HIP_TRY(hipMalloc(&R.ws, L.total));
-    R.own_ws = true;
+    HIP_TRY(hipMalloc(&res.ws, L.total));
+    res.own_ws = true;
   } else {
     if (ws_bytes < L.total) {
       why = "workspace of " + std::to_string(ws_bytes) + " bytes, need " + std::to_string(L.total);
       return CQSA_ESMALL;
     }
-    R.ws = ws;
+    res.ws = ws;
   }
   // carve the workspace
-  char* cur = static_cast<char*>(R.ws);
+  char* cur = static_cast<char*>(res.ws);
   auto take = [&](int64_t bytes) {
     char* r = cur;
     cur += bytes;
@@ -351,26 +351,26 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
   float* host_n = nullptr;
   float* host_ml = nullptr;
   if (!fp.acc_on_device) {
-    HIP_TRY(hipHostMalloc(reinterpret_cast<void**>(&R.host_acc), N * (nrow_f + mlrow_f) * sizeof(float),
+    HIP_TRY(hipHostMalloc(reinterpret_cast<void**>(&res.host_acc), N * (nrow_f + mlrow_f) * sizeof(float),
                           hipHostMallocDefault));
-    host_n = R.host_acc;
-    host_ml = R.host_acc + N * nrow_f;
+    host_n = res.host_acc;
+    host_ml = res.host_acc + N * nrow_f;
   }
-  R.caller = caller;
-  for (auto& s : R.s) HIP_TRY(hipStreamCreateWithFlags(&s, hipStreamNonBlocking));
-  hipStream_t s_kv = R.s[0], s_q = R.s[1], s_c = caller, s_d = R.s[2];
+  res.caller = caller;
+  for (auto& s : res.s) HIP_TRY(hipStreamCreateWithFlags(&s, hipStreamNonBlocking));
+  hipStream_t s_kv = res.s[0], s_q = res.s[1], s_c = caller, s_d = res.s[2];
   hipEvent_t start, kv_ready[2], kv_free[2], q_ready[2], c_done[2], slot_free[2], task_done[3];
-  HIP_TRY(R.event(start));
-  for (int i = 0; i < 3; ++i) HIP_TRY(R.event(task_done[i]));
+  HIP_TRY(res.event(start));
+  for (int i = 0; i < 3; ++i) HIP_TRY(res.event(task_done[i]));
   for (int i = 0; i < 2; ++i) {
-    HIP_TRY(R.event(kv_ready[i]));
-    HIP_TRY(R.event(kv_free[i]));
-    HIP_TRY(R.event(q_ready[i]));
-    HIP_TRY(R.event(c_done[i]));
-    HIP_TRY(R.event(slot_free[i]));
+    HIP_TRY(res.event(kv_ready[i]));
+    HIP_TRY(res.event(kv_free[i]));
+    HIP_TRY(res.event(q_ready[i]));
+    HIP_TRY(res.event(c_done[i]));
+    HIP_TRY(res.event(slot_free[i]));
   }
   HIP_TRY(hipEventRecord(start, caller));
-  for (hipStream_t s : R.s) HIP_TRY(hipStreamWaitEvent(s, start, 0));
+  for (hipStream_t s : res.s) HIP_TRY(hipStreamWaitEvent(s, start, 0));
 
   PhaseTimer tm;
   tm.on = stats != nullptr;
@@ -576,7 +576,7 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
     HIP_TRY(hipEventRecord(task_done[ti % 3], s_c));
   }
   HIP_TRY(hipStreamSynchronize(s_c));
-  for (hipStream_t s : R.s) HIP_TRY(hipStreamSynchronize(s));
+  for (hipStream_t s : res.s) HIP_TRY(hipStreamSynchronize(s));
   if (progress)
     for (int64_t t = std::max<int64_t>(0, n_tasks - 2); t < n_tasks; ++t) report(t);
   HIP_TRY(hipGetLastError());
