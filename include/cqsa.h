@@ -213,8 +213,13 @@ cqsa_status cqsa_workspace_size(const cqsa_plan* plan, cqsa_residency res, int64
  * of the wispaper explainer: compute the local numerators and denominators; the CQS
  * Mask selects the keys).  For every task t and every query row i of t:
  *     s_ij = (1/sqrt(d)) <q_i, k_j> over the keys j that t admits for i,
- *     m = log2(e) * max_j s_ij,  l = sum_j 2^(log2(e) s_ij - m),
+ *     m = a reference with  M - 8 <= m <= M,  M = log2(e) * max_j s_ij
+ *         (bf16: moved lazily, so it can trail the max by up to 8; float32: m = M),
+ *     l = sum_j 2^(log2(e) s_ij - m),
  *     n = sum_j 2^(log2(e) s_ij - m) v_j            (unnormalised, float32)
+ * The triple is exact for whatever m it carries; only m + log2 l and n / l are
+ * invariants, and the merge uses nothing else.  A row no key reaches holds
+ * (m, l, n) = (-inf, 0, 0).
  * q, k, v: device [N, H, d] in the plan's dtype (read only).
  * n_out: device float32 [V][N][H][d]; ml_out: device float32 [V][N][H][2] holding (m, l);
  *   V = visits; slot s of row i holds the s-th task (ascending id) that visits row i.
