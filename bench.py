@@ -346,6 +346,13 @@ def main():
                         "host_pinned_bytes": e["host_pinned_bytes"], "bytes_h2d": e["bytes_h2d"],
                         "bytes_d2h": e["bytes_d2h"], "est_hours": round(e["t_est_s"] / 3600, 2),
                         "attn_hours": round(e["t_attn_s"] / 3600, 2), "h2d_hours": round(e["t_h2d_s"] / 3600, 2)})
+            if sbwd is not None:
+                # not a plan of the backward: the forward estimate scaled by the streamed backward's
+                # measured time over the streamed forward's on the 16 GiB workload
+                ratio = sbwd["wall_s"] / stream_res["wall_s"]
+                dry[-1]["bwd_hours_by_ratio"] = round(e["t_est_s"] * ratio / 3600, 1)
+                dry[-1]["bwd_ratio_note"] = (f"extrapolation: forward estimate x {ratio:.2f}, the measured streamed "
+                                             "backward / forward time of the N=212992, 16-head workload")
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: oracle cpu baseline")
