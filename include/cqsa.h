@@ -19,7 +19,8 @@
  * Conventions for every call
  *   - Tensors are token-major [N, H, d] (batch 1), row stride H*d elements.
  *     dtype CQSA_BF16 = bfloat16 (2 bytes), CQSA_F32 = float32.
- *   - Attention is non-causal over all N keys with softmax scale 1/sqrt(d).
+ *   - Attention is over all N keys (non-causal) unless the plan was created with
+ *     CQSA_FLAG_CAUSAL (row i then attends keys j <= i); softmax scale 1/sqrt(d).
  *   - Every call returns a cqsa_status; 0 is success.  On failure nothing is
  *     guaranteed about outputs, and cqsa_last_error() returns a thread-local
  *     message.  No C++ exception crosses this boundary.
@@ -95,7 +96,7 @@ typedef struct {
   int64_t stream_workspace_bytes; /* device bytes the host-pinned path needs (<= budget) */
   int64_t device_workspace_bytes; /* device bytes the device-resident path needs */
   int64_t host_acc_bytes;       /* pinned host accumulator the host-pinned path allocates (0 if on device) */
-  double useful_flop;           /* 4 * N^2 * d * H */
+  double useful_flop;           /* 4 * N^2 * d * H; 2 * N * (N+1) * d * H with CQSA_FLAG_CAUSAL */
   int64_t padded_tokens;        /* N_pad = unit_tokens * n_units (== n_tokens unless padded) */
 } cqsa_plan_info;
 
@@ -137,7 +138,7 @@ typedef struct {
                                    and bytes_h2d + bytes_d2d is exact */
   int64_t bytes_d2d;            /* K/V rows of shared chunks copied device to device */
   int64_t merge_bytes;          /* HBM bytes of all merge launches */
-  double useful_flop;           /* 4 N^2 d H */
+  double useful_flop;           /* 4 N^2 d H; 2 N (N+1) d H with CQSA_FLAG_CAUSAL */
   double t_attn_s, t_merge_s, t_h2d_s, t_d2h_s;
   double t_est_s;               /* max(attn + merge (+ unoverlapped K/V loads), h2d, d2h) */
   int32_t materializable;       /* 1 if cqsa_plan_create builds this plan */
@@ -243,7 +244,8 @@ cqsa_status cqsa_merge(const cqsa_plan* plan, const float* n_in, const float* ml
                        void* o, float* lse, void* stream);
 
 /*
- * Full CQS forward: O = softmax(Q K^T / sqrt(d)) V and LSE, exact up to rounding.
+ * Full CQS forward: O = softmax(Q K^T / sqrt(d)) V and LSE, exact up to rounding (with
+ * CQSA_FLAG_CAUSAL the softmax runs over keys j <= i).
  *   CQSA_RES_DEVICE: q, k, v, o, lse are device pointers; runs cqsa_partials then
  *     cqsa_merge on stream using `workspace` (>= cqsa_workspace_size bytes) for the
  *     partial slots.  Stream-ordered: returns after enqueuing unless the library had
@@ -300,7 +302,8 @@ cqsa_status cqsa_backward_workspace_size(const cqsa_plan* plan, cqsa_residency r
  *   workspace: device buffer >= cqsa_backward_workspace_size(res) bytes, or NULL (the
  *     library allocates and frees it).
  *   stats: optional; t_attn_ms = the two gradient kernels, t_merge_ms = the Delta /
- *     transpose pass and the slot sums, useful_flop = 10 N^2 d H.
+ *     transpose pass and the slot sums, useful_flop = 2.5 times the forward's
+ *     (10 N^2 d H; 5 N (N+1) d H with CQSA_FLAG_CAUSAL).
  * Errors: EINVAL, ESMALL, EBUDGET (workspace over the plan's budget), EHIP, ENOMEM.
  */
 cqsa_status cqsa_backward(const cqsa_plan* plan, const void* q, const void* k, const void* v,
