@@ -25,7 +25,10 @@
  *     guaranteed about outputs, and cqsa_last_error() returns a thread-local
  *     message.  No C++ exception crosses this boundary.
  *   - "stream" is a hipStream_t passed as void* (NULL = the null stream).
- *   - Device pointers must be on the current HIP device.
+ *   - Device pointers must be on the current HIP device.  Device tensors (and any
+ *     workspace) must start on a 16-byte boundary, an LSE array on a 4-byte one
+ *     (rows are moved in 16-byte vectors; every row stride is a multiple of 128 bytes);
+ *     a misaligned pointer is EINVAL.  Host-pinned tensors have no such requirement.
  */
 #ifndef CQSA_H
 #define CQSA_H

@@ -3,7 +3,9 @@
 // thread-local message; no exception crosses the boundary.
 #include <hip/hip_runtime_api.h>
 
+#include <cstdint>
 #include <cstring>
+#include <initializer_list>
 #include <exception>
 #include <new>
 #include <string>
@@ -29,6 +31,18 @@ cqsa_status ok() {
   g_last_error.clear();
   return CQSA_OK;
 }
+
+// The kernels move tensor rows in 16-byte vectors; the row stride H*d is a multiple of
+// 128 bytes, so the base addresses decide the alignment.
+bool aligned(const void* p, uintptr_t bytes) { return (reinterpret_cast<uintptr_t>(p) % bytes) == 0; }
+
+bool aligned16(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (!aligned(p, 16)) return false;
+  return true;
+}
+
+constexpr const char* kAlignWhy = "device tensors and workspaces must start on a 16-byte boundary (lse on a 4-byte one)";
 
 template <typename F>
 cqsa_status guarded(F&& f) {
@@ -186,6 +200,7 @@ cqsa_status cqsa_partials(const cqsa_plan* plan, const void* q, const void* k, c
   return guarded([&]() -> cqsa_status {
     if (plan == nullptr || q == nullptr || k == nullptr || v == nullptr || n_out == nullptr || ml_out == nullptr)
       return fail(CQSA_EINVAL, "NULL argument");
+    if (!aligned16({q, k, v, n_out, ml_out})) return fail(CQSA_EINVAL, kAlignWhy);
     std::string why;
     const cqsa_status s = cqsa::run_partials(plan->p, q, k, v, n_out, ml_out, static_cast<hipStream_t>(stream), why);
     return s == CQSA_OK ? ok() : fail(s, why);
@@ -197,6 +212,7 @@ cqsa_status cqsa_merge(const cqsa_plan* plan, const float* n_in, const float* ml
   return guarded([&]() -> cqsa_status {
     if (plan == nullptr || n_in == nullptr || ml_in == nullptr || o == nullptr)
       return fail(CQSA_EINVAL, "NULL argument");
+    if (!aligned16({n_in, ml_in, o}) || !aligned(lse, 4)) return fail(CQSA_EINVAL, kAlignWhy);
     std::string why;
     const cqsa_status s = cqsa::run_merge(plan->p, n_in, ml_in, o, lse, static_cast<hipStream_t>(stream), why);
     return s == CQSA_OK ? ok() : fail(s, why);
@@ -211,6 +227,9 @@ cqsa_status cqsa_forward(const cqsa_plan* plan, const void* q, const void* k, co
       return fail(CQSA_EINVAL, "NULL argument");
     if (res != CQSA_RES_DEVICE && res != CQSA_RES_HOST_PINNED) return fail(CQSA_EINVAL, "unknown residency");
     if (workspace != nullptr && workspace_bytes <= 0) return fail(CQSA_EINVAL, "workspace size must be positive");
+    if (!aligned(workspace, 16) ||
+        (res == CQSA_RES_DEVICE && (!aligned16({q, k, v, o}) || !aligned(lse, 4))))
+      return fail(CQSA_EINVAL, kAlignWhy);
     std::string why;
     const cqsa_status s = cqsa::run_forward(plan->p, q, k, v, o, lse, res, workspace, workspace_bytes,
                                             static_cast<hipStream_t>(stream), stats, why);
@@ -242,6 +261,9 @@ cqsa_status cqsa_backward(const cqsa_plan* plan, const void* q, const void* k, c
       return fail(CQSA_EINVAL, "NULL argument");
     if (res != CQSA_RES_DEVICE && res != CQSA_RES_HOST_PINNED) return fail(CQSA_EINVAL, "unknown residency");
     if (workspace != nullptr && workspace_bytes <= 0) return fail(CQSA_EINVAL, "workspace size must be positive");
+    if (!aligned(workspace, 16) ||
+        (res == CQSA_RES_DEVICE && (!aligned16({q, k, v, o, d_o, dq, dk, dv}) || !aligned(lse, 4))))
+      return fail(CQSA_EINVAL, kAlignWhy);
     std::string why;
     const cqsa_status s = cqsa::run_backward(plan->p, q, k, v, o, lse, d_o, dq, dk, dv, res, workspace,
                                              workspace_bytes, static_cast<hipStream_t>(stream), stats, why);

@@ -178,6 +178,23 @@ def test_bad_flags_and_null_arguments(lib):
     lib.cqsa_plan_destroy(None)
 
 
+def test_misaligned_device_pointers_are_rejected(lib):
+    """Device tensors and workspaces must start on 16 bytes (lse on 4); the check runs
+    before any HIP call, so fake addresses are never dereferenced."""
+    import ctypes
+    good, bad = 1 << 20, (1 << 20) + 2
+    with cqsa.Plan(49, 1, 64, cqsa.CQSA_BF16, [3]) as p:
+        h = p.handle
+        assert lib.cqsa_partials(h, good, good, bad, good, good, None) == -1
+        assert "16-byte" in cqsa.cqsa_last_error()
+        assert lib.cqsa_merge(h, good, good, good, good + 2, None) == -1
+        assert lib.cqsa_forward(h, bad, good, good, good, None, cqsa.CQSA_RES_DEVICE, None, 0, None, None) == -1
+        assert lib.cqsa_forward(h, good, good, good, good, None, cqsa.CQSA_RES_HOST_PINNED, bad, 64, None, None) == -1
+        assert lib.cqsa_backward(h, good, good, good, good, good, good, good, bad, good, cqsa.CQSA_RES_DEVICE, None, 0,
+                                 None, None) == -1
+        assert "16-byte" in cqsa.cqsa_last_error()
+
+
 def test_status_strings(lib):
     for s in (0, -1, -2, -3, -4, -5, -6, -7):
         assert cqsa.cqsa_status_string(s)
