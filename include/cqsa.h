@@ -253,7 +253,8 @@ cqsa_status cqsa_merge(const cqsa_plan* plan, const float* n_in, const float* ml
  *     cqsa_merge on stream using `workspace` (>= cqsa_workspace_size bytes) for the
  *     partial slots.  Stream-ordered: returns after enqueuing unless the library had
  *     to allocate the workspace itself (workspace == NULL), or stats != NULL.
- *   CQSA_RES_HOST_PINNED: q, k, v, o, lse are pinned host pointers (lse may be NULL).
+ *   CQSA_RES_HOST_PINNED: q, k, v, o, lse are pinned host pointers (lse may be NULL);
+ *     a device pointer or pageable host memory among them is EINVAL, before any copy.
  *     Tasks run in ascending id; each task's K/V segments are gathered into device
  *     staging with hipMemcpyAsync on copy streams, double-buffered when the mode says
  *     so, query units are streamed in blocks, partials are merged into the
@@ -295,7 +296,8 @@ cqsa_status cqsa_backward_workspace_size(const cqsa_plan* plan, cqsa_residency r
  *     forward's outputs (lse: float32 [H, N], natural log).
  *   dq, dk, dv: [N, H, d] in the plan's dtype (written; round to nearest even).
  *   res: CQSA_RES_DEVICE (device pointers; stream-ordered like cqsa_forward) or
- *     CQSA_RES_HOST_PINNED (pinned host pointers; synchronous): Delta of every row is
+ *     CQSA_RES_HOST_PINNED (pinned host pointers, else EINVAL before any copy;
+ *     synchronous): Delta of every row is
  *     formed first from O and dO streamed in unit blocks; then per task in ascending id
  *     its Q, K, V, dO rows are staged and transposed on the device, its L and Delta
  *     rows gathered, and for each of its units the dQ and dK/dV terms are added into

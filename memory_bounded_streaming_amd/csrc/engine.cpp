@@ -22,6 +22,8 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <initializer_list>
+#include <utility>
 #include <vector>
 
 #include "kernels.hpp"
@@ -81,6 +83,24 @@ struct PhaseTimer {
 };
 
 enum { PH_H2D = 0, PH_ATTN = 1, PH_MERGE = 2, PH_D2H = 3 };
+
+// The host-pinned paths copy with explicit host <-> device directions and overlap the
+// copies with compute, so every host tensor must be pinned host memory (hipHostMalloc,
+// torch pin_memory).  A device pointer or pageable memory is rejected before any copy.
+cqsa_status check_pinned(std::initializer_list<std::pair<const void*, const char*>> ps, std::string& why) {
+  for (const auto& pr : ps) {
+    if (pr.first == nullptr) continue;
+    hipPointerAttribute_t a{};
+    const hipError_t e = hipPointerGetAttributes(&a, pr.first);
+    if (e != hipSuccess) (void)hipGetLastError();  // pageable memory may be reported as an error
+    if (e != hipSuccess || a.type != hipMemoryTypeHost) {
+      why = std::string(pr.second) +
+            " is not pinned host memory (the host-pinned residency needs hipHostMalloc or pin_memory buffers)";
+      return CQSA_EINVAL;
+    }
+  }
+  return CQSA_OK;
+}
 
 }  // namespace
 
@@ -292,6 +312,10 @@ struct StreamRes {
 
 cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const char* v, char* o, float* lse,
                            void* ws, int64_t ws_bytes, hipStream_t caller, cqsa_stats* stats, std::string& why) {
+  {
+    const cqsa_status pin = check_pinned({{q, "q"}, {k, "k"}, {v, "v"}, {o, "o"}, {lse, "lse"}}, why);
+    if (pin != CQSA_OK) return pin;
+  }
   const auto t0 = std::chrono::steady_clock::now();
   const Footprint fp = p.stream_fp;
   const StreamLayout L = stream_layout(p, fp.acc_on_device, fp.kv_buffers);
@@ -643,6 +667,12 @@ struct BwdStreamRes {
 cqsa_status backward_stream(const Plan& p, const char* q, const char* k, const char* v, const char* o,
                             const float* lse, const char* d_o, char* dq, char* dk, char* dv, void* ws,
                             int64_t ws_bytes, hipStream_t caller, cqsa_stats* stats, std::string& why) {
+  {
+    const cqsa_status pin = check_pinned({{q, "q"}, {k, "k"}, {v, "v"}, {o, "o"}, {lse, "lse"}, {d_o, "d_o"},
+                                          {dq, "dq"}, {dk, "dk"}, {dv, "dv"}},
+                                         why);
+    if (pin != CQSA_OK) return pin;
+  }
   const bool causal = (p.flags & CQSA_FLAG_CAUSAL) != 0;
   if (p.bwd_stream_fp.bytes < 0) {
     why = "no streamed backward layout fits the budget of " + std::to_string(p.budget) + " bytes";

@@ -97,3 +97,33 @@ def test_stream_respects_budget_and_reports_phases():
     rows = np.arange(0, n, 37)
     o_ref, _ = attention_fp64(q, k, v, rows=rows, dtype="bf16")
     assert rowwise_rel_err(as_f64(oa[rows], "bf16"), o_ref) <= BF16_REL_TOL
+
+
+def test_host_pinned_residency_rejects_device_and_pageable_buffers():
+    """The streamed paths copy with explicit host/device directions: a device tensor or
+    pageable host memory given as a host-pinned buffer is EINVAL before any copy, and a
+    correct call on the same plan still works afterwards."""
+    torch = pytest.importorskip("torch")
+    n, h, d = 7 * 64, 1, 64
+    q, k, v = gen_qkv(3, n, h, d, "bf16")
+    with cqsa.Plan(n, h, d, cqsa.CQSA_BF16, [3]) as p:
+        pins = []
+        for x in (q, k, v):
+            t, a = pinned((n, h, d), "bf16")
+            a[...] = x
+            pins.append(t)
+        to, oa = pinned((n, h, d), "bf16")
+        dev = to_device(q, "bf16")
+        pageable = np.zeros((n, h, d), np.uint16)
+        for bad in ((dev, pins[1], pins[2], to), (pins[0], pins[1], pins[2], pageable)):
+            with pytest.raises(cqsa.CqsaError) as e:
+                p.forward(*bad, None, residency=cqsa.CQSA_RES_HOST_PINNED)
+            assert e.value.status == -1 and "pinned" in str(e.value)
+        lse = torch.empty((h, n), dtype=torch.float32, pin_memory=True)
+        g = [pinned((n, h, d), "bf16")[0] for _ in range(3)]
+        with pytest.raises(cqsa.CqsaError) as e:
+            p.backward(pins[0], pins[1], pins[2], to, lse, dev, *g, residency=cqsa.CQSA_RES_HOST_PINNED)
+        assert e.value.status == -1 and "d_o" in str(e.value)
+        p.forward(*pins, to, lse, residency=cqsa.CQSA_RES_HOST_PINNED)
+        o_dev, _ = _device_forward(p, q, k, v, n, h, d, "bf16")
+        assert np.array_equal(oa, o_dev)
