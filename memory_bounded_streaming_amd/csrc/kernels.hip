@@ -119,6 +119,11 @@ __global__ __launch_bounds__(512) void attn_partial_bf16(AttnParams P) {
       qf[kk] = as_bf16x8(u);
     }
   }
+  // Complete the Q loads here, on every path into the key loop.  Otherwise the wait for
+  // them lands on the loop's first score product, inside the loop, where it also waits
+  // for the next tile's loads in flight on every iteration.
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) asm volatile("" ::"v"(qf[kk]));
 
   // global -> register fetch of one tile.  Each thread's chunks sit at fixed offsets
   // from the tile's first row (computed once); on a run's ragged last tile the rows past
