@@ -250,6 +250,7 @@ __global__ __launch_bounds__(512) void attn_bwd_dkdv_bf16(BwdParams P) {
 
   uint4 rq[T::RPT], rg[T::RPT], rqt[T::TPT], rgt[T::TPT];
   float rl = 0.f;
+  bool rl_ok = false;
   auto fetch = [&](const TileCursor& c) {
     const int64_t start = c.start + c.k0;
     const int nv = min(T::QT, c.len - c.k0);
@@ -276,12 +277,13 @@ __global__ __launch_bounds__(512) void attn_bwd_dkdv_bf16(BwdParams P) {
         rgt[i] = load_tr_chunk(dOt + dd * P.np, start + 8 * c8, 8 * c8, nv);
       }
     }
+    // L and Delta of the tile's rows: loaded raw (rows past the run's end read the tile's
+    // first row) and turned into their staged values only at the stash, so no
+    // instruction here waits for the loads in flight
     if (tid < 2 * T::QT) {
       const int r = tid & (T::QT - 1);
-      if (tid < T::QT)
-        rl = r < nv ? L[start + r] * kLog2e : INFINITY;
-      else
-        rl = r < nv ? Dl[start + r] : 0.f;
+      rl_ok = r < nv;
+      rl = (tid < T::QT ? L : Dl)[start + (rl_ok ? r : 0)];
     }
   };
   auto stash = [&](int stage) {
@@ -309,7 +311,12 @@ __global__ __launch_bounds__(512) void attn_bwd_dkdv_bf16(BwdParams P) {
         *reinterpret_cast<uint4*>(gts + dd * T::TSTR + c8 * 8) = rgt[i];
       }
     }
-    if (tid < 2 * T::QT) ls[tid] = rl;
+    if (tid < 2 * T::QT) {
+      if (tid < T::QT)
+        ls[tid] = rl_ok ? rl * kLog2e : INFINITY;
+      else
+        ls[tid] = rl_ok ? rl : 0.f;
+    }
   };
 
   f32x16 dk[NDT], dv[NDT];
