@@ -51,7 +51,7 @@ def kernel_source_hash():
 
 def measured_traffic(kernel_hash, units_per_launch):
     """HBM bytes per launch from the committed rocprofv3 PMC summary, if it matches this kernel."""
-    path = os.path.join(ROOT, "profiles", "attn_partial_bf16_d128_n57344_h8_l3_traffic.json")
+    path = TRAFFIC_RECORD
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -59,6 +59,59 @@ def measured_traffic(kernel_hash, units_per_launch):
     if rec.get("kernel_source_sha256_16") != kernel_hash:
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "attn_partial_bf16_d128_n57344_h8_l3_traffic.json")
+
+
+def traffic_record(fetch_csv, write_csv, kernel_hash):
+    """HBM traffic record of the partial and merge kernels from two rocprofv3 counter runs.
+
+    fetch_csv / write_csv: `run_counter_collection.csv` of a `--pmc FETCH_SIZE` and of a
+    `--pmc WRITE_SIZE` run of this script with --calib-copy (KiB per dispatch).  Each
+    counter is scaled by what it reads for the 1 GiB calibration copy (1 GiB read and
+    1 GiB written), then averaged over the launches of each kernel.
+    """
+    import csv
+
+    def per_kernel(path, counter):
+        calib, part, merge = [], [], []
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] != counter:
+                    continue
+                value, name = float(row["Counter_Value"]), row["Kernel_Name"]
+                if "copyBuffer" in name and value > 1000.0:
+                    calib.append(value)
+                elif "attn_partial_bf16<128>" in name:
+                    part.append(value)
+                elif "merge_partials<128" in name:
+                    merge.append(value)
+        if not calib or not part or not merge:
+            raise ValueError(f"{path}: needs the calibration copy and both kernels under {counter}")
+        return calib[0], part, merge
+
+    cf, fetch, mfetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    cw, write, mwrite = per_kernel(write_csv, "WRITE_SIZE")
+    fscale, wscale = GiB / (cf * 1024.0), GiB / (cw * 1024.0)
+    mean = lambda xs: sum(xs) / len(xs)  # noqa: E731
+    read_b = mean(fetch) * 1024.0 * fscale
+    write_b = mean(write) * 1024.0 * wscale
+    merge_b = mean(mfetch) * 1024.0 * fscale + mean(mwrite) * 1024.0 * wscale
+    return {
+        "kernel": "attn_partial_bf16<128>",
+        "workload": "N=57344, H=8, d=128, bf16, CQS l=3, device-resident (one launch per step)",
+        "kernel_source_sha256_16": kernel_hash,
+        "fetch_size_kib_per_launch": fetch,
+        "write_size_kib_per_launch": write,
+        "calibration": {"kernel": "__amd_rocclr_copyBuffer (1 GiB device copy: 1 GiB read, 1 GiB written)",
+                        "fetch_size_kib": cf, "write_size_kib": cw,
+                        "fetch_scale": round(fscale, 5), "write_scale": round(wscale, 5)},
+        "hbm_bytes_read_per_launch": int(round(read_b)),
+        "hbm_bytes_written_per_launch": int(round(write_b)),
+        "hbm_bytes_per_launch": int(round(read_b + write_b)),
+        "merge": {"fetch_size_kib": mfetch, "write_size_kib": mwrite, "hbm_bytes_per_launch": int(round(merge_b))},
+    }
 
 
 def cpu_baseline(rows_wanted=1024):
@@ -293,7 +346,16 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=8192)
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one plain device copy of 1 GiB first (reference for HBM traffic counters)")
+    ap.add_argument("--traffic-record", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the traffic record from two rocprofv3 counter CSVs and exit (no GPU use)")
     args = ap.parse_args()
+    if args.traffic_record:
+        rec = traffic_record(args.traffic_record[0], args.traffic_record[1], kernel_source_hash())
+        with open(TRAFFIC_RECORD, "w") as f:
+            json.dump(rec, f, indent=2)
+            f.write("\n")
+        print(json.dumps(rec))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path",
               file=sys.stderr)

@@ -1,0 +1,49 @@
+"""Host logic of the bench's HBM-traffic record (no GPU): the counters of each kernel are
+scaled by what the same counter reads for a 1 GiB calibration copy, then averaged over
+launches."""
+import csv
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+FIELDS = ["Counter_Name", "Kernel_Name", "Counter_Value"]
+
+
+def _csv(path, counter, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=FIELDS)
+        w.writeheader()
+        for name, value in rows:
+            w.writerow({"Counter_Name": counter, "Kernel_Name": name, "Counter_Value": value})
+
+
+def test_traffic_record_scales_by_the_calibration_copy(tmp_path):
+    part = "void cqsa::(anonymous namespace)::attn_partial_bf16<128>(cqsa::(anonymous namespace)::AttnParams)"
+    merge = "void cqsa::(anonymous namespace)::merge_partials<128, unsigned short>(cqsa::(anonymous namespace)::MergeParams)"
+    copy = "__amd_rocclr_copyBuffer"
+    # FETCH_SIZE reads half of the bytes (factor 2), WRITE_SIZE all of them
+    _csv(tmp_path / "f.csv", "FETCH_SIZE", [(copy, 524288.0), (copy, 12.0), (part, 1000.0), (part, 1002.0),
+                                             (merge, 300.0), (merge, 300.0)])
+    _csv(tmp_path / "w.csv", "WRITE_SIZE", [(copy, 1048576.0), (part, 700.0), (part, 700.0),
+                                             (merge, 100.0), (merge, 102.0)])
+    rec = bench.traffic_record(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), "0123456789abcdef")
+    assert rec["calibration"]["fetch_scale"] == 2.0 and rec["calibration"]["write_scale"] == 1.0
+    assert rec["hbm_bytes_read_per_launch"] == 1001 * 1024 * 2
+    assert rec["hbm_bytes_written_per_launch"] == 700 * 1024
+    assert rec["hbm_bytes_per_launch"] == (1001 * 2 + 700) * 1024
+    assert rec["merge"]["hbm_bytes_per_launch"] == (300 * 2 + 101) * 1024
+    assert rec["kernel_source_sha256_16"] == "0123456789abcdef"
+
+
+def test_traffic_record_needs_the_calibration_copy(tmp_path):
+    _csv(tmp_path / "f.csv", "FETCH_SIZE", [("attn_partial_bf16<128>", 1.0), ("merge_partials<128", 1.0)])
+    _csv(tmp_path / "w.csv", "WRITE_SIZE", [("attn_partial_bf16<128>", 1.0), ("merge_partials<128", 1.0)])
+    with pytest.raises(ValueError):
+        bench.traffic_record(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), "x")
+
