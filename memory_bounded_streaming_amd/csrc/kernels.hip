@@ -185,6 +185,9 @@ __global__ __launch_bounds__(512) void attn_partial_bf16(AttnParams P) {
   __syncthreads();
 
   while (cur.run < nrun) {
+    // Scheduling hint: the backend's MFMA/LDS interleaving for a single wave's tile loop
+    // (measured 1.8 % faster here, identical bits).
+    __builtin_amdgcn_iglp_opt(1);
     const int nv = min(T::KT, cur.len - cur.k0);
     const u16* ks = reinterpret_cast<const u16*>(smem + stage * T::STAGE);
     const u16* vs = reinterpret_cast<const u16*>(smem + stage * T::STAGE + T::KBYTES);
