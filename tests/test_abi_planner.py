@@ -340,3 +340,24 @@ def test_causal_schedule_and_coverage_bit_exact(levels, n):
         lower = np.tril(np.ones((u, u), dtype=bool))
         assert (cov[lower] >= 0).all() and (cov[~lower] == -1).all()
         assert p.info["useful_flop"] == pytest.approx(2.0 * n * (n + 1) * 64 * 2)
+
+
+def test_last_error_is_per_thread(lib):
+    """Each thread reads back the message of its own last failure."""
+    import threading
+    results = {}
+
+    def worker(tag, l):
+        try:
+            cqsa.cqsa_difference_set(l)
+        except cqsa.CqsaError:
+            pass
+        results[tag] = cqsa.cqsa_last_error()
+
+    threads = [threading.Thread(target=worker, args=(i, l)) for i, l in enumerate((7, 0, 7, 11))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert "l=7" in results[0] and results[2] == results[0]
+    assert "1..10" in results[1] and results[3] == results[1]

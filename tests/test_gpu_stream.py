@@ -127,3 +127,36 @@ def test_host_pinned_residency_rejects_device_and_pageable_buffers():
         p.forward(*pins, to, lse, residency=cqsa.CQSA_RES_HOST_PINNED)
         o_dev, _ = _device_forward(p, q, k, v, n, h, d, "bf16")
         assert np.array_equal(oa, o_dev)
+
+
+def test_concurrent_first_calls_on_one_plan():
+    """Two threads make the first forward calls on one plan at once, each on its own stream
+    (both race to upload the plan's descriptor tables); both outputs equal a later
+    sequential call bit for bit."""
+    import threading
+    torch = pytest.importorskip("torch")
+    n, h, d = 7 * 96, 2, 128
+    q, k, v = gen_qkv(11, n, h, d, "bf16")
+    qd, kd, vd = (to_device(x, "bf16") for x in (q, k, v))
+    with cqsa.Plan(n, h, d, cqsa.CQSA_BF16, [3]) as p:
+        outs = [empty_device((n, h, d), "bf16") for _ in range(2)]
+        streams = [torch.cuda.Stream() for _ in range(2)]
+        errors = []
+
+        def worker(i):
+            try:
+                with torch.cuda.stream(streams[i]):
+                    p.forward(qd, kd, vd, outs[i], None, stream=streams[i])
+                streams[i].synchronize()
+            except Exception as e:  # reported below
+                errors.append(e)
+
+        threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+        for t in threads:
+            t.start()
+        for t in threads:
+            t.join()
+        assert not errors, errors
+        o_seq, _ = _device_forward(p, q, k, v, n, h, d, "bf16")
+    for o in outs:
+        assert np.array_equal(to_numpy(o, "bf16"), o_seq)
