@@ -1,16 +1,22 @@
-"""Benchmark of the CQS attention forward on one MI355X.
+"""Benchmark of the CQS-streamed attention forward on one MI355X.
 
-A step is one pass of the whole hot path over the workload: the masked attention
-partials of every CQS task followed by the merge into O and LSE.  The default
-workload is N=57344 tokens, 8 heads, d=128, bf16, CQS l=3 (7 chunks of 8192),
-Q/K/V resident in HBM (inputs are resident before the timed region starts).
+A step is one call of the whole hot path on the 8 GiB streamed workload: N=1,376,256
+tokens, 8 heads, d=128, bf16, CQS l=5 (21 chunks of 65,536), Q/K/V/O/LSE in pinned host
+memory and a device-memory budget of 8 GiB.  Every step gathers each task's K/V segments
+and Q blocks into device staging (hipMemcpyAsync, double buffered), runs the masked
+attention partials, merges them into the accumulator (kept in pinned host memory under
+this budget, with round trips) and returns O and LSE -- the inputs are resident in host
+memory before the timed region starts, as the method keeps them.
 
-Prints one JSON line: useful attention TFLOP/s (4 N^2 d H per step), the fraction
-of the bf16 dense MFMA peak, the roofline of the partial kernel (its average launch
-duration measured with HIP events on the stream it runs on), the fp64 oracle timed
-on a bounded sample of host cores, and the host-pinned streamed run of the
-N=212992, 16-head workload under a 16 GiB budget (PCIe-inclusive, reported beside
-the value, never as it).
+Prints one JSON line: useful attention TFLOP/s (4 N^2 d H per step) and its fraction of
+the bf16 dense MFMA peak, the roofline of the partial kernel (its launches timed with HIP
+events on the stream it runs on, inside the timed calls), the stream phases' rates while
+copying against the pinned-copy rate measured on the box, the merge kernel against HBM,
+peak device memory (modelled and observed) against the budget, the forward error on
+sampled rows against the fp64 oracle, and the oracle itself timed on those rows on the
+host's cores.  Secondary keys: the device-resident N=57,344 workload, its backward, the
+16 GiB streamed workload (N=212,992, 16 heads) and its backward, and the billion-token
+dry run priced with this run's rates.
 """
 import argparse
 import hashlib
@@ -33,7 +39,9 @@ WORKLOADS = {
     # name: (N, H, d, levels, budget, residency description)
     "device_n57344": (57344, 8, 128, [3], 0, "device"),
     "pinned_n212992": (212992, 16, 128, [4], 16 * GiB, "host_pinned"),
+    "pinned_n1376256": (1376256, 8, 128, [5], 8 * GiB, "host_pinned"),
 }
+HEADLINE = "pinned_n1376256"
 
 
 def log(msg):
@@ -49,9 +57,9 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel_hash, units_per_launch):
-    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it matches this kernel."""
-    path = TRAFFIC_RECORD
+def measured_traffic(kernel_hash, record):
+    """HBM bytes per launch from a committed rocprofv3 PMC record, if it matches this kernel."""
+    path = TRAFFIC_RECORDS[record]
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -61,10 +69,18 @@ def measured_traffic(kernel_hash, units_per_launch):
     return rec.get("hbm_bytes_per_launch")
 
 
-TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "attn_partial_bf16_d128_n57344_h8_l3_traffic.json")
+TRAFFIC_RECORDS = {
+    "device_n57344": os.path.join(ROOT, "profiles", "attn_partial_bf16_d128_n57344_h8_l3_traffic.json"),
+    "pinned_n1376256": os.path.join(ROOT, "profiles", "attn_partial_bf16_d128_n1376256_h8_l5_traffic.json"),
+}
+TRAFFIC_WORKLOADS = {
+    "device_n57344": "N=57344, H=8, d=128, bf16, CQS l=3, device-resident (one launch per step)",
+    "pinned_n1376256": "N=1376256, H=8, d=128, bf16, CQS l=5, pinned host memory, 8 GiB budget "
+                       "(105 launches per step, one per (task, query unit))",
+}
 
 
-def traffic_record(fetch_csv, write_csv, kernel_hash):
+def traffic_record(fetch_csv, write_csv, kernel_hash, workload=TRAFFIC_WORKLOADS["device_n57344"]):
     """HBM traffic record of the partial and merge kernels from two rocprofv3 counter runs.
 
     fetch_csv / write_csv: `run_counter_collection.csv` of a `--pmc FETCH_SIZE` and of a
@@ -100,7 +116,8 @@ def traffic_record(fetch_csv, write_csv, kernel_hash):
     merge_b = mean(mfetch) * 1024.0 * fscale + mean(mwrite) * 1024.0 * wscale
     return {
         "kernel": "attn_partial_bf16<128>",
-        "workload": "N=57344, H=8, d=128, bf16, CQS l=3, device-resident (one launch per step)",
+        "workload": workload,
+        "launches": len(fetch),
         "kernel_source_sha256_16": kernel_hash,
         "fetch_size_kib_per_launch": fetch,
         "write_size_kib_per_launch": write,
@@ -114,28 +131,71 @@ def traffic_record(fetch_csv, write_csv, kernel_hash):
     }
 
 
-def cpu_baseline(rows_wanted=1024):
-    """The fp64 oracle on a bounded sample of the N=57344, 8-head workload (all keys, sampled query rows)."""
-    from memory_bounded_streaming_amd.inputs import gen_qkv, sample_rows
-    from oracle.attention import attention_fp64
+def copy_summary(trace_csv):
+    """Host-to-device and device-to-host busy time from a rocprofv3 memory-copy trace.
+
+    For each direction: the number of copies, the union of their [start, end] intervals
+    (copies on several streams at once count once) and the span from the first start to
+    the last end, in ms.  Byte counts are not in the trace; the engine's counters give them.
+    """
+    import csv
+    iv = {"h2d": [], "d2h": []}
+    with open(trace_csv) as f:
+        for row in csv.DictReader(f):
+            direction = (row.get("Direction") or "").upper()
+            key = "h2d" if "HOST_TO_DEVICE" in direction else "d2h" if "DEVICE_TO_HOST" in direction else None
+            if key is None:
+                continue
+            iv[key].append((int(row["Start_Timestamp"]), int(row["End_Timestamp"])))
+    out = {}
+    for key, xs in iv.items():
+        xs.sort()
+        busy, cb, ce = 0, None, None
+        for b, e in xs:
+            if ce is not None and b <= ce:
+                ce = max(ce, e)
+                continue
+            if ce is not None:
+                busy += ce - cb
+            cb, ce = b, e
+        if ce is not None:
+            busy += ce - cb
+        out[key] = {"copies": len(xs), "busy_ms": busy / 1e6,
+                    "span_ms": (xs[-1][1] - xs[0][0]) / 1e6 if xs else 0.0}
+    return out
+
+
+def blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        return max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:
-        threads = len(os.sched_getaffinity(0))
-    n, h, d = 57344, 8, 128
-    q, k, v = gen_qkv(0, n, h, d, "bf16")
-    rows = sample_rows(n, rows_wanted, 0)
+        return len(os.sched_getaffinity(0))
+
+
+def oracle_check(q, k, v, o_bits, lse, rows_wanted, seed):
+    """The fp64 oracle on sampled rows of a workload (all keys): its time on the host's
+    cores (the cpu_baseline) and the GPU output's error on those rows."""
+    from memory_bounded_streaming_amd.inputs import bf16_bits_to_f32, sample_rows
+    from oracle.attention import attention_fp64
+    from oracle.tolerance import error_report
+    n, h, d = q.shape
+    rows = sample_rows(n, rows_wanted, seed)
     t0 = time.perf_counter()
-    attention_fp64(q, k, v, rows=rows, dtype="bf16")
+    o_ref, lse_ref = attention_fp64(q, k, v, rows=rows, dtype="bf16")
     dt = time.perf_counter() - t0
     flop = 4.0 * rows.size * n * d * h
-    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{rows.size} sampled query rows x {h} heads of the N={n}, d={d} workload against all "
-                      f"{n} keys, fp64 two-pass softmax; {dt:.1f} s wall; rate = 4*rows*N*d*H / time",
-            "sample_wall_s": round(dt, 2),
-            "extrapolated_full_n_s": round(dt * n / rows.size, 1),
-            "extrapolation": f"sample wall x N/rows = time for all {n} query rows (not measured)"}
+    cpu = {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads()), "kind": "oracle",
+           "sample": f"{rows.size} seeded sampled query rows x {h} heads of the N={n}, d={d} workload against "
+                     f"all {n} keys, fp64 two-pass softmax; {dt:.1f} s wall; rate = 4*rows*N*d*H / time",
+           "sample_wall_s": round(dt, 2),
+           "extrapolated_full_n_s": round(dt * n / rows.size, 1),
+           "extrapolation": f"sample wall x N/rows = time for all {n} query rows (not measured)"}
+    rep = error_report(bf16_bits_to_f32(o_bits[rows]).astype(np.float64), o_ref)
+    err = {"rows": int(rows.size), "heads": h, "reference": "dense fp64 oracle on the same bf16 inputs",
+           "max_abs": rep["max_abs"], "mean_abs": rep["mean_abs"], "rowwise_rel": rep["rowwise_rel"],
+           "lse_max_abs": float(np.abs(lse[:, rows] - lse_ref).max())}
+    return cpu, err
 
 
 def run_device(args, torch, cqsa):
@@ -290,14 +350,103 @@ def pcie_achievable(torch, nbytes=512 << 20, reps=5):
     return out
 
 
-def run_streamed(args, torch, cqsa):
+def pinned_inputs(torch, seed, n, h, d, count=3):
+    """Q, K, V (and dO for count=4) drawn straight into pinned host memory."""
     from memory_bounded_streaming_amd.inputs import gen_tensor
-    n, h, d, levels, budget, _ = WORKLOADS["pinned_n212992"]
     ts = []
-    for i in range(3):
+    for i in range(count):
         t = torch.empty((n, h, d), dtype=torch.int16, pin_memory=True)
-        gen_tensor(args.seed, i, n, h, d, "bf16", out=t.numpy().view(np.uint16))
+        gen_tensor(seed, i, n, h, d, "bf16", out=t.numpy().view(np.uint16))
         ts.append(t)
+    return ts
+
+
+def phase_rates(st, pcie):
+    """Rates of the stream phases while copying (bytes / busy time) and their fraction of the
+    pinned-copy rate measured on the box."""
+    h2d = st["bytes_h2d"] / (st["t_h2d_ms"] / 1e3) / 1e9 if st["t_h2d_ms"] else None
+    d2h = st["bytes_d2h"] / (st["t_d2h_ms"] / 1e3) / 1e9 if st["t_d2h_ms"] else None
+    return {
+        "h2d_gbs": h2d, "d2h_gbs": d2h,
+        "h2d_busy_ms": st["t_h2d_ms"], "d2h_busy_ms": st["t_d2h_ms"],
+        "h2d_achievable_gbs": pcie["h2d_gbs"], "d2h_achievable_gbs": pcie["d2h_gbs"],
+        "h2d_frac_of_achievable": h2d / pcie["h2d_gbs"] if h2d else None,
+        "d2h_frac_of_achievable": d2h / pcie["d2h_gbs"] if d2h else None,
+        "bytes_h2d": st["bytes_h2d"], "bytes_d2h": st["bytes_d2h"], "bytes_d2d_chunk_reuse": st["bytes_d2d"],
+        "copies_h2d": st["n_h2d_copies"], "copies_d2h": st["n_d2h_copies"],
+        "rate_note": "bytes / union of the phase's event-timed copy intervals over its streams",
+    }
+
+
+def run_headline(args, torch, cqsa):
+    """The streamed forward at a fixed 8 GiB budget: warm-up calls, then exactly
+    args.steps timed calls of cqsa_forward (synchronous) with Q/K/V resident in pinned
+    host memory.  The first call runs on a fresh plan with a library-allocated workspace,
+    so its observed peak covers every device byte the call holds."""
+    n, h, d, levels, budget, _ = WORKLOADS[HEADLINE]
+    log(f"bench: drawing the N={n} workload into pinned memory")
+    q, k, v = pinned_inputs(torch, args.seed, n, h, d)
+    o = torch.empty((n, h, d), dtype=torch.int16, pin_memory=True)
+    lse = torch.empty((h, n), dtype=torch.float32, pin_memory=True)
+    plan = cqsa.Plan(n, h, d, cqsa.CQSA_BF16, levels, budget_bytes=budget)
+    info = plan.info
+
+    def call():
+        return plan.forward(q, k, v, o, lse, residency=cqsa.CQSA_RES_HOST_PINNED, stats=True)
+
+    first = None
+    for i in range(args.warmup):
+        st = call()
+        first = first or st
+        log(f"bench: warm-up call {i + 1}/{args.warmup}: {st['t_total_ms'] / 1e3:.2f} s")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    timed = []
+    for i in range(args.steps):
+        timed.append(call())
+        log(f"bench: timed call {i + 1}/{args.steps}: {timed[-1]['t_total_ms'] / 1e3:.2f} s")
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    first = first or timed[0]
+    flop = info["useful_flop"]
+    ms = wall / args.steps * 1e3
+    attn_ms = float(np.mean([st["t_attn_ms"] for st in timed]))
+    merge_ms = float(np.mean([st["t_merge_ms"] for st in timed]))
+    launches = timed[0]["n_attn_launches"]
+    est = cqsa.cqsa_plan_estimate(n, h, d, cqsa.CQSA_BF16, levels, budget_bytes=budget,
+                                  rates={"attn_tflops": 1.0, "merge_gbs": 1.0, "h2d_gbs": 1.0, "d2h_gbs": 1.0})
+    merge_bytes = est["merge_bytes"]
+    pcie = pcie_achievable(torch)
+    last = timed[-1]
+    rates = phase_rates(last, pcie)
+    rates["h2d_gbs_mean"] = float(np.mean([st["bytes_h2d"] / st["t_h2d_ms"] / 1e6 for st in timed]))
+    rates["d2h_gbs_mean"] = float(np.mean([st["bytes_d2h"] / st["t_d2h_ms"] / 1e6 for st in timed]))
+    out = {
+        "plan": info, "ms_per_step": ms, "value": flop / (ms / 1e3) / 1e12,
+        "attn_ms": attn_ms, "attn_launches": launches, "attn_tflops": flop / (attn_ms / 1e3) / 1e12,
+        "merge_ms": merge_ms, "merge_bytes": merge_bytes, "merge_gbs": merge_bytes / (merge_ms / 1e3) / 1e9,
+        "merge_launches": timed[0]["n_merge_launches"], "stream": rates,
+        "memory": {"budget_bytes": budget, "peak_device_bytes_modelled": first["peak_device_bytes"],
+                   "peak_device_bytes_observed": first["observed_peak_bytes"],
+                   "device_free_at_entry": first["device_free_at_entry"],
+                   "stream_workspace_bytes": info["stream_workspace_bytes"],
+                   "host_accumulator_bytes": info["host_acc_bytes"],
+                   "observed_note": "hipMemGetInfo free memory at entry minus its minimum over the first call "
+                                    "(fresh plan, library-allocated workspace)"},
+        "calls_s": [round(st["t_total_ms"] / 1e3, 3) for st in timed],
+    }
+    if not args.no_cpu_baseline:
+        log(f"bench: oracle on {args.cpu_rows} sampled rows of the N={n} workload")
+        qn, kn, vn = (t.numpy().view(np.uint16) for t in (q, k, v))
+        out["cpu_baseline"], out["error"] = oracle_check(qn, kn, vn, o.numpy().view(np.uint16), lse.numpy(),
+                                                         args.cpu_rows, args.seed)
+    plan.close()
+    return out
+
+
+def run_streamed(args, torch, cqsa):
+    n, h, d, levels, budget, _ = WORKLOADS["pinned_n212992"]
+    ts = pinned_inputs(torch, args.seed, n, h, d)
     o = torch.empty((n, h, d), dtype=torch.int16, pin_memory=True)
     lse = torch.empty((h, n), dtype=torch.float32, pin_memory=True)
     with cqsa.Plan(n, h, d, cqsa.CQSA_BF16, levels, budget_bytes=budget) as plan:
@@ -308,8 +457,6 @@ def run_streamed(args, torch, cqsa):
         wall = time.perf_counter() - t0
         flop = plan.info["useful_flop"]
         pcie = pcie_achievable(torch)
-        h2d = st["bytes_h2d"] / (st["t_h2d_ms"] / 1e3) / 1e9 if st["t_h2d_ms"] else None
-        d2h = st["bytes_d2h"] / (st["t_d2h_ms"] / 1e3) / 1e9 if st["t_d2h_ms"] else None
         return {
             "workload": f"N={n}, H={h}, d={d}, bf16, CQS l={levels[0]} (c=13), Q/K/V in pinned host memory, "
                         f"device budget {budget // GiB} GiB",
@@ -317,17 +464,9 @@ def run_streamed(args, torch, cqsa):
             "tflops_pcie_inclusive": flop / wall / 1e12,
             "wall_s": wall,
             "attn_tflops": flop / (st["t_attn_ms"] / 1e3) / 1e12,
-            "h2d_gbs": h2d,
-            "d2h_gbs": d2h,
-            "h2d_achievable_gbs": pcie["h2d_gbs"],
-            "d2h_achievable_gbs": pcie["d2h_gbs"],
-            "h2d_frac_of_achievable": h2d / pcie["h2d_gbs"] if h2d else None,
-            "d2h_frac_of_achievable": d2h / pcie["d2h_gbs"] if d2h else None,
             "merge_ms": st["t_merge_ms"],
             "attn_ms": st["t_attn_ms"],
-            "bytes_h2d": st["bytes_h2d"],
-            "bytes_d2h": st["bytes_d2h"],
-            "bytes_d2d_chunk_reuse": st["bytes_d2d"],
+            "stream": phase_rates(st, pcie),
             "peak_device_bytes": st["peak_device_bytes"],
             "budget_bytes": budget,
         }
@@ -340,25 +479,42 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-streamed", action="store_true")
+    ap.add_argument("--no-device", action="store_true", help="skip the device-resident N=57344 leg")
+    ap.add_argument("--no-streamed", action="store_true", help="skip the N=212992 streamed leg")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-streamed-backward", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=8192)
+    ap.add_argument("--headline-only", action="store_true", help="run the headline workload and nothing else")
+    ap.add_argument("--device-only", action="store_true",
+                    help="run only the device-resident N=57344 leg (its kernel trace and counters)")
+    ap.add_argument("--cpu-rows", type=int, default=256)
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one plain device copy of 1 GiB first (reference for HBM traffic counters)")
     ap.add_argument("--traffic-record", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic record from two rocprofv3 counter CSVs and exit (no GPU use)")
+    ap.add_argument("--traffic-workload", default=HEADLINE, choices=sorted(TRAFFIC_RECORDS),
+                    help="which workload's record --traffic-record writes")
+    ap.add_argument("--copy-summary", metavar="TRACE_CSV",
+                    help="print the copy busy times of a rocprofv3 memory-copy trace and exit (no GPU use)")
     args = ap.parse_args()
     if args.traffic_record:
-        rec = traffic_record(args.traffic_record[0], args.traffic_record[1], kernel_source_hash())
-        with open(TRAFFIC_RECORD, "w") as f:
+        rec = traffic_record(args.traffic_record[0], args.traffic_record[1], kernel_source_hash(),
+                             TRAFFIC_WORKLOADS[args.traffic_workload])
+        with open(TRAFFIC_RECORDS[args.traffic_workload], "w") as f:
             json.dump(rec, f, indent=2)
             f.write("\n")
         print(json.dumps(rec))
         return
+    if args.copy_summary:
+        print(json.dumps(copy_summary(args.copy_summary)))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path",
               file=sys.stderr)
+        sys.exit(2)
+    if args.headline_only:
+        args.no_device = args.no_streamed = args.no_backward = args.no_streamed_backward = True
+    if args.steps < 1 or args.warmup < 0:
+        print("need --steps >= 1 and --warmup >= 0", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -373,11 +529,22 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         log("bench: calibration copy of 1 GiB done")
-    log("bench: device-resident workload")
-    dres = run_device(args, torch, cqsa)
-    log(f"bench: {dres['value']:.1f} TFLOP/s end-to-end, partial kernel {dres['attn_tflops']:.1f} TFLOP/s")
+    if args.device_only:
+        log("bench: device-resident workload only")
+        dres = run_device(args, torch, cqsa)
+        print(json.dumps({"device_resident": dres}), flush=True)
+        return
+
+    log("bench: headline, the streamed N=1376256 workload under 8 GiB")
+    head = run_headline(args, torch, cqsa)
+    log(f"bench: {head['value']:.1f} TFLOP/s end-to-end, partial kernel {head['attn_tflops']:.1f} TFLOP/s")
+    dres = None
+    if not args.no_device:
+        log("bench: device-resident workload")
+        dres = run_device(args, torch, cqsa)
+        log(f"bench: device-resident {dres['value']:.1f} TFLOP/s, partial kernel {dres['attn_tflops']:.1f} TFLOP/s")
     bwd = None
-    if not args.no_backward:
+    if not args.no_backward and dres is not None:
         log("bench: backward of the device-resident workload")
         bwd = run_backward(args, torch, cqsa)
         bwd["fwd_bwd_ratio"] = round((bwd["ms_per_step"] + dres["ms_per_step"]) / dres["ms_per_step"], 3)
@@ -385,7 +552,7 @@ def main():
         log(f"bench: backward {bwd['tflops_useful']:.1f} useful TFLOP/s, {bwd['ms_per_step']:.2f} ms")
     stream_res = None
     if not args.no_streamed:
-        log("bench: host-pinned streamed workload")
+        log("bench: host-pinned streamed N=212992 workload")
         stream_res = run_streamed(args, torch, cqsa)
         log(f"bench: streamed {stream_res['tflops_pcie_inclusive']:.1f} TFLOP/s PCIe-inclusive")
     sbwd = None
@@ -396,8 +563,8 @@ def main():
     dry = None
     if stream_res is not None:
         # the billion-token case priced with this run's measured rates (plan-only, no data)
-        rates = {"attn_tflops": dres["attn_tflops"], "merge_gbs": dres["merge_gbs"],
-                 "h2d_gbs": stream_res["h2d_achievable_gbs"], "d2h_gbs": stream_res["d2h_achievable_gbs"]}
+        rates = {"attn_tflops": head["attn_tflops"], "merge_gbs": head["merge_gbs"],
+                 "h2d_gbs": head["stream"]["h2d_achievable_gbs"], "d2h_gbs": head["stream"]["d2h_achievable_gbs"]}
         dry = []
         for budget in (16 * GiB, 2 * GiB):
             e = cqsa.cqsa_plan_estimate(1 << 30, 1, 128, cqsa.CQSA_BF16, [3], n_levels=0, budget_bytes=budget,
@@ -415,51 +582,69 @@ def main():
                 dry[-1]["bwd_hours_by_ratio"] = round(e["t_est_s"] * ratio / 3600, 1)
                 dry[-1]["bwd_ratio_note"] = (f"extrapolation: forward estimate x {ratio:.2f}, the measured streamed "
                                              "backward / forward time of the N=212992, 16-head workload")
-    cpu = None
-    if not args.no_cpu_baseline:
-        log("bench: oracle cpu baseline")
-        cpu = cpu_baseline(args.cpu_rows)
 
-    n, h, d, levels, _, _ = WORKLOADS["device_n57344"]
-    flop = dres["plan"]["useful_flop"]
+    n, h, d, levels, budget, _ = WORKLOADS[HEADLINE]
     khash = kernel_source_hash()
-    traffic = measured_traffic(khash, 1)
+    flop = head["plan"]["useful_flop"]
+    device_resident = None
+    if dres is not None:
+        device_resident = {
+            "workload": "N=57344, 8 heads, d=128, bf16, CQS l=3 (c=7 chunks of 8192), Q/K/V device-resident",
+            "tflops": round(dres["value"], 3), "ms_per_step": round(dres["ms_per_step"], 4),
+            "roofline": {"bound": "mfma", "kernel": "attn_partial_bf16<128>",
+                         "achieved": round(dres["attn_tflops"], 3), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(dres["attn_tflops"] / BF16_MFMA_PEAK_TFLOPS, 4),
+                         "traffic": measured_traffic(khash, "device_n57344"),
+                         "flop_per_launch": dres["plan"]["useful_flop"], "avg_launch_ms": round(dres["attn_ms"], 4)},
+            "merge": {"bound": "hbm", "achieved": round(dres["merge_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": round(dres["merge_gbs"] / HBM_PEAK_GBS, 4), "bytes_per_launch": dres["merge_bytes"],
+                      "avg_launch_ms": round(dres["merge_ms"], 4)},
+        }
     line = {
         "metric": METRIC,
-        "value": round(dres["value"], 3),
+        "value": round(head["value"], 3),
         "unit": "TFLOP/s",
-        "pct_bf16_mfma_peak": round(100.0 * dres["value"] / BF16_MFMA_PEAK_TFLOPS, 3),
+        "pct_bf16_mfma_peak": round(100.0 * head["value"] / BF16_MFMA_PEAK_TFLOPS, 3),
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(dres["ms_per_step"], 4),
+        "ms_per_step": round(head["ms_per_step"], 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic: Q/K/V i.i.d. N(0,1) rounded to bf16, seed %d" % args.seed,
         "config": {"workload": f"N={n} tokens, {h} heads, d={d}, bf16, non-causal, CQS l={levels[0]} "
-                               f"(c=7 chunks of 8192), Q/K/V device-resident",
-                   "n_tokens": n, "heads": h, "head_dim": d, "levels": levels, "residency": "device"},
+                               f"(c=21 chunks of 65536), Q/K/V/O/LSE in pinned host memory, "
+                               f"device budget {budget // GiB} GiB (CQS-streamed forward)",
+                   "n_tokens": n, "heads": h, "head_dim": d, "levels": levels, "residency": "host_pinned",
+                   "budget_bytes": budget, "stream_mode": cqsa.MODE_NAMES[head["plan"]["stream_mode"]]},
         "roofline": {
             "bound": "mfma",
             "kernel": "attn_partial_bf16<128>",
-            "achieved": round(dres["attn_tflops"], 3),
+            "achieved": round(head["attn_tflops"], 3),
             "peak": BF16_MFMA_PEAK_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": round(dres["attn_tflops"] / BF16_MFMA_PEAK_TFLOPS, 4),
-            "traffic": traffic,
-            "flop_per_launch": flop,
-            "avg_launch_ms": round(dres["attn_ms"], 4),
+            "frac": round(head["attn_tflops"] / BF16_MFMA_PEAK_TFLOPS, 4),
+            "traffic": measured_traffic(khash, HEADLINE),
+            "launches_per_step": head["attn_launches"],
+            "flop_per_launch": flop / head["attn_launches"],
+            "avg_launch_ms": round(head["attn_ms"] / head["attn_launches"], 4),
         },
-        "merge": {"bound": "hbm", "achieved": round(dres["merge_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                  "frac": round(dres["merge_gbs"] / HBM_PEAK_GBS, 4), "bytes_per_launch": dres["merge_bytes"],
-                  "avg_launch_ms": round(dres["merge_ms"], 4)},
-        "streamed": stream_res,
+        "merge": {"bound": "hbm", "achieved": round(head["merge_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                  "frac": round(head["merge_gbs"] / HBM_PEAK_GBS, 4), "bytes_per_step": head["merge_bytes"],
+                  "launches_per_step": head["merge_launches"],
+                  "avg_launch_ms": round(head["merge_ms"] / head["merge_launches"], 4)},
+        "stream": head["stream"],
+        "memory": head["memory"],
+        "error": head.get("error"),
+        "cpu_baseline": head.get("cpu_baseline"),
+        "calls_s": head["calls_s"],
+        "device_resident": device_resident,
+        "streamed_16gib": stream_res,
         "backward": bwd,
         "streamed_backward": sbwd,
         "dry_run_1b_tokens": dry,
-        "cpu_baseline": cpu,
         "kernel_source_sha256_16": khash,
     }
     print(json.dumps(line), flush=True)

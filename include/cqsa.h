@@ -76,6 +76,14 @@ typedef enum {
  * unit does not come after the query unit, and the diagonal unit block is masked
  * element by element.  useful_flop becomes 2 N (N+1) d H. */
 #define CQSA_FLAG_CAUSAL 0x8u
+/* Budget from the device: the plan's budget becomes the free memory of the current HIP
+ * device (hipMemGetInfo, read once at plan creation) minus budget_bytes, which is then a
+ * safety margin (>= 0).  "Stream-CQSA: Exact Out-of-Memory Recovery for Attention",
+ * abstract: the attention call is partitioned into subproblems that fit the memory the
+ * device has; the Lattice summary: subproblems fit arbitrary memory budgets.  This is
+ * the one plan_create option that makes a HIP call; EHIP without a usable device,
+ * EBUDGET if the margin exceeds the free memory. */
+#define CQSA_FLAG_FREE_BUDGET 0x10u
 
 #define CQSA_MAX_LEVELS 12
 #define CQSA_MAX_L 10
@@ -105,12 +113,23 @@ typedef struct {
 
 typedef struct {
   double t_total_ms;            /* wall time of the call (host clock) */
-  double t_h2d_ms, t_attn_ms, t_merge_ms, t_d2h_ms; /* summed event-timed durations per phase */
+  /* Busy time of each phase: the union of its event-timed intervals over every stream
+   * that runs it (copies on two streams at once count once), so bytes / time is the
+   * phase's rate while it is active. */
+  double t_h2d_ms, t_attn_ms, t_merge_ms, t_d2h_ms;
   int64_t bytes_h2d, bytes_d2h;
-  int64_t peak_device_bytes;    /* workspace bytes used by the call */
+  int64_t peak_device_bytes;    /* modelled: workspace + descriptor tables of the plan run */
   int64_t n_attn_launches, n_merge_launches, n_h2d_copies, n_d2h_copies;
   double useful_flop;
   int64_t bytes_d2d;            /* K/V rows reused from the previous task's staging buffer */
+  /* Observed: free device memory (hipMemGetInfo) at entry minus its minimum, polled after
+   * every allocation and after each task is enqueued.  Device memory the library or the
+   * caller held before the call (a caller workspace, descriptor tables an earlier call on
+   * the plan uploaded) is not in it. */
+  int64_t observed_peak_bytes;
+  int64_t device_free_at_entry; /* hipMemGetInfo free bytes when the call began */
+  int32_t levels_used;          /* levels of the plan that ran (more than the caller's after a re-plan) */
+  int32_t replans;              /* out-of-memory re-plans made inside the call (host-pinned path) */
 } cqsa_stats;
 
 /* Measured rates a dry run prices a plan with (all > 0). */
@@ -187,7 +206,10 @@ cqsa_status cqsa_plan_create(int64_t n, int32_t heads, int32_t head_dim, cqsa_dt
 cqsa_status cqsa_plan_info_get(const cqsa_plan* plan, cqsa_plan_info* out);
 
 /*
- * Canonical schedule record (int64, host).  Layout:
+ * Canonical schedule record (int64, host): the tasks of the CQS Divide in the order they
+ * run ("The 'CQS Divide'" and "Implementation: From High-Level Logic to GPU Kernels"
+ * sections of the wispaper explainer: subsequence tasks, each a set of chunks, with the
+ * CQS Mask deciding which key ranges each query range of a task computes).  Layout:
  *   n_levels, (c_k, l_k) per level, n_tasks, unit_tokens, n_units, then per task in
  *   ascending id: tid, t_1..t_L, n_segments, (global_start, length, local_offset) per
  *   segment in tokens, n_query_units, and per local query unit: global_unit, n_runs,
@@ -248,7 +270,12 @@ cqsa_status cqsa_merge(const cqsa_plan* plan, const float* n_in, const float* ml
 
 /*
  * Full CQS forward: O = softmax(Q K^T / sqrt(d)) V and LSE, exact up to rounding (with
- * CQSA_FLAG_CAUSAL the softmax runs over keys j <= i).
+ * CQSA_FLAG_CAUSAL the softmax runs over keys j <= i).  "Stream-CQSA: Exact
+ * Out-of-Memory Recovery for Attention", abstract: independent subsequence tasks whose
+ * local statistics recompose into the full output; "Stream-CQSA: Breaking the
+ * Billion-Token Barrier on a Single GPU", section "Implementation: From High-Level Logic
+ * to GPU Kernels": Q_i, K_i, V_i streamed to the GPU, local numerators and denominators,
+ * aggregation in host memory; Lattice summary: subproblems within a memory budget.
  *   CQSA_RES_DEVICE: q, k, v, o, lse are device pointers; runs cqsa_partials then
  *     cqsa_merge on stream using `workspace` (>= cqsa_workspace_size bytes) for the
  *     partial slots.  Stream-ordered: returns after enqueuing unless the library had
@@ -259,11 +286,19 @@ cqsa_status cqsa_merge(const cqsa_plan* plan, const float* n_in, const float* ml
  *     staging with hipMemcpyAsync on copy streams, double-buffered when the mode says
  *     so, query units are streamed in blocks, partials are merged into the
  *     accumulator (device, or pinned host memory with H2D/D2H round trips), and the
- *     finished O/LSE blocks are copied back.  Device memory used is the workspace
- *     (<= budget).  Synchronous: returns after all work is complete.
+ *     finished O blocks are copied back as each unit completes; LSE is kept [H][N] on
+ *     the device for the call and copied back once at the end.  Device memory used is
+ *     the workspace (<= budget).  Synchronous: returns after all work is complete.  If
+ *     the library must allocate the workspace and the device is out of memory, the
+ *     call re-plans one level deeper (cqsa_plan_fallback, budget = free memory minus
+ *     1/16) and retries, up to CQSA_MAX_LEVELS levels; the caller's plan is unchanged.
  * workspace: device buffer or NULL (then the library allocates exactly the size
  *   needed and frees it before returning).  lse may be NULL.
  * stats: optional; when given, phases are timed with HIP events.
+ * Debugging aids (environment, read at each call): CQSA_SYNC=1 waits for the device
+ *   after every step the host-pinned path enqueues (streams effectively serialised);
+ *   CQSA_CANARY=1 surrounds every piece of the host-pinned workspace with guard words
+ *   and checks them after the call (EHIP naming the piece if one was overwritten).
  * Errors: EINVAL, ESMALL, EBUDGET (device path over budget), EHIP, ENOMEM.
  */
 cqsa_status cqsa_forward(const cqsa_plan* plan, const void* q, const void* k, const void* v,
@@ -332,6 +367,33 @@ cqsa_status cqsa_backward(const cqsa_plan* plan, const void* q, const void* k, c
 cqsa_status cqsa_plan_estimate(int64_t n, int32_t heads, int32_t head_dim, cqsa_dtype dtype,
                                const int32_t* l_levels, int32_t n_levels, int64_t budget_bytes,
                                uint32_t flags, const cqsa_rates* rates, cqsa_estimate* out);
+
+/*
+ * The plan the out-of-memory recovery falls back to: one CQS Divide level deeper than
+ * `plan` ("Stream-CQSA: Exact Out-of-Memory Recovery for Attention", abstract: a
+ * memory-capacity failure becomes a recoverable execution path; "The Recursive Benefit"
+ * section of the wispaper explainer: a task that is still too large is divided again).
+ * The new level repeats the l of the plan's innermost level (3 if that l is 1, an
+ * undivided plan); CQSA_FLAG_PAD is added when N no longer divides into the deeper unit
+ * grid (exact: padding is never read).  budget_bytes (> 0) replaces the plan's budget;
+ * if even the deeper plan's footprint exceeds it, further levels are added until one
+ * fits.  Every other property (dtype, causality, flags) is kept.  When the host-pinned
+ * cqsa_forward cannot allocate its device workspace (ENOMEM from the HIP allocator and
+ * no caller workspace), it builds this plan with the device's free memory minus 1/16 as
+ * the budget and runs it inside the same call (stats.replans counts such re-plans).
+ * Host-only.  *out receives a plan the caller frees with cqsa_plan_destroy.  Errors:
+ * EINVAL, EBUDGET (no depth up to CQSA_MAX_LEVELS fits), EDIVIDE (fewer tokens than
+ * units), ENOMEM (the deeper plan is too large to build).
+ */
+cqsa_status cqsa_plan_fallback(const cqsa_plan* plan, int64_t budget_bytes, cqsa_plan** out);
+
+/*
+ * Fault injection for tests of the recovery paths (callers: test suites only).  The
+ * next `count` device allocations the library makes (workspaces, descriptor tables)
+ * fail as if the device were out of memory, without calling the HIP allocator; 0
+ * clears it.  Process-wide.  Errors: EINVAL (count < 0).
+ */
+cqsa_status cqsa_debug_fail_allocations(int32_t count);
 
 /* Static text for a status code. */
 const char* cqsa_status_string(cqsa_status status);

@@ -18,7 +18,8 @@ import numpy as np
 
 __all__ = [
     "CqsaError", "load", "CQSA_BF16", "CQSA_F32", "CQSA_RES_DEVICE", "CQSA_RES_HOST_PINNED",
-    "CQSA_FLAG_HOST_ACC", "CQSA_FLAG_KV_SINGLE", "CQSA_FLAG_PAD", "CQSA_FLAG_CAUSAL", "MODE_NAMES",
+    "CQSA_FLAG_HOST_ACC", "CQSA_FLAG_KV_SINGLE", "CQSA_FLAG_PAD", "CQSA_FLAG_CAUSAL", "CQSA_FLAG_FREE_BUDGET",
+    "MODE_NAMES", "cqsa_plan_fallback", "cqsa_debug_fail_allocations",
     "cqsa_version", "cqsa_difference_set", "cqsa_plan_create", "cqsa_plan_info_get", "cqsa_plan_schedule",
     "cqsa_plan_coverage", "cqsa_plan_destroy", "cqsa_workspace_size", "cqsa_partials", "cqsa_merge",
     "cqsa_forward", "cqsa_backward_workspace_size", "cqsa_backward", "cqsa_plan_estimate", "cqsa_status_string", "cqsa_last_error", "Plan",
@@ -27,6 +28,7 @@ __all__ = [
 CQSA_BF16, CQSA_F32 = 0, 1
 CQSA_RES_DEVICE, CQSA_RES_HOST_PINNED = 0, 1
 CQSA_FLAG_HOST_ACC, CQSA_FLAG_KV_SINGLE, CQSA_FLAG_PAD, CQSA_FLAG_CAUSAL = 0x1, 0x2, 0x4, 0x8
+CQSA_FLAG_FREE_BUDGET = 0x10
 MODE_NAMES = {1: "device_acc_kv2", 2: "host_acc_kv2", 3: "device_acc_kv1", 4: "host_acc_kv1"}
 MAX_LEVELS = 12
 
@@ -62,7 +64,8 @@ class Stats(ctypes.Structure):
         ("bytes_h2d", ctypes.c_int64), ("bytes_d2h", ctypes.c_int64), ("peak_device_bytes", ctypes.c_int64),
         ("n_attn_launches", ctypes.c_int64), ("n_merge_launches", ctypes.c_int64),
         ("n_h2d_copies", ctypes.c_int64), ("n_d2h_copies", ctypes.c_int64), ("useful_flop", ctypes.c_double),
-        ("bytes_d2d", ctypes.c_int64),
+        ("bytes_d2d", ctypes.c_int64), ("observed_peak_bytes", ctypes.c_int64),
+        ("device_free_at_entry", ctypes.c_int64), ("levels_used", ctypes.c_int32), ("replans", ctypes.c_int32),
     ]
 
 
@@ -110,6 +113,8 @@ EXPORTS = {
     "cqsa_plan_estimate": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int,
                                           ctypes.POINTER(ctypes.c_int32), ctypes.c_int32, ctypes.c_int64,
                                           ctypes.c_uint32, ctypes.POINTER(Rates), ctypes.POINTER(Estimate)]),
+    "cqsa_plan_fallback": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(ctypes.c_void_p)]),
+    "cqsa_debug_fail_allocations": (ctypes.c_int, [ctypes.c_int32]),
     "cqsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "cqsa_last_error": (ctypes.c_char_p, []),
 }
@@ -287,12 +292,29 @@ def cqsa_plan_estimate(n: int, heads: int, head_dim: int, dtype: int, l_levels, 
     return d
 
 
+def cqsa_plan_fallback(plan: int, budget_bytes: int) -> int:
+    """Handle of the plan one level deeper under budget_bytes; free it with cqsa_plan_destroy."""
+    out = ctypes.c_void_p()
+    _check(load().cqsa_plan_fallback(plan, budget_bytes, ctypes.byref(out)))
+    return out.value
+
+
+def cqsa_debug_fail_allocations(count: int) -> None:
+    _check(load().cqsa_debug_fail_allocations(count))
+
+
 class Plan:
     """Owning wrapper of a plan handle (the same calls, with the handle bound)."""
 
-    def __init__(self, n, heads, head_dim, dtype, l_levels, n_levels=None, budget_bytes=0, flags=0):
-        self.handle = cqsa_plan_create(n, heads, head_dim, dtype, l_levels, n_levels, budget_bytes, flags)
+    def __init__(self, n, heads, head_dim, dtype, l_levels, n_levels=None, budget_bytes=0, flags=0, handle=None):
+        if handle is None:
+            handle = cqsa_plan_create(n, heads, head_dim, dtype, l_levels, n_levels, budget_bytes, flags)
+        self.handle = handle
         self.info = cqsa_plan_info_get(self.handle)
+
+    def fallback(self, budget_bytes):
+        """The out-of-memory fallback plan (one level deeper) as an owning Plan."""
+        return Plan(None, None, None, None, None, handle=cqsa_plan_fallback(self.handle, budget_bytes))
 
     def schedule(self):
         return cqsa_plan_schedule(self.handle)

@@ -44,6 +44,24 @@ bool aligned16(std::initializer_list<const void*> ps) {
 
 constexpr const char* kAlignWhy = "device tensors and workspaces must start on a 16-byte boundary (lse on a 4-byte one)";
 
+// CQSA_FLAG_FREE_BUDGET: the budget is the current device's free memory less the margin
+// the caller passed as budget_bytes.
+cqsa_status free_budget(uint32_t flags, int64_t& budget) {
+  if (!(flags & CQSA_FLAG_FREE_BUDGET)) return CQSA_OK;
+  if (budget < 0) return fail(CQSA_EINVAL, "the margin (budget_bytes) must be >= 0");
+  size_t free_b = 0, total_b = 0;
+  const hipError_t e = hipMemGetInfo(&free_b, &total_b);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(CQSA_EHIP, std::string("hipMemGetInfo: ") + hipGetErrorString(e));
+  }
+  if (static_cast<int64_t>(free_b) <= budget)
+    return fail(CQSA_EBUDGET, "the margin of " + std::to_string(budget) + " bytes exceeds the " +
+                                  std::to_string(free_b) + " bytes free on the device");
+  budget = static_cast<int64_t>(free_b) - budget;
+  return CQSA_OK;
+}
+
 template <typename F>
 cqsa_status guarded(F&& f) {
   try {
@@ -96,6 +114,8 @@ cqsa_status cqsa_plan_create(int64_t n, int32_t heads, int32_t head_dim, cqsa_dt
   return guarded([&]() -> cqsa_status {
     if (out == nullptr) return fail(CQSA_EINVAL, "out is NULL");
     *out = nullptr;
+    const cqsa_status fb = free_budget(flags, budget_bytes);
+    if (fb != CQSA_OK) return fb;
     auto* plan = new cqsa_plan();
     std::string why;
     const cqsa_status s = cqsa::build_plan(n, heads, head_dim, dtype, l_levels, n_levels, budget_bytes, flags,
@@ -276,11 +296,35 @@ cqsa_status cqsa_plan_estimate(int64_t n, int32_t heads, int32_t head_dim, cqsa_
                                const cqsa_rates* rates, cqsa_estimate* out) {
   return guarded([&]() -> cqsa_status {
     if (rates == nullptr || out == nullptr) return fail(CQSA_EINVAL, "NULL argument");
+    const cqsa_status fb = free_budget(flags, budget_bytes);
+    if (fb != CQSA_OK) return fb;
     std::string why;
     const cqsa_status s = cqsa::estimate_plan(n, heads, head_dim, dtype, l_levels, n_levels, budget_bytes, flags,
                                               *rates, *out, why);
     return s == CQSA_OK ? ok() : fail(s, why);
   });
+}
+
+cqsa_status cqsa_plan_fallback(const cqsa_plan* plan, int64_t budget_bytes, cqsa_plan** out) {
+  return guarded([&]() -> cqsa_status {
+    if (plan == nullptr || out == nullptr) return fail(CQSA_EINVAL, "NULL argument");
+    *out = nullptr;
+    auto* next = new cqsa_plan();
+    std::string why;
+    const cqsa_status s = cqsa::fallback_plan(plan->p, budget_bytes, next->p, why);
+    if (s != CQSA_OK) {
+      delete next;
+      return fail(s, why);
+    }
+    *out = next;
+    return ok();
+  });
+}
+
+cqsa_status cqsa_debug_fail_allocations(int32_t count) {
+  if (count < 0) return fail(CQSA_EINVAL, "count must be >= 0");
+  cqsa::set_fail_allocations(count);
+  return ok();
 }
 
 }  // extern "C"

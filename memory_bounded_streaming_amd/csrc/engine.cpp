@@ -17,12 +17,14 @@
 #include "engine.hpp"
 
 #include <algorithm>
+#include <atomic>
 #include <chrono>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <initializer_list>
+#include <memory>
 #include <utility>
 #include <vector>
 
@@ -45,10 +47,64 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 float scale_log2(const Plan& p) { return static_cast<float>(1.0 / std::sqrt(double(p.d))) * kLog2e; }
 
-// Timing of one phase: pairs of events, summed after the final synchronisation.
+// Device allocations of the library go through here: a test can make the next few fail
+// as if the device were out of memory (cqsa_debug_fail_allocations).
+std::atomic<int> g_fail_allocs{0};
+
+hipError_t dev_malloc(void** ptr, int64_t bytes) {
+  int pending = g_fail_allocs.load();
+  while (pending > 0)
+    if (g_fail_allocs.compare_exchange_weak(pending, pending - 1)) {
+      *ptr = nullptr;
+      return hipErrorOutOfMemory;
+    }
+  return hipMalloc(ptr, static_cast<size_t>(bytes));
+}
+
+// Observed device memory of a call: free memory at entry, and its minimum over the polls.
+struct MemWatch {
+  size_t free0 = 0, min_free = 0;
+  bool ok = false;
+  void begin() {
+    size_t f = 0, t = 0;
+    if (hipMemGetInfo(&f, &t) == hipSuccess) {
+      free0 = min_free = f;
+      ok = true;
+    } else {
+      (void)hipGetLastError();
+    }
+  }
+  void poll() {
+    if (!ok) return;
+    size_t f = 0, t = 0;
+    if (hipMemGetInfo(&f, &t) == hipSuccess)
+      min_free = std::min(min_free, f);
+    else
+      (void)hipGetLastError();
+  }
+  int64_t peak() const { return ok ? static_cast<int64_t>(free0 - min_free) : -1; }
+};
+
+bool env_on(const char* name) {
+  const char* v = std::getenv(name);
+  return v != nullptr && v[0] != '\0' && v[0] != '0';
+}
+
+// Timing of the phases: begin/end event pairs per interval, read after the final
+// synchronisation.  A phase's time is the union of its intervals, each placed on one
+// time line by its offset from a reference event recorded first on the caller's stream
+// (every engine stream waits for the caller before its first step), so intervals of
+// one phase on two streams at once count once.
 struct PhaseTimer {
   bool on = false;
+  hipEvent_t ref = nullptr;
   std::vector<std::pair<hipEvent_t, hipEvent_t>> spans[4];  // h2d, attn, merge, d2h
+  hipError_t start(hipStream_t s) {
+    if (!on) return hipSuccess;
+    hipError_t e = hipEventCreate(&ref);
+    if (e != hipSuccess) return e;
+    return hipEventRecord(ref, s);
+  }
   hipError_t begin(int phase, hipStream_t s, hipEvent_t& ev) {
     ev = nullptr;
     if (!on) return hipSuccess;
@@ -66,14 +122,41 @@ struct PhaseTimer {
     return hipEventRecord(ev, s);
   }
   double total(int phase) const {
-    double ms = 0;
+    std::vector<std::pair<double, double>> iv;
     for (auto& sp : spans[phase]) {
-      float t = 0;
-      if (sp.first && sp.second && hipEventElapsedTime(&t, sp.first, sp.second) == hipSuccess) ms += t;
+      float b = 0, e = 0;
+      if (!sp.first || !sp.second) continue;
+      if (ref) {
+        if (hipEventElapsedTime(&b, ref, sp.first) != hipSuccess || hipEventElapsedTime(&e, ref, sp.second) != hipSuccess)
+          continue;
+      } else if (hipEventElapsedTime(&e, sp.first, sp.second) != hipSuccess) {
+        continue;
+      }
+      iv.push_back({b, e});
     }
+    if (ref == nullptr) {  // one stream: the intervals do not overlap
+      double ms = 0;
+      for (auto& x : iv) ms += x.second - x.first;
+      return ms;
+    }
+    std::sort(iv.begin(), iv.end());
+    double ms = 0, cb = 0, ce = -1;
+    bool open = false;
+    for (auto& x : iv) {
+      if (open && x.first <= ce) {
+        ce = std::max(ce, x.second);
+        continue;
+      }
+      if (open) ms += ce - cb;
+      cb = x.first;
+      ce = x.second;
+      open = true;
+    }
+    if (open) ms += ce - cb;
     return ms;
   }
   ~PhaseTimer() {
+    if (ref) (void)hipEventDestroy(ref);
     for (auto& v : spans)
       for (auto& sp : v) {
         if (sp.first) (void)hipEventDestroy(sp.first);
@@ -138,7 +221,7 @@ cqsa_status device_tables(const Plan& p, DeviceTables& out, std::string& why) {
     std::memcpy(host.data() + b0 + b1 + b2 + b3 + b4 + b5 + b6 + b7, p.bstream_kruns.data(),
                 p.bstream_kruns.size() * sizeof(KeyRun));
     void* mem = nullptr;
-    HIP_TRY(hipMalloc(&mem, host.size()));
+    HIP_TRY(dev_malloc(&mem, static_cast<int64_t>(host.size())));
     hipError_t e = hipMemcpy(mem, host.data(), host.size(), hipMemcpyHostToDevice);
     if (e != hipSuccess) {
       (void)hipFree(mem);
@@ -160,6 +243,19 @@ cqsa_status device_tables(const Plan& p, DeviceTables& out, std::string& why) {
   out.bytes = b0 + b1 + b2 + b3 + b4 + b5 + b6 + b7 + b8;
   return CQSA_OK;
 }
+
+int64_t table_bytes(const Plan& p) {
+  return align_up(int64_t(p.dev_items.size()) * sizeof(WorkItem)) + align_up(int64_t(p.dev_runs.size()) * sizeof(KeyRun)) +
+         align_up(int64_t(p.stream_items.size()) * sizeof(WorkItem)) +
+         align_up(int64_t(p.stream_runs.size()) * sizeof(KeyRun)) +
+         align_up(int64_t(p.dev_kitems.size()) * sizeof(WorkItem)) +
+         align_up(int64_t(p.dev_kruns.size()) * sizeof(KeyRun)) +
+         align_up(int64_t(p.bstream_items.size()) * sizeof(WorkItem)) +
+         align_up(int64_t(p.bstream_kitems.size()) * sizeof(WorkItem)) +
+         align_up(int64_t(p.bstream_kruns.size()) * sizeof(KeyRun));
+}
+
+void set_fail_allocations(int count) { g_fail_allocs.store(count); }
 
 void free_device_tables(const Plan& p) {
   std::lock_guard<std::mutex> lock(p.dev_mu);
@@ -226,13 +322,16 @@ namespace {
 
 cqsa_status forward_device(const Plan& p, const void* q, const void* k, const void* v, void* o, float* lse,
                            void* ws, int64_t ws_bytes, hipStream_t stream, cqsa_stats* stats, std::string& why) {
-  if (p.budget > 0 && p.device_ws > p.budget) {
-    why = "device-resident path needs " + std::to_string(p.device_ws) + " workspace bytes, over the budget";
+  if (p.budget > 0 && p.device_ws + table_bytes(p) > p.budget) {
+    why = "device-resident path needs " + std::to_string(p.device_ws) + " workspace bytes and " +
+          std::to_string(table_bytes(p)) + " descriptor bytes, over the budget";
     return CQSA_EBUDGET;
   }
+  MemWatch mw;
+  if (stats) mw.begin();
   bool owned = false;
   if (ws == nullptr) {
-    HIP_TRY(hipMalloc(&ws, p.device_ws));
+    HIP_TRY(dev_malloc(&ws, p.device_ws));
     owned = true;
   } else if (ws_bytes < p.device_ws) {
     why = "workspace of " + std::to_string(ws_bytes) + " bytes, need " + std::to_string(p.device_ws);
@@ -254,6 +353,7 @@ cqsa_status forward_device(const Plan& p, const void* q, const void* k, const vo
   };
   if (tm.begin(PH_ATTN, stream, ev) != hipSuccess) return fail(CQSA_EHIP);
   st = run_partials(p, q, k, v, n_slots, ml_slots, stream, why);
+  mw.poll();
   if (st != CQSA_OK) return fail(st);
   if (tm.end(PH_ATTN, stream) != hipSuccess || tm.begin(PH_MERGE, stream, ev) != hipSuccess) return fail(CQSA_EHIP);
   st = run_merge(p, n_slots, ml_slots, o, lse, stream, why);
@@ -266,18 +366,20 @@ cqsa_status forward_device(const Plan& p, const void* q, const void* k, const vo
       return fail(CQSA_EHIP);
     }
   }
+  mw.poll();
   if (owned) (void)hipFree(ws);
   if (stats) {
-    DeviceTables t{};
-    (void)device_tables(p, t, why);
     std::memset(stats, 0, sizeof(*stats));
     stats->t_total_ms = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
     stats->t_attn_ms = tm.total(PH_ATTN);
     stats->t_merge_ms = tm.total(PH_MERGE);
-    stats->peak_device_bytes = p.device_ws + t.bytes;
+    stats->peak_device_bytes = p.device_ws + table_bytes(p);
     stats->n_attn_launches = 1;
     stats->n_merge_launches = 1;
     stats->useful_flop = p.useful_flop();
+    stats->observed_peak_bytes = mw.peak();
+    stats->device_free_at_entry = static_cast<int64_t>(mw.free0);
+    stats->levels_used = static_cast<int32_t>(p.ls.size());
   }
   return CQSA_OK;
 }
@@ -310,22 +412,64 @@ struct StreamRes {
   }
 };
 
-cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const char* v, char* o, float* lse,
-                           void* ws, int64_t ws_bytes, hipStream_t caller, cqsa_stats* stats, std::string& why) {
-  {
-    const cqsa_status pin = check_pinned({{q, "q"}, {k, "k"}, {v, "v"}, {o, "o"}, {lse, "lse"}}, why);
-    if (pin != CQSA_OK) return pin;
+// Guard words around the pieces of a workspace the library allocated (CQSA_CANARY=1):
+// filled before the call, compared after it.
+constexpr int64_t kGuardBytes = 256;
+constexpr uint32_t kGuardWord = 0xC0DEC0DEu;
+
+struct Canary {
+  bool on = false;
+  std::vector<std::pair<char*, std::string>> guards;  // guard address, piece name
+  hipError_t fill(hipStream_t s) {
+    for (auto& g : guards) {
+      hipError_t e = hipMemsetD32Async(reinterpret_cast<hipDeviceptr_t>(g.first), static_cast<int>(kGuardWord),
+                                       kGuardBytes / 4, s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
   }
+  // the name of the first piece whose guard changed, "" if none
+  std::string check() const {
+    std::vector<uint32_t> host(kGuardBytes / 4);
+    for (auto& g : guards) {
+      if (hipMemcpy(host.data(), g.first, kGuardBytes, hipMemcpyDeviceToHost) != hipSuccess) return g.second + " (unreadable)";
+      for (uint32_t w : host)
+        if (w != kGuardWord) return g.second;
+    }
+    return "";
+  }
+};
+
+// One attempt of the streamed forward with plan p.  dev_oom reports that the device
+// workspace (or the descriptor tables) could not be allocated, the failure the caller
+// recovers from by re-planning.
+cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const char* v, char* o, float* lse,
+                           void* ws, int64_t ws_bytes, hipStream_t caller, cqsa_stats* stats, MemWatch& mw,
+                           bool& dev_oom, std::string& why) {
+  dev_oom = false;
   const auto t0 = std::chrono::steady_clock::now();
   const Footprint fp = p.stream_fp;
   const StreamLayout L = stream_layout(p, fp.acc_on_device, fp.kv_buffers);
+  const bool sync = env_on("CQSA_SYNC");
+  Canary canary;
+  canary.on = ws == nullptr && env_on("CQSA_CANARY");
   DeviceTables tabs{};
   cqsa_status st = device_tables(p, tabs, why);
+  if (st == CQSA_ENOMEM) dev_oom = true;
   if (st != CQSA_OK) return st;
+  mw.poll();
 
   StreamRes res;
+  const int kPieces = 2 * fp.kv_buffers + 2 * 7 + 3;  // upper bound of the pieces carved below
   if (ws == nullptr) {
-    HIP_TRY(hipMalloc(&res.ws, L.total));
+    const int64_t bytes = L.total + (canary.on ? kPieces * kGuardBytes : 0);
+    const hipError_t e = dev_malloc(&res.ws, bytes);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      why = "device workspace of " + std::to_string(bytes) + " bytes: " + hipGetErrorString(e);
+      dev_oom = e == hipErrorOutOfMemory;
+      return dev_oom ? CQSA_ENOMEM : CQSA_EHIP;
+    }
     res.own_ws = true;
   } else {
     if (ws_bytes < L.total) {
@@ -334,18 +478,23 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
     }
     res.ws = ws;
   }
-  // carve the workspace
+  mw.poll();
+  // carve the workspace (a guard follows every piece in canary mode)
   char* cur = static_cast<char*>(res.ws);
-  auto take = [&](int64_t bytes) {
+  auto take = [&](int64_t bytes, const char* name) {
     char* r = cur;
     cur += bytes;
+    if (canary.on) {
+      canary.guards.push_back({cur, name});
+      cur += kGuardBytes;
+    }
     return r;
   };
   char* kst[2] = {nullptr, nullptr};
   char* vst[2] = {nullptr, nullptr};
   for (int b = 0; b < fp.kv_buffers; ++b) {
-    kst[b] = take(L.kv_stage);
-    vst[b] = take(L.kv_stage);
+    kst[b] = take(L.kv_stage, "K staging");
+    vst[b] = take(L.kv_stage, "V staging");
   }
   struct Slot {
     char* q;
@@ -354,19 +503,18 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
     float* an;
     float* aml;
     char* o;
-    float* lse;
   } slot[2];
   for (auto& s : slot) {
-    s.q = take(L.q_blk);
-    s.n = reinterpret_cast<float*>(take(L.n_blk));
-    s.ml = reinterpret_cast<float*>(take(L.ml_blk));
-    s.an = fp.acc_on_device ? nullptr : reinterpret_cast<float*>(take(L.n_blk));
-    s.aml = fp.acc_on_device ? nullptr : reinterpret_cast<float*>(take(L.ml_blk));
-    s.o = take(L.o_blk);
-    s.lse = reinterpret_cast<float*>(take(L.lse_blk));
+    s.q = take(L.q_blk, "Q block");
+    s.n = reinterpret_cast<float*>(take(L.n_blk, "partial n block"));
+    s.ml = reinterpret_cast<float*>(take(L.ml_blk, "partial (m, l) block"));
+    s.an = fp.acc_on_device ? nullptr : reinterpret_cast<float*>(take(L.n_blk, "accumulator n block"));
+    s.aml = fp.acc_on_device ? nullptr : reinterpret_cast<float*>(take(L.ml_blk, "accumulator (m, l) block"));
+    s.o = take(L.o_blk, "O block");
   }
-  float* acc_n = fp.acc_on_device ? reinterpret_cast<float*>(take(L.acc_n)) : nullptr;
-  float* acc_ml = fp.acc_on_device ? reinterpret_cast<float*>(take(L.acc_ml)) : nullptr;
+  float* lse_dev = reinterpret_cast<float*>(take(L.lse_all, "LSE"));
+  float* acc_n = fp.acc_on_device ? reinterpret_cast<float*>(take(L.acc_n, "accumulator n")) : nullptr;
+  float* acc_ml = fp.acc_on_device ? reinterpret_cast<float*>(take(L.acc_ml, "accumulator (m, l)")) : nullptr;
 
   const int64_t H = p.heads, D = p.d, U = p.unit, N = p.n;
   const int64_t row_in = p.row_in_bytes();
@@ -382,9 +530,11 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
   }
   res.caller = caller;
   for (auto& s : res.s) HIP_TRY(hipStreamCreateWithFlags(&s, hipStreamNonBlocking));
+  mw.poll();
   hipStream_t s_kv = res.s[0], s_q = res.s[1], s_c = caller, s_d = res.s[2];
-  hipEvent_t start, kv_ready[2], kv_free[2], q_ready[2], c_done[2], slot_free[2], task_done[3];
+  hipEvent_t start, kv_ready[2], kv_free[2], q_ready[2], c_done[2], slot_free[2], task_done[3], all_merged;
   HIP_TRY(res.event(start));
+  HIP_TRY(res.event(all_merged));
   for (int i = 0; i < 3; ++i) HIP_TRY(res.event(task_done[i]));
   for (int i = 0; i < 2; ++i) {
     HIP_TRY(res.event(kv_ready[i]));
@@ -393,11 +543,14 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
     HIP_TRY(res.event(c_done[i]));
     HIP_TRY(res.event(slot_free[i]));
   }
-  HIP_TRY(hipEventRecord(start, caller));
-  for (hipStream_t s : res.s) HIP_TRY(hipStreamWaitEvent(s, start, 0));
-
   PhaseTimer tm;
   tm.on = stats != nullptr;
+  HIP_TRY(tm.start(caller));
+  if (canary.on) HIP_TRY(canary.fill(caller));
+  HIP_TRY(hipEventRecord(start, caller));
+  for (hipStream_t s : res.s) HIP_TRY(hipStreamWaitEvent(s, start, 0));
+  auto step = [&]() -> hipError_t { return sync ? hipDeviceSynchronize() : hipSuccess; };
+
   hipEvent_t tev;
   int64_t bytes_h2d = 0, bytes_d2h = 0, bytes_d2d = 0, n_attn = 0, n_merge = 0, n_h2d = 0, n_d2h = 0;
   const int64_t tu = p.task_units;
@@ -420,6 +573,7 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
     // keep the host at most two tasks ahead of the GPU
     if (ti >= 2) {
       HIP_TRY(hipEventSynchronize(task_done[(ti - 2) % 3]));
+      mw.poll();
       if (progress) report(static_cast<int64_t>(ti) - 2);
     }
     if (static_cast<int64_t>(ti) >= fp.kv_buffers) HIP_TRY(hipStreamWaitEvent(s_kv, kv_free[b], 0));
@@ -469,6 +623,7 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
     HIP_TRY(tm.end(PH_H2D, s_kv));
     HIP_TRY(hipEventRecord(kv_ready[b], s_kv));
     HIP_TRY(hipStreamWaitEvent(s_c, kv_ready[b], 0));
+    HIP_TRY(step());
 
     for (int64_t a = 0; a < tu; ++a, ++blk) {
       const int j = static_cast<int>(blk % 2);
@@ -495,6 +650,7 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
       HIP_TRY(tm.end(PH_H2D, s_q));
       HIP_TRY(hipEventRecord(q_ready[j], s_q));
       HIP_TRY(hipStreamWaitEvent(s_c, q_ready[j], 0));
+      HIP_TRY(step());
 
       // partials of (task, unit)
       float* pn = S.n;
@@ -522,7 +678,8 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
       HIP_TRY(tm.end(PH_ATTN, s_c));
       ++n_attn;
 
-      // merge into the accumulator (ascending task order per row)
+      // merge into the accumulator (ascending task order per row); the final merge of a
+      // unit writes its O block and its LSE rows straight into the resident [H][N] array
       MergeLaunch m{};
       m.dtype = p.dtype;
       m.d = p.d;
@@ -530,9 +687,9 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
       m.rows = R;
       m.final_out = last;
       m.o_out = S.o;
-      m.lse_out = S.lse;
-      m.lse_stride = U;
-      m.lse_row0 = 0;
+      m.lse_out = lse_dev;
+      m.lse_stride = N;
+      m.lse_row0 = pu * U;
       bool do_merge = true;
       if (fp.acc_on_device) {
         float* an = acc_n + pu * U * nrow_f;
@@ -568,6 +725,7 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
         ++n_merge;
       }
       HIP_TRY(hipEventRecord(c_done[j], s_c));
+      HIP_TRY(step());
 
       // D2H: finished output block, or the accumulator block back to host memory
       HIP_TRY(hipStreamWaitEvent(s_d, c_done[j], 0));
@@ -576,14 +734,6 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
         HIP_TRY(hipMemcpyAsync(o + pu * U * H * D * e, S.o, R * H * D * e, hipMemcpyDeviceToHost, s_d));
         bytes_d2h += R * H * D * e;
         ++n_d2h;
-        if (lse != nullptr) {
-          // one contiguous copy per head: LSE is [H][N] on the host and [H][U] in the block
-          // (a strided 2-D copy of the same bytes runs several times slower)
-          for (int64_t h = 0; h < H; ++h)
-            HIP_TRY(hipMemcpyAsync(lse + h * N + pu * U, S.lse + h * U, R * sizeof(float), hipMemcpyDeviceToHost, s_d));
-          bytes_d2h += H * R * 4;
-          n_d2h += H;
-        }
       } else if (!fp.acc_on_device) {
         const float* sn = first ? S.n : S.an;
         const float* sml = first ? S.ml : S.aml;
@@ -595,15 +745,34 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
       }
       HIP_TRY(tm.end(PH_D2H, s_d));
       HIP_TRY(hipEventRecord(slot_free[j], s_d));
+      HIP_TRY(step());
     }
     HIP_TRY(hipEventRecord(kv_free[b], s_c));  // after the task's last launch on s_c
     HIP_TRY(hipEventRecord(task_done[ti % 3], s_c));
   }
+  // LSE of every row, in one copy once the last merge has written it
+  if (lse != nullptr) {
+    HIP_TRY(hipEventRecord(all_merged, s_c));
+    HIP_TRY(hipStreamWaitEvent(s_d, all_merged, 0));
+    HIP_TRY(tm.begin(PH_D2H, s_d, tev));
+    HIP_TRY(hipMemcpyAsync(lse, lse_dev, H * N * sizeof(float), hipMemcpyDeviceToHost, s_d));
+    HIP_TRY(tm.end(PH_D2H, s_d));
+    bytes_d2h += H * N * 4;
+    ++n_d2h;
+  }
   HIP_TRY(hipStreamSynchronize(s_c));
   for (hipStream_t s : res.s) HIP_TRY(hipStreamSynchronize(s));
+  mw.poll();
   if (progress)
     for (int64_t t = std::max<int64_t>(0, n_tasks - 2); t < n_tasks; ++t) report(t);
   HIP_TRY(hipGetLastError());
+  if (canary.on) {
+    const std::string bad = canary.check();
+    if (!bad.empty()) {
+      why = "workspace guard after the " + bad + " was overwritten";
+      return CQSA_EHIP;
+    }
+  }
   if (stats) {
     std::memset(stats, 0, sizeof(*stats));
     stats->t_h2d_ms = tm.total(PH_H2D);
@@ -619,9 +788,60 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
     stats->n_h2d_copies = n_h2d;
     stats->n_d2h_copies = n_d2h;
     stats->useful_flop = p.useful_flop();
+    stats->levels_used = static_cast<int32_t>(p.ls.size());
     stats->t_total_ms = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
   }
   return CQSA_OK;
+}
+
+// The streamed forward with the out-of-memory recovery: when the device workspace of a
+// plan cannot be allocated, re-plan one level deeper under the memory the device has
+// now (less a 1/16 margin) and run that plan inside the same call; the caller's plan is
+// unchanged and the result is the same attention (a different division of it).
+cqsa_status forward_stream_recover(const Plan& p, const char* q, const char* k, const char* v, char* o, float* lse,
+                                   void* ws, int64_t ws_bytes, hipStream_t caller, cqsa_stats* stats,
+                                   std::string& why) {
+  {
+    const cqsa_status pin = check_pinned({{q, "q"}, {k, "k"}, {v, "v"}, {o, "o"}, {lse, "lse"}}, why);
+    if (pin != CQSA_OK) return pin;
+  }
+  const auto t0 = std::chrono::steady_clock::now();
+  MemWatch mw;
+  mw.begin();
+  bool dev_oom = false;
+  cqsa_status st = forward_stream(p, q, k, v, o, lse, ws, ws_bytes, caller, stats, mw, dev_oom, why);
+  std::unique_ptr<Plan> fb;
+  int replans = 0;
+  while (st == CQSA_ENOMEM && dev_oom && ws == nullptr) {
+    size_t free_b = 0, total_b = 0;
+    if (hipMemGetInfo(&free_b, &total_b) != hipSuccess) {
+      (void)hipGetLastError();
+      return st;
+    }
+    int64_t budget = static_cast<int64_t>(free_b - free_b / 16);
+    const Plan& cur = fb ? *fb : p;
+    if (cur.budget > 0) budget = std::min(budget, cur.budget);
+    auto next = std::make_unique<Plan>();
+    std::string w;
+    const cqsa_status fs = fallback_plan(cur, budget, *next, w);
+    if (fs != CQSA_OK) {
+      why += "; no deeper plan fits the " + std::to_string(budget) + " bytes the device has free: " + w;
+      return st;
+    }
+    if (fb) free_device_tables(*fb);
+    fb = std::move(next);
+    ++replans;
+    why.clear();
+    st = forward_stream(*fb, q, k, v, o, lse, ws, ws_bytes, caller, stats, mw, dev_oom, why);
+  }
+  if (fb) free_device_tables(*fb);
+  if (st == CQSA_OK && stats) {
+    stats->observed_peak_bytes = mw.peak();
+    stats->device_free_at_entry = static_cast<int64_t>(mw.free0);
+    stats->replans = replans;
+    stats->t_total_ms = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+  }
+  return st;
 }
 
 }  // namespace
@@ -679,6 +899,8 @@ cqsa_status backward_stream(const Plan& p, const char* q, const char* k, const c
     return CQSA_EBUDGET;
   }
   const auto t0 = std::chrono::steady_clock::now();
+  MemWatch mw;
+  if (stats) mw.begin();
   const bool dev_acc = p.bwd_stream_fp.acc_on_device;
   const int nset = p.bwd_stream_fp.kv_buffers;
   const BwdStreamLayout L = bwd_stream_layout(p, dev_acc, nset);
@@ -688,7 +910,7 @@ cqsa_status backward_stream(const Plan& p, const char* q, const char* k, const c
   BwdStreamRes R;
   R.caller = caller;
   if (ws == nullptr) {
-    HIP_TRY(hipMalloc(&R.ws, L.total));
+    HIP_TRY(dev_malloc(&R.ws, L.total));
     R.own_ws = true;
   } else {
     if (ws_bytes < L.total) {
@@ -742,6 +964,7 @@ cqsa_status backward_stream(const Plan& p, const char* q, const char* k, const c
   char* outs[3] = {dq, dk, dv};
 
   for (auto& s : R.s) HIP_TRY(hipStreamCreateWithFlags(&s, hipStreamNonBlocking));
+  mw.poll();
   hipStream_t s_h = R.s[0], s_d = R.s[1], s_c = caller;
   hipEvent_t start, staged, stage_free[2], acc_ready[2], c_done[2], slot_free[2];
   HIP_TRY(R.event(start));
@@ -752,10 +975,11 @@ cqsa_status backward_stream(const Plan& p, const char* q, const char* k, const c
     HIP_TRY(R.event(c_done[i]));
     HIP_TRY(R.event(slot_free[i]));
   }
-  HIP_TRY(hipEventRecord(start, caller));
-  for (hipStream_t s : R.s) HIP_TRY(hipStreamWaitEvent(s, start, 0));
   PhaseTimer tm;
   tm.on = stats != nullptr;
+  HIP_TRY(tm.start(caller));
+  HIP_TRY(hipEventRecord(start, caller));
+  for (hipStream_t s : R.s) HIP_TRY(hipStreamWaitEvent(s, start, 0));
   hipEvent_t tev;
   int64_t bytes_h2d = 0, bytes_d2h = 0, n_attn = 0, n_merge = 0, n_h2d = 0, n_d2h = 0;
 
@@ -924,9 +1148,11 @@ cqsa_status backward_stream(const Plan& p, const char* q, const char* k, const c
       HIP_TRY(hipEventRecord(slot_free[j], s_d));
     }
     HIP_TRY(hipEventRecord(stage_free[sb], s_c));
+    mw.poll();
   }
   HIP_TRY(hipStreamSynchronize(s_c));
   for (hipStream_t s : R.s) HIP_TRY(hipStreamSynchronize(s));
+  mw.poll();
   HIP_TRY(hipGetLastError());
   if (stats) {
     std::memset(stats, 0, sizeof(*stats));
@@ -942,6 +1168,9 @@ cqsa_status backward_stream(const Plan& p, const char* q, const char* k, const c
     stats->n_h2d_copies = n_h2d;
     stats->n_d2h_copies = n_d2h;
     stats->useful_flop = 2.5 * p.useful_flop();
+    stats->observed_peak_bytes = mw.peak();
+    stats->device_free_at_entry = static_cast<int64_t>(mw.free0);
+    stats->levels_used = static_cast<int32_t>(p.ls.size());
     stats->t_total_ms = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
   }
   return CQSA_OK;
@@ -968,13 +1197,15 @@ cqsa_status run_backward(const Plan& p, const void* q, const void* k, const void
     why = "device-resident backward needs " + std::to_string(p.bwd_device_ws) + " workspace bytes, over the budget";
     return CQSA_EBUDGET;
   }
+  MemWatch mw;
+  if (stats) mw.begin();
   DeviceTables t{};
   cqsa_status st = device_tables(p, t, why);
   if (st != CQSA_OK) return st;
   const BwdLayout L = bwd_layout(p);
   bool owned = false;
   if (ws == nullptr) {
-    HIP_TRY(hipMalloc(&ws, L.total));
+    HIP_TRY(dev_malloc(&ws, L.total));
     owned = true;
   } else if (ws_bytes < L.total) {
     why = "workspace of " + std::to_string(ws_bytes) + " bytes, need " + std::to_string(L.total);
@@ -1075,9 +1306,13 @@ cqsa_status run_backward(const Plan& p, const void* q, const void* k, const void
     HIP_TRY(launch_sum_slots(sl, stream));
   }
   HIP_TRY(tm.end(PH_MERGE, stream));
+  mw.poll();
   if (owned || stats) HIP_TRY(hipStreamSynchronize(stream));
   if (stats) {
     std::memset(stats, 0, sizeof(*stats));
+    stats->observed_peak_bytes = mw.peak();
+    stats->device_free_at_entry = static_cast<int64_t>(mw.free0);
+    stats->levels_used = static_cast<int32_t>(p.ls.size());
     stats->t_total_ms = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
     stats->t_attn_ms = tm.total(PH_ATTN);
     stats->t_merge_ms = tm.total(PH_MERGE);
@@ -1093,8 +1328,9 @@ cqsa_status run_forward(const Plan& p, const void* q, const void* k, const void*
                         cqsa_residency res, void* ws, int64_t ws_bytes, hipStream_t stream, cqsa_stats* stats,
                         std::string& why) {
   if (res == CQSA_RES_DEVICE) return forward_device(p, q, k, v, o, lse, ws, ws_bytes, stream, stats, why);
-  return forward_stream(p, static_cast<const char*>(q), static_cast<const char*>(k), static_cast<const char*>(v),
-                        static_cast<char*>(o), lse, ws, ws_bytes, stream, stats, why);
+  return forward_stream_recover(p, static_cast<const char*>(q), static_cast<const char*>(k),
+                                static_cast<const char*>(v), static_cast<char*>(o), lse, ws, ws_bytes, stream, stats,
+                                why);
 }
 
 }  // namespace cqsa

@@ -26,6 +26,10 @@ struct DeviceTables {
 // Descriptor tables of the plan on the current device (uploaded on first use).
 cqsa_status device_tables(const Plan& p, DeviceTables& out, std::string& why);
 void free_device_tables(const Plan& p);
+// Bytes of the plan's descriptor tables on a device.
+int64_t table_bytes(const Plan& p);
+// Make the next `count` device allocations of the library fail as out of memory.
+void set_fail_allocations(int count);
 
 cqsa_status run_partials(const Plan& p, const void* q, const void* k, const void* v, float* n_out,
                          float* ml_out, hipStream_t stream, std::string& why);

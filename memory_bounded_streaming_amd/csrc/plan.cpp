@@ -79,11 +79,11 @@ StreamLayout stream_layout(const Plan& p, bool acc_on_device, int kv_buffers) {
   s.n_blk = align_up(u * h * d * 4);
   s.ml_blk = align_up(u * h * 2 * 4);
   s.o_blk = align_up(u * h * d * e);
-  s.lse_blk = align_up(h * u * 4);
+  s.lse_all = align_up(h * p.n * 4);
   s.acc_n = acc_on_device ? align_up(p.n * h * d * 4) : 0;
   s.acc_ml = acc_on_device ? align_up(p.n * h * 2 * 4) : 0;
-  const int64_t slot = s.q_blk + s.n_blk + s.ml_blk + (acc_on_device ? 0 : s.n_blk + s.ml_blk) + s.o_blk + s.lse_blk;
-  s.total = 2 * kv_buffers * s.kv_stage + 2 * slot + s.acc_n + s.acc_ml;
+  const int64_t slot = s.q_blk + s.n_blk + s.ml_blk + (acc_on_device ? 0 : s.n_blk + s.ml_blk) + s.o_blk;
+  s.total = 2 * kv_buffers * s.kv_stage + 2 * slot + s.lse_all + s.acc_n + s.acc_ml;
   return s;
 }
 
@@ -116,6 +116,9 @@ BwdStreamLayout bwd_stream_layout(const Plan& p, bool acc_on_device, int stage_s
 }
 
 namespace {
+
+constexpr uint32_t kKnownFlags =
+    CQSA_FLAG_HOST_ACC | CQSA_FLAG_KV_SINGLE | CQSA_FLAG_PAD | CQSA_FLAG_CAUSAL | CQSA_FLAG_FREE_BUDGET;
 
 // Every innermost task with its units, per-level chunk of each local unit, admitted
 // runs and segments.  With several levels a (task, query unit) may admit no key at all
@@ -465,11 +468,43 @@ cqsa_status build_fixed(int64_t n, int heads, int d, cqsa_dtype dtype, const std
 
 }  // namespace
 
+cqsa_status fallback_plan(const Plan& p, int64_t budget, Plan& out, std::string& why) {
+  if (budget <= 0) {
+    why = "the fallback budget must be positive";
+    return CQSA_EINVAL;
+  }
+  // the deeper plan repeats the innermost division (an undivided plan divides with l = 3)
+  std::vector<int> levels = p.ls;
+  const int l = levels.back() > 1 ? levels.back() : 3;
+  if (levels.size() == 1 && levels[0] == 1) levels.clear();
+  std::string last_why = "no level count fits";
+  cqsa_status last = CQSA_EBUDGET;
+  while (static_cast<int>(levels.size()) < CQSA_MAX_LEVELS) {
+    levels.push_back(l);
+    int64_t prod_c = 1;
+    for (int x : levels) prod_c *= x * (x - 1) + 1;
+    if (prod_c > p.n) {
+      why = "N=" + std::to_string(p.n) + " has fewer tokens than the " + std::to_string(prod_c) +
+            " units of a deeper plan";
+      return CQSA_EDIVIDE;
+    }
+    // padding is exact (never read), so a deeper grid that N does not divide is padded
+    const uint32_t flags = (p.flags & ~CQSA_FLAG_FREE_BUDGET) | (p.n % prod_c != 0 ? CQSA_FLAG_PAD : 0u);
+    std::string w;
+    last = build_fixed(p.n, p.heads, p.d, p.dtype, levels, budget, flags, out, w);
+    if (last == CQSA_OK) return CQSA_OK;
+    last_why = w;
+    if (last != CQSA_EBUDGET) break;
+  }
+  why = last_why;
+  return last;
+}
+
 cqsa_status build_plan(int64_t n, int heads, int d, cqsa_dtype dtype, const int32_t* ls, int n_levels,
                        int64_t budget, uint32_t flags, Plan& out, std::string& why) {
   if (n < 1 || heads < 1 || (d != 64 && d != 128) || ls == nullptr || n_levels < 0 ||
       n_levels > CQSA_MAX_LEVELS || budget < 0 || (dtype != CQSA_BF16 && dtype != CQSA_F32) ||
-      (flags & ~(CQSA_FLAG_HOST_ACC | CQSA_FLAG_KV_SINGLE | CQSA_FLAG_PAD | CQSA_FLAG_CAUSAL)) != 0) {
+      (flags & ~kKnownFlags) != 0) {
     why = "need n>=1, heads>=1, head_dim 64 or 128, 0<=n_levels<=" + std::to_string(CQSA_MAX_LEVELS) +
           ", budget>=0, known dtype and flags";
     return CQSA_EINVAL;
@@ -556,7 +591,7 @@ cqsa_status estimate_plan(int64_t n, int heads, int d, cqsa_dtype dtype, const i
                           std::string& why) {
   if (n < 1 || heads < 1 || (d != 64 && d != 128) || ls == nullptr || n_levels < 0 ||
       n_levels > CQSA_MAX_LEVELS || budget < 0 || (dtype != CQSA_BF16 && dtype != CQSA_F32) ||
-      (flags & ~(CQSA_FLAG_HOST_ACC | CQSA_FLAG_KV_SINGLE | CQSA_FLAG_PAD | CQSA_FLAG_CAUSAL)) != 0 || !(r.attn_tflops > 0) ||
+      (flags & ~kKnownFlags) != 0 || !(r.attn_tflops > 0) ||
       !(r.merge_gbs > 0) || !(r.h2d_gbs > 0) || !(r.d2h_gbs > 0)) {
     why = "the arguments of cqsa_plan_create, and every rate must be positive";
     return CQSA_EINVAL;

@@ -130,7 +130,8 @@ BwdStreamLayout bwd_stream_layout(const Plan& p, bool acc_on_device, int stage_s
 // Byte size of each piece of the streamed path's workspace, in the order it is carved.
 struct StreamLayout {
   int64_t kv_stage;     // one K or V staging buffer (task_tokens rows)
-  int64_t q_blk, n_blk, ml_blk, o_blk, lse_blk;  // per ring slot (unit rows)
+  int64_t q_blk, n_blk, ml_blk, o_blk;  // per ring slot (unit rows)
+  int64_t lse_all;      // LSE [H][N] fp32, resident for the call (copied back once)
   int64_t acc_n, acc_ml; // device accumulator (0 when on host)
   int64_t total;
 };
@@ -142,6 +143,11 @@ inline int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; 
 // Build a plan; on failure returns the status and fills why.
 cqsa_status build_plan(int64_t n, int heads, int d, cqsa_dtype dtype, const int32_t* ls,
                        int n_levels, int64_t budget, uint32_t flags, Plan& out, std::string& why);
+
+// The out-of-memory fallback of `p`: one level deeper (repeating the innermost l, 3 for
+// an undivided plan), padded when N no longer divides, under `budget`; further levels
+// while no staging mode fits (cqsa_plan_fallback).
+cqsa_status fallback_plan(const Plan& p, int64_t budget, Plan& out, std::string& why);
 
 // Closed-form dry run of the streamed forward (cqsa_plan_estimate).
 cqsa_status estimate_plan(int64_t n, int heads, int d, cqsa_dtype dtype, const int32_t* ls, int n_levels,

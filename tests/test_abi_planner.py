@@ -31,7 +31,7 @@ def _header_symbols():
 
 def test_library_exports_every_declared_symbol(lib):
     names = _header_symbols()
-    assert len(names) == 16
+    assert len(names) == 18
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(cqsa.EXPORTS)
@@ -163,7 +163,7 @@ def test_plan_errors(args, status):
 
 def test_bad_flags_and_null_arguments(lib):
     with pytest.raises(cqsa.CqsaError) as e:
-        cqsa.cqsa_plan_create(49, 1, 64, cqsa.CQSA_BF16, [3], flags=0x10)
+        cqsa.cqsa_plan_create(49, 1, 64, cqsa.CQSA_BF16, [3], flags=0x40)
     assert e.value.status == -1
     import ctypes
     assert lib.cqsa_plan_create(49, 1, 64, 0, None, 1, 0, 0, ctypes.byref(ctypes.c_void_p())) == -1

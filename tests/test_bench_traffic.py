@@ -47,3 +47,20 @@ def test_traffic_record_needs_the_calibration_copy(tmp_path):
     with pytest.raises(ValueError):
         bench.traffic_record(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), "x")
 
+
+
+def test_copy_summary_takes_the_union_of_copy_intervals(tmp_path):
+    # two host-to-device copies overlapping on two streams count once; device-to-host apart
+    path = tmp_path / "copies.csv"
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kind", "Direction", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for d, b, e in [("MEMORY_COPY_HOST_TO_DEVICE", 0, 4_000_000), ("MEMORY_COPY_HOST_TO_DEVICE", 1_000_000, 6_000_000),
+                        ("MEMORY_COPY_HOST_TO_DEVICE", 10_000_000, 11_000_000),
+                        ("MEMORY_COPY_DEVICE_TO_HOST", 2_000_000, 3_000_000),
+                        ("MEMORY_COPY_DEVICE_TO_HOST", 5_000_000, 7_000_000),
+                        ("MEMORY_COPY_DEVICE_TO_DEVICE", 0, 9_000_000)]:
+            w.writerow({"Kind": "MEMORY_COPY", "Direction": d, "Start_Timestamp": b, "End_Timestamp": e})
+    out = bench.copy_summary(str(path))
+    assert out["h2d"] == {"copies": 3, "busy_ms": 7.0, "span_ms": 11.0}
+    assert out["d2h"] == {"copies": 2, "busy_ms": 3.0, "span_ms": 5.0}
