@@ -472,6 +472,15 @@ def run_streamed(args, torch, cqsa):
         }
 
 
+def guarded(name, fn):
+    """Run a secondary leg; its failure is recorded in the line instead of ending the run."""
+    try:
+        return fn()
+    except Exception as exc:  # noqa: BLE001 -- any failure of a secondary leg is reported, not raised
+        log(f"bench: {name} failed: {exc}")
+        return {"error": f"{type(exc).__name__}: {exc}"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -541,25 +550,32 @@ def main():
     dres = None
     if not args.no_device:
         log("bench: device-resident workload")
-        dres = run_device(args, torch, cqsa)
-        log(f"bench: device-resident {dres['value']:.1f} TFLOP/s, partial kernel {dres['attn_tflops']:.1f} TFLOP/s")
+        dres = guarded("device-resident leg", lambda: run_device(args, torch, cqsa))
+        if "error" in dres:
+            dres = None
+        else:
+            log(f"bench: device-resident {dres['value']:.1f} TFLOP/s, partial kernel "
+                f"{dres['attn_tflops']:.1f} TFLOP/s")
     bwd = None
     if not args.no_backward and dres is not None:
         log("bench: backward of the device-resident workload")
-        bwd = run_backward(args, torch, cqsa)
-        bwd["fwd_bwd_ratio"] = round((bwd["ms_per_step"] + dres["ms_per_step"]) / dres["ms_per_step"], 3)
-        bwd.pop("fwd_bwd_ratio_note")
-        log(f"bench: backward {bwd['tflops_useful']:.1f} useful TFLOP/s, {bwd['ms_per_step']:.2f} ms")
+        bwd = guarded("backward leg", lambda: run_backward(args, torch, cqsa))
+        if "error" not in bwd:
+            bwd["fwd_bwd_ratio"] = round((bwd["ms_per_step"] + dres["ms_per_step"]) / dres["ms_per_step"], 3)
+            bwd.pop("fwd_bwd_ratio_note")
+            log(f"bench: backward {bwd['tflops_useful']:.1f} useful TFLOP/s, {bwd['ms_per_step']:.2f} ms")
     stream_res = None
     if not args.no_streamed:
         log("bench: host-pinned streamed N=212992 workload")
-        stream_res = run_streamed(args, torch, cqsa)
-        log(f"bench: streamed {stream_res['tflops_pcie_inclusive']:.1f} TFLOP/s PCIe-inclusive")
+        stream_res = guarded("streamed 16 GiB leg", lambda: run_streamed(args, torch, cqsa))
+        if "error" not in stream_res:
+            log(f"bench: streamed {stream_res['tflops_pcie_inclusive']:.1f} TFLOP/s PCIe-inclusive")
     sbwd = None
     if not args.no_streamed and not args.no_streamed_backward:
         log("bench: host-pinned streamed backward")
-        sbwd = run_streamed_backward(args, torch, cqsa)
-        log(f"bench: streamed backward {sbwd['tflops_pcie_inclusive']:.1f} useful TFLOP/s PCIe-inclusive")
+        sbwd = guarded("streamed backward leg", lambda: run_streamed_backward(args, torch, cqsa))
+        if "error" not in sbwd:
+            log(f"bench: streamed backward {sbwd['tflops_pcie_inclusive']:.1f} useful TFLOP/s PCIe-inclusive")
     dry = None
     if stream_res is not None:
         # the billion-token case priced with this run's measured rates (plan-only, no data)
@@ -567,19 +583,23 @@ def main():
                  "h2d_gbs": head["stream"]["h2d_achievable_gbs"], "d2h_gbs": head["stream"]["d2h_achievable_gbs"]}
         dry = []
         for budget in (16 * GiB, 2 * GiB):
-            e = cqsa.cqsa_plan_estimate(1 << 30, 1, 128, cqsa.CQSA_BF16, [3], n_levels=0, budget_bytes=budget,
-                                        flags=cqsa.CQSA_FLAG_PAD, rates=rates)
-            dry.append({"n_tokens": 1 << 30, "heads": 1, "head_dim": 128, "budget_bytes": budget,
+            def one(budget=budget):
+                e = cqsa.cqsa_plan_estimate(1 << 30, 1, 128, cqsa.CQSA_BF16, [3], n_levels=0, budget_bytes=budget,
+                                            flags=cqsa.CQSA_FLAG_PAD, rates=rates)
+                return {"n_tokens": 1 << 30, "heads": 1, "head_dim": 128, "budget_bytes": budget,
                         "levels": e["l"], "task_tokens": e["task_tokens"],
                         "mode": cqsa.MODE_NAMES[e["stream_mode"]], "stream_workspace_bytes": e["stream_workspace_bytes"],
                         "host_pinned_bytes": e["host_pinned_bytes"], "bytes_h2d": e["bytes_h2d"],
                         "bytes_d2h": e["bytes_d2h"], "est_hours": round(e["t_est_s"] / 3600, 2),
-                        "attn_hours": round(e["t_attn_s"] / 3600, 2), "h2d_hours": round(e["t_h2d_s"] / 3600, 2)})
-            if sbwd is not None:
+                        "attn_hours": round(e["t_attn_s"] / 3600, 2), "h2d_hours": round(e["t_h2d_s"] / 3600, 2),
+                        "t_est_s": e["t_est_s"]}
+            dry.append(guarded(f"dry run at {budget // GiB} GiB", one))
+            ok = "error" not in dry[-1]
+            if ok and sbwd is not None and "error" not in sbwd and "error" not in stream_res:
                 # not a plan of the backward: the forward estimate scaled by the streamed backward's
                 # measured time over the streamed forward's on the 16 GiB workload
                 ratio = sbwd["wall_s"] / stream_res["wall_s"]
-                dry[-1]["bwd_hours_by_ratio"] = round(e["t_est_s"] * ratio / 3600, 1)
+                dry[-1]["bwd_hours_by_ratio"] = round(dry[-1]["t_est_s"] * ratio / 3600, 1)
                 dry[-1]["bwd_ratio_note"] = (f"extrapolation: forward estimate x {ratio:.2f}, the measured streamed "
                                              "backward / forward time of the N=212992, 16-head workload")
 

@@ -503,6 +503,7 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
     float* an;
     float* aml;
     char* o;
+    float* lse;
   } slot[2];
   for (auto& s : slot) {
     s.q = take(L.q_blk, "Q block");
@@ -511,8 +512,9 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
     s.an = fp.acc_on_device ? nullptr : reinterpret_cast<float*>(take(L.n_blk, "accumulator n block"));
     s.aml = fp.acc_on_device ? nullptr : reinterpret_cast<float*>(take(L.ml_blk, "accumulator (m, l) block"));
     s.o = take(L.o_blk, "O block");
+    s.lse = L.lse_blk ? reinterpret_cast<float*>(take(L.lse_blk, "LSE block")) : nullptr;
   }
-  float* lse_dev = reinterpret_cast<float*>(take(L.lse_all, "LSE"));
+  float* lse_dev = L.lse_all ? reinterpret_cast<float*>(take(L.lse_all, "LSE")) : nullptr;
   float* acc_n = fp.acc_on_device ? reinterpret_cast<float*>(take(L.acc_n, "accumulator n")) : nullptr;
   float* acc_ml = fp.acc_on_device ? reinterpret_cast<float*>(take(L.acc_ml, "accumulator (m, l)")) : nullptr;
 
@@ -679,7 +681,8 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
       ++n_attn;
 
       // merge into the accumulator (ascending task order per row); the final merge of a
-      // unit writes its O block and its LSE rows straight into the resident [H][N] array
+      // unit writes its O block, and its LSE rows into the resident [H][N] array or the
+      // slot's [H][unit] block
       MergeLaunch m{};
       m.dtype = p.dtype;
       m.d = p.d;
@@ -687,9 +690,9 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
       m.rows = R;
       m.final_out = last;
       m.o_out = S.o;
-      m.lse_out = lse_dev;
-      m.lse_stride = N;
-      m.lse_row0 = pu * U;
+      m.lse_out = lse_dev ? lse_dev : S.lse;
+      m.lse_stride = lse_dev ? N : U;
+      m.lse_row0 = lse_dev ? pu * U : 0;
       bool do_merge = true;
       if (fp.acc_on_device) {
         float* an = acc_n + pu * U * nrow_f;
@@ -734,6 +737,13 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
         HIP_TRY(hipMemcpyAsync(o + pu * U * H * D * e, S.o, R * H * D * e, hipMemcpyDeviceToHost, s_d));
         bytes_d2h += R * H * D * e;
         ++n_d2h;
+        if (lse != nullptr && lse_dev == nullptr) {
+          // LSE is [H][N] on the host and [H][U] in the block: one contiguous copy per head
+          for (int64_t hh = 0; hh < H; ++hh)
+            HIP_TRY(hipMemcpyAsync(lse + hh * N + pu * U, S.lse + hh * U, R * sizeof(float), hipMemcpyDeviceToHost, s_d));
+          bytes_d2h += H * R * 4;
+          n_d2h += H;
+        }
       } else if (!fp.acc_on_device) {
         const float* sn = first ? S.n : S.an;
         const float* sml = first ? S.ml : S.aml;
@@ -751,7 +761,7 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
     HIP_TRY(hipEventRecord(task_done[ti % 3], s_c));
   }
   // LSE of every row, in one copy once the last merge has written it
-  if (lse != nullptr) {
+  if (lse != nullptr && lse_dev != nullptr) {
     HIP_TRY(hipEventRecord(all_merged, s_c));
     HIP_TRY(hipStreamWaitEvent(s_d, all_merged, 0));
     HIP_TRY(tm.begin(PH_D2H, s_d, tev));

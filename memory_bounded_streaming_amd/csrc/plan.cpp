@@ -79,10 +79,15 @@ StreamLayout stream_layout(const Plan& p, bool acc_on_device, int kv_buffers) {
   s.n_blk = align_up(u * h * d * 4);
   s.ml_blk = align_up(u * h * 2 * 4);
   s.o_blk = align_up(u * h * d * e);
-  s.lse_all = align_up(h * p.n * 4);
+  // LSE of every row stays on the device (one copy back at the end) while it is a small
+  // share of the budget; otherwise each finished block's LSE goes back per head
+  const int64_t lse_all = align_up(h * p.n * 4);
+  const bool resident = p.budget == 0 || lse_all <= p.budget / 16;
+  s.lse_all = resident ? lse_all : 0;
+  s.lse_blk = resident ? 0 : align_up(h * u * 4);
   s.acc_n = acc_on_device ? align_up(p.n * h * d * 4) : 0;
   s.acc_ml = acc_on_device ? align_up(p.n * h * 2 * 4) : 0;
-  const int64_t slot = s.q_blk + s.n_blk + s.ml_blk + (acc_on_device ? 0 : s.n_blk + s.ml_blk) + s.o_blk;
+  const int64_t slot = s.q_blk + s.n_blk + s.ml_blk + (acc_on_device ? 0 : s.n_blk + s.ml_blk) + s.o_blk + s.lse_blk;
   s.total = 2 * kv_buffers * s.kv_stage + 2 * slot + s.lse_all + s.acc_n + s.acc_ml;
   return s;
 }

@@ -131,7 +131,9 @@ BwdStreamLayout bwd_stream_layout(const Plan& p, bool acc_on_device, int stage_s
 struct StreamLayout {
   int64_t kv_stage;     // one K or V staging buffer (task_tokens rows)
   int64_t q_blk, n_blk, ml_blk, o_blk;  // per ring slot (unit rows)
-  int64_t lse_all;      // LSE [H][N] fp32, resident for the call (copied back once)
+  int64_t lse_blk;      // per ring slot: LSE [H][unit] of a finished block (0 when resident)
+  int64_t lse_all;      // LSE [H][N] fp32 resident for the call and copied back once, when
+                        // it is at most 1/16 of the budget (0 otherwise)
   int64_t acc_n, acc_ml; // device accumulator (0 when on host)
   int64_t total;
 };
