@@ -555,6 +555,14 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
 
   hipEvent_t tev;
   int64_t bytes_h2d = 0, bytes_d2h = 0, bytes_d2d = 0, n_attn = 0, n_merge = 0, n_h2d = 0, n_d2h = 0;
+  // Every host <-> device copy is timed on its own (the union of the copies' intervals is
+  // the phase's busy time, as a copy trace counts it); device copies are not timed.
+  auto copy = [&](int phase, void* dst, const void* src, int64_t bytes, hipMemcpyKind kind, hipStream_t s) {
+    hipError_t e = phase >= 0 ? tm.begin(phase, s, tev) : hipSuccess;
+    if (e == hipSuccess) e = hipMemcpyAsync(dst, src, static_cast<size_t>(bytes), kind, s);
+    if (e == hipSuccess && phase >= 0) e = tm.end(phase, s);
+    return e;
+  };
   const int64_t tu = p.task_units;
   const float c2 = scale_log2(p);
   const int64_t e = p.elem_bytes();
@@ -579,7 +587,6 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
       if (progress) report(static_cast<int64_t>(ti) - 2);
     }
     if (static_cast<int64_t>(ti) >= fp.kv_buffers) HIP_TRY(hipStreamWaitEvent(s_kv, kv_free[b], 0));
-    HIP_TRY(tm.begin(PH_H2D, s_kv, tev));
     // Chunk reuse: consecutive tasks of one outer task share exactly one inner chunk
     // (a perfect difference set meets its own shift in one residue).  With two staging
     // buffers the previous task's copy of it is still resident, so those rows are copied
@@ -609,20 +616,21 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
         }
         const int64_t rows = stop - pos, dst = (g.local_offset + pos - g.global_start) * row_in;
         if (hit != nullptr) {
+          // on the copy engines: a device copy through compute units would take CUs from the
+          // partial kernel running beside it
           const int64_t src = (hit->local_offset + pos - hit->global_start) * row_in;
-          HIP_TRY(hipMemcpyAsync(kst[b] + dst, kst[b ^ 1] + src, rows * row_in, hipMemcpyDeviceToDevice, s_kv));
-          HIP_TRY(hipMemcpyAsync(vst[b] + dst, vst[b ^ 1] + src, rows * row_in, hipMemcpyDeviceToDevice, s_kv));
+          HIP_TRY(copy(-1, kst[b] + dst, kst[b ^ 1] + src, rows * row_in, hipMemcpyDeviceToDeviceNoCU, s_kv));
+          HIP_TRY(copy(-1, vst[b] + dst, vst[b ^ 1] + src, rows * row_in, hipMemcpyDeviceToDeviceNoCU, s_kv));
           bytes_d2d += 2 * rows * row_in;
         } else {
-          HIP_TRY(hipMemcpyAsync(kst[b] + dst, k + pos * row_in, rows * row_in, hipMemcpyHostToDevice, s_kv));
-          HIP_TRY(hipMemcpyAsync(vst[b] + dst, v + pos * row_in, rows * row_in, hipMemcpyHostToDevice, s_kv));
+          HIP_TRY(copy(PH_H2D, kst[b] + dst, k + pos * row_in, rows * row_in, hipMemcpyHostToDevice, s_kv));
+          HIP_TRY(copy(PH_H2D, vst[b] + dst, v + pos * row_in, rows * row_in, hipMemcpyHostToDevice, s_kv));
           bytes_h2d += 2 * rows * row_in;
           n_h2d += 2;
         }
         pos = stop;
       }
     }
-    HIP_TRY(tm.end(PH_H2D, s_kv));
     HIP_TRY(hipEventRecord(kv_ready[b], s_kv));
     HIP_TRY(hipStreamWaitEvent(s_c, kv_ready[b], 0));
     HIP_TRY(step());
@@ -639,17 +647,15 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
       if (!fp.acc_on_device && !first && last_block[pu] == blk - 1)
         HIP_TRY(hipStreamWaitEvent(s_q, slot_free[(blk - 1) % 2], 0));
       // H2D: Q block (+ accumulator block)
-      HIP_TRY(tm.begin(PH_H2D, s_q, tev));
-      HIP_TRY(hipMemcpyAsync(S.q, q + pu * U * row_in, R * row_in, hipMemcpyHostToDevice, s_q));
+      HIP_TRY(copy(PH_H2D, S.q, q + pu * U * row_in, R * row_in, hipMemcpyHostToDevice, s_q));
       bytes_h2d += R * row_in;
       ++n_h2d;
       if (!fp.acc_on_device && !first) {
-        HIP_TRY(hipMemcpyAsync(S.an, host_n + pu * U * nrow_f, R * nrow_f * 4, hipMemcpyHostToDevice, s_q));
-        HIP_TRY(hipMemcpyAsync(S.aml, host_ml + pu * U * mlrow_f, R * mlrow_f * 4, hipMemcpyHostToDevice, s_q));
+        HIP_TRY(copy(PH_H2D, S.an, host_n + pu * U * nrow_f, R * nrow_f * 4, hipMemcpyHostToDevice, s_q));
+        HIP_TRY(copy(PH_H2D, S.aml, host_ml + pu * U * mlrow_f, R * mlrow_f * 4, hipMemcpyHostToDevice, s_q));
         bytes_h2d += R * (nrow_f + mlrow_f) * 4;
         n_h2d += 2;
       }
-      HIP_TRY(tm.end(PH_H2D, s_q));
       HIP_TRY(hipEventRecord(q_ready[j], s_q));
       HIP_TRY(hipStreamWaitEvent(s_c, q_ready[j], 0));
       HIP_TRY(step());
@@ -732,28 +738,26 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
 
       // D2H: finished output block, or the accumulator block back to host memory
       HIP_TRY(hipStreamWaitEvent(s_d, c_done[j], 0));
-      HIP_TRY(tm.begin(PH_D2H, s_d, tev));
       if (last) {
-        HIP_TRY(hipMemcpyAsync(o + pu * U * H * D * e, S.o, R * H * D * e, hipMemcpyDeviceToHost, s_d));
+        HIP_TRY(copy(PH_D2H, o + pu * U * H * D * e, S.o, R * H * D * e, hipMemcpyDeviceToHost, s_d));
         bytes_d2h += R * H * D * e;
         ++n_d2h;
         if (lse != nullptr && lse_dev == nullptr) {
           // LSE is [H][N] on the host and [H][U] in the block: one contiguous copy per head
           for (int64_t hh = 0; hh < H; ++hh)
-            HIP_TRY(hipMemcpyAsync(lse + hh * N + pu * U, S.lse + hh * U, R * sizeof(float), hipMemcpyDeviceToHost, s_d));
+            HIP_TRY(copy(PH_D2H, lse + hh * N + pu * U, S.lse + hh * U, R * 4, hipMemcpyDeviceToHost, s_d));
           bytes_d2h += H * R * 4;
           n_d2h += H;
         }
       } else if (!fp.acc_on_device) {
         const float* sn = first ? S.n : S.an;
         const float* sml = first ? S.ml : S.aml;
-        HIP_TRY(hipMemcpyAsync(host_n + pu * U * nrow_f, sn, R * nrow_f * 4, hipMemcpyDeviceToHost, s_d));
-        HIP_TRY(hipMemcpyAsync(host_ml + pu * U * mlrow_f, sml, R * mlrow_f * 4, hipMemcpyDeviceToHost, s_d));
+        HIP_TRY(copy(PH_D2H, host_n + pu * U * nrow_f, sn, R * nrow_f * 4, hipMemcpyDeviceToHost, s_d));
+        HIP_TRY(copy(PH_D2H, host_ml + pu * U * mlrow_f, sml, R * mlrow_f * 4, hipMemcpyDeviceToHost, s_d));
         bytes_d2h += R * (nrow_f + mlrow_f) * 4;
         n_d2h += 2;
         last_block[pu] = blk;
       }
-      HIP_TRY(tm.end(PH_D2H, s_d));
       HIP_TRY(hipEventRecord(slot_free[j], s_d));
       HIP_TRY(step());
     }
@@ -764,9 +768,7 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
   if (lse != nullptr && lse_dev != nullptr) {
     HIP_TRY(hipEventRecord(all_merged, s_c));
     HIP_TRY(hipStreamWaitEvent(s_d, all_merged, 0));
-    HIP_TRY(tm.begin(PH_D2H, s_d, tev));
-    HIP_TRY(hipMemcpyAsync(lse, lse_dev, H * N * sizeof(float), hipMemcpyDeviceToHost, s_d));
-    HIP_TRY(tm.end(PH_D2H, s_d));
+    HIP_TRY(copy(PH_D2H, lse, lse_dev, H * N * 4, hipMemcpyDeviceToHost, s_d));
     bytes_d2h += H * N * 4;
     ++n_d2h;
   }
