@@ -306,6 +306,29 @@ cqsa_status cqsa_forward(const cqsa_plan* plan, const void* q, const void* k, co
                          int64_t workspace_bytes, void* stream, cqsa_stats* stats);
 
 /*
+ * cqsa_forward with CQSA_RES_DEVICE for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same kernels and the same result, bit for bit, but the partial slots and the forward
+ * descriptor tables live in a fixed array of device memory of the library, 256 MiB on
+ * each device the library runs on, held from this call's first use on the device until
+ * the process ends.  The plan must need at most that much:
+ *     align256(V*N*H*d*4) + align256(V*N*H*2*4) + align256(items*32) + align256(runs*16)
+ * (V = visits; e.g. N = 14,336, H = 8, d = 128 with one level of l = 3 needs 179 MB);
+ * a larger plan gets ESMALL and nothing is enqueued.  Nothing is allocated or freed, and
+ * the plan's own device tables are not used: each call copies the forward descriptor
+ * table from the plan's host memory into the array with hipMemcpyAsync on stream.
+ * The array keeps what the last call left; nothing in it is read before the call writes
+ * it.  Every call on one device shares that device's array: calls that overlap on one
+ * device (on different streams, or from several threads) race; calls on one stream are
+ * ordered.  The plan's budget is not applied (the array is the bound).
+ * q, k, v, o, lse: device pointers, layouts of cqsa_forward (lse may be NULL).
+ * Enqueued on stream; returns before the kernels finish.
+ * Errors: EINVAL (NULL or misaligned pointer), ESMALL (plan larger than the array), EHIP.
+ */
+cqsa_status cqsa_forward_noalloc(const cqsa_plan* plan, const void* q, const void* k, const void* v,
+                                 void* o, float* lse, void* stream);
+
+/*
  * Device workspace bytes cqsa_backward needs for res.  CQSA_RES_DEVICE: Delta [H][N]
  * fp32, for bf16 three transposed copies (Q, K, dO) [H][d][round_up(N, 64)], and the
  * visit slots of dQ, dK, dV [V][N][H][d] fp32 (V = prod(l_k)).  CQSA_RES_HOST_PINNED:

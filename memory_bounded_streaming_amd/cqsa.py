@@ -22,7 +22,7 @@ __all__ = [
     "MODE_NAMES", "cqsa_plan_fallback", "cqsa_debug_fail_allocations",
     "cqsa_version", "cqsa_difference_set", "cqsa_plan_create", "cqsa_plan_info_get", "cqsa_plan_schedule",
     "cqsa_plan_coverage", "cqsa_plan_destroy", "cqsa_workspace_size", "cqsa_partials", "cqsa_merge",
-    "cqsa_forward", "cqsa_backward_workspace_size", "cqsa_backward", "cqsa_plan_estimate", "cqsa_status_string", "cqsa_last_error", "Plan",
+    "cqsa_forward", "cqsa_forward_noalloc", "cqsa_backward_workspace_size", "cqsa_backward", "cqsa_plan_estimate", "cqsa_status_string", "cqsa_last_error", "Plan",
 ]
 
 CQSA_BF16, CQSA_F32 = 0, 1
@@ -107,6 +107,7 @@ EXPORTS = {
     "cqsa_merge": (ctypes.c_int, [ctypes.c_void_p] + [ctypes.c_void_p] * 5),
     "cqsa_forward": (ctypes.c_int, [ctypes.c_void_p] + [ctypes.c_void_p] * 5 +
                      [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.POINTER(Stats)]),
+    "cqsa_forward_noalloc": (ctypes.c_int, [ctypes.c_void_p] + [ctypes.c_void_p] * 6),
     "cqsa_backward_workspace_size": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_int64)]),
     "cqsa_backward": (ctypes.c_int, [ctypes.c_void_p] + [ctypes.c_void_p] * 9 +
                       [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.POINTER(Stats)]),
@@ -256,6 +257,11 @@ def cqsa_forward(plan: int, q, k, v, o, lse=None, residency: int = CQSA_RES_DEVI
     return {name: getattr(st, name) for name, _ in Stats._fields_}
 
 
+def cqsa_forward_noalloc(plan: int, q, k, v, o, lse=None, stream=None) -> None:
+    """Device-resident forward with the library's static scratch array (no allocation)."""
+    _check(load().cqsa_forward_noalloc(plan, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _stream(stream)))
+
+
 def cqsa_backward_workspace_size(plan: int, residency: int = CQSA_RES_DEVICE) -> int:
     out = ctypes.c_int64()
     _check(load().cqsa_backward_workspace_size(plan, residency, ctypes.byref(out)))
@@ -333,6 +339,9 @@ class Plan:
 
     def forward(self, *a, **kw):
         return cqsa_forward(self.handle, *a, **kw)
+
+    def forward_noalloc(self, *a, **kw):
+        return cqsa_forward_noalloc(self.handle, *a, **kw)
 
     def backward_workspace_size(self, residency=CQSA_RES_DEVICE):
         return cqsa_backward_workspace_size(self.handle, residency)

@@ -257,6 +257,17 @@ cqsa_status cqsa_forward(const cqsa_plan* plan, const void* q, const void* k, co
   });
 }
 
+cqsa_status cqsa_forward_noalloc(const cqsa_plan* plan, const void* q, const void* k, const void* v, void* o,
+                                 float* lse, void* stream) {
+  return guarded([&]() -> cqsa_status {
+    if (plan == nullptr || q == nullptr || k == nullptr || v == nullptr || o == nullptr)
+      return fail(CQSA_EINVAL, "NULL argument");
+    if (!aligned16({q, k, v, o}) || !aligned(lse, 4)) return fail(CQSA_EINVAL, kAlignWhy);
+    std::string why;
+    const cqsa_status s = cqsa::forward_static(plan->p, q, k, v, o, lse, static_cast<hipStream_t>(stream), why);
+    return s == CQSA_OK ? ok() : fail(s, why);
+  });
+}
 
 cqsa_status cqsa_backward_workspace_size(const cqsa_plan* plan, cqsa_residency res, int64_t* bytes) {
   return guarded([&]() -> cqsa_status {

@@ -277,6 +277,12 @@ cqsa_status run_partials(const Plan& p, const void* q, const void* k, const void
   DeviceTables t{};
   cqsa_status st = device_tables(p, t, why);
   if (st != CQSA_OK) return st;
+  return run_partials_with(p, q, k, v, n_out, ml_out, t.dev_items, t.dev_runs, stream, why);
+}
+
+cqsa_status run_partials_with(const Plan& p, const void* q, const void* k, const void* v, float* n_out,
+                              float* ml_out, const WorkItem* items, const KeyRun* runs, hipStream_t stream,
+                              std::string& why) {
   AttnLaunch a{};
   a.dtype = p.dtype;
   a.d = p.d;
@@ -286,8 +292,8 @@ cqsa_status run_partials(const Plan& p, const void* q, const void* k, const void
   a.v = v;
   a.n_out = n_out;
   a.ml_out = ml_out;
-  a.items = t.dev_items;
-  a.runs = t.dev_runs;
+  a.items = items;
+  a.runs = runs;
   a.n_items = static_cast<int>(p.dev_items.size());
   a.q_len = static_cast<int>(p.unit);
   a.scale_log2 = scale_log2(p);

@@ -33,12 +33,23 @@ void set_fail_allocations(int count);
 
 cqsa_status run_partials(const Plan& p, const void* q, const void* k, const void* v, float* n_out,
                          float* ml_out, hipStream_t stream, std::string& why);
+// The same launch with the forward descriptor tables (the plan's dev_items and dev_runs)
+// already on the device at items and runs.
+cqsa_status run_partials_with(const Plan& p, const void* q, const void* k, const void* v, float* n_out,
+                              float* ml_out, const WorkItem* items, const KeyRun* runs, hipStream_t stream,
+                              std::string& why);
 cqsa_status run_merge(const Plan& p, const float* n_in, const float* ml_in, void* o, float* lse,
                       hipStream_t stream, std::string& why);
 // Gradients dQ, dK, dV of the forward for upstream gradient d_o (device-resident).
 cqsa_status run_backward(const Plan& p, const void* q, const void* k, const void* v, const void* o,
                          const float* lse, const void* d_o, void* dq, void* dk, void* dv, cqsa_residency res,
                          void* ws, int64_t ws_bytes, hipStream_t stream, cqsa_stats* stats, std::string& why);
+// Device-resident forward with the partial slots and descriptor tables in the library's
+// static device array (no allocation); ESMALL when the plan needs more than it holds.
+cqsa_status forward_static(const Plan& p, const void* q, const void* k, const void* v, void* o, float* lse,
+                           hipStream_t stream, std::string& why);
+int64_t static_scratch_capacity();
+int64_t static_scratch_need(const Plan& p);
 cqsa_status run_forward(const Plan& p, const void* q, const void* k, const void* v, void* o, float* lse,
                         cqsa_residency res, void* ws, int64_t ws_bytes, hipStream_t stream,
                         cqsa_stats* stats, std::string& why);

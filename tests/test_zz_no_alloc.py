@@ -1,0 +1,106 @@
+"""cqsa_forward_noalloc: the device-resident forward whose partial slots and descriptor
+tables live in the library's static device array.
+
+GPU: two calls in a row (the second with a smaller plan, another dtype and the causal
+mask), then the first plan once more, each compared bit for bit with cqsa_forward
+(CQSA_RES_DEVICE, caller workspace) on the same inputs, and on sampled rows with the
+fp64 oracle.  CPU: the argument checks and the size limit, which return before any
+device work.
+"""
+import numpy as np
+import pytest
+
+from memory_bounded_streaming_amd import cqsa
+from memory_bounded_streaming_amd.inputs import gen_qkv, sample_rows
+from oracle.attention import attention_fp64
+from oracle.tolerance import BF16_LSE_TOL, BF16_REL_TOL, F32_ABS_TOL, F32_LSE_TOL, max_abs_err, rowwise_rel_err
+
+from gpu_util import DT, as_f64, empty_device, log, to_device, to_numpy
+
+SCRATCH_BYTES = 256 << 20
+
+# (levels, unit tokens, heads, head_dim, dtype, flags); the first needs 179 MB of the array
+CALLS = [
+    ([3], 2048, 8, 128, "bf16", 0),
+    ([3], 100, 2, 64, "f32", cqsa.CQSA_FLAG_CAUSAL),
+]
+
+
+def _run_pair(torch, case, seed):
+    levels, u, h, d, dtype, flags = case
+    n = int(np.prod([l * (l - 1) + 1 for l in levels])) * u
+    log(f"no-alloc forward l{levels} N={n} H={h} d={d} {dtype} flags={flags}")
+    q, k, v = gen_qkv(seed, n, h, d, dtype)
+    qd, kd, vd = (to_device(x, dtype) for x in (q, k, v))
+    p = cqsa.Plan(n, h, d, DT[dtype], levels, flags=flags)
+    o = empty_device((n, h, d), dtype)
+    o.view(torch.int16 if dtype == "bf16" else torch.int32).fill_(-1)   # NaN bit patterns
+    lse = torch.full((h, n), float("nan"), device="cuda")
+    p.forward_noalloc(qd, kd, vd, o, lse)
+    return p, (q, k, v), (qd, kd, vd), o, lse
+
+
+def _check_against_forward(torch, case, p, host, dev, o, lse):
+    levels, u, h, d, dtype, flags = case
+    n = o.shape[0]
+    o_ref = empty_device((n, h, d), dtype)
+    lse_ref = torch.empty((h, n), device="cuda")
+    ws = torch.empty(p.workspace_size(cqsa.CQSA_RES_DEVICE), dtype=torch.uint8, device="cuda")
+    p.forward(*dev, o_ref, lse_ref, residency=cqsa.CQSA_RES_DEVICE, workspace=ws)
+    torch.cuda.synchronize()
+    a, b = to_numpy(o, dtype), to_numpy(o_ref, dtype)
+    assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), "O differs from cqsa_forward"
+    la, lb = lse.cpu().numpy(), lse_ref.cpu().numpy()
+    assert np.array_equal(la.view(np.uint32), lb.view(np.uint32)), "LSE differs from cqsa_forward"
+    # and both agree with the oracle on sampled rows
+    rows = sample_rows(n, 48, seed=n, unit_tokens=u)
+    o_or, lse_or = attention_fp64(*host, rows=rows, dtype=dtype, causal=bool(flags & cqsa.CQSA_FLAG_CAUSAL))
+    out = as_f64(a[rows], dtype)
+    if dtype == "f32":
+        assert max_abs_err(out, o_or) <= F32_ABS_TOL
+        assert np.abs(la[:, rows] - lse_or).max() <= F32_LSE_TOL
+    else:
+        assert rowwise_rel_err(out, o_or) <= BF16_REL_TOL
+        assert np.abs(la[:, rows] - lse_or).max() <= BF16_LSE_TOL
+
+
+@pytest.mark.gpu
+def test_noalloc_matches_forward_on_two_calls_in_a_row():
+    torch = pytest.importorskip("torch")
+    first = _run_pair(torch, CALLS[0], seed=71)
+    second = _run_pair(torch, CALLS[1], seed=72)  # smaller plan, right after the first
+    torch.cuda.synchronize()
+    for case, (p, host, dev, o, lse) in ((CALLS[0], first), (CALLS[1], second)):
+        _check_against_forward(torch, case, p, host, dev, o, lse)
+    # the first plan again: the array now holds the second plan's tables and slots
+    p, host, dev, o, lse = first
+    o.view(torch.int16).fill_(-1)
+    lse.fill_(float("nan"))
+    p.forward_noalloc(*dev, o, lse)
+    torch.cuda.synchronize()
+    _check_against_forward(torch, CALLS[0], p, host, dev, o, lse)
+    for item in (first, second):
+        item[0].close()
+
+
+def test_noalloc_rejects_a_plan_larger_than_the_array():
+    # N = 57,344, H = 8, d = 128, l = 3: three visit slots of 57,344 x 8 x 130 float32 (715 MB)
+    with cqsa.Plan(57344, 8, 128, cqsa.CQSA_BF16, [3]) as p:
+        with pytest.raises(cqsa.CqsaError) as e:
+            p.forward_noalloc(256, 256, 256, 256, None)
+        assert e.value.status == -7
+        assert str(SCRATCH_BYTES) in e.value.detail
+
+
+def test_noalloc_argument_checks():
+    with cqsa.Plan(7 * 16, 1, 64, cqsa.CQSA_F32, [3]) as p:
+        with pytest.raises(cqsa.CqsaError) as e:
+            p.forward_noalloc(256, 0, 256, 256, None)
+        assert e.value.status == -1
+        with pytest.raises(cqsa.CqsaError) as e:
+            p.forward_noalloc(256, 256, 264, 256, None)   # 8-byte aligned only
+        assert e.value.status == -1
+        with pytest.raises(cqsa.CqsaError) as e:
+            p.forward_noalloc(256, 256, 256, 256, 258)    # lse not 4-byte aligned
+        assert e.value.status == -1
+    assert cqsa.load().cqsa_forward_noalloc(None, 256, 256, 256, 256, None, None) == -1
