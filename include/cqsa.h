@@ -225,7 +225,8 @@ cqsa_status cqsa_plan_schedule(const cqsa_plan* plan, int64_t* buf, int64_t cap,
  */
 cqsa_status cqsa_plan_coverage(const cqsa_plan* plan, int32_t* table, int64_t cap, int64_t* needed);
 
-/* Free a plan and any device descriptor tables it cached.  NULL is ignored. */
+/* Free a plan, the device descriptor tables it cached and the pinned host accumulator it
+ * keeps between streamed forward calls.  NULL is ignored.  No call may be running on it. */
 void cqsa_plan_destroy(cqsa_plan* plan);
 
 /*
@@ -285,9 +286,13 @@ cqsa_status cqsa_merge(const cqsa_plan* plan, const float* n_in, const float* ml
  *     Tasks run in ascending id; each task's K/V segments are gathered into device
  *     staging with hipMemcpyAsync on copy streams, double-buffered when the mode says
  *     so, query units are streamed in blocks, partials are merged into the
- *     accumulator (device, or pinned host memory with H2D/D2H round trips), and the
+ *     accumulator (device, or pinned host memory with H2D/D2H round trips: allocated by
+ *     the plan's first such call, N*H*(d+2)*4 bytes, and kept with the plan until
+ *     cqsa_plan_destroy; a call made while another uses it allocates its own), and the
  *     finished O blocks are copied back as each unit completes; LSE is kept [H][N] on
- *     the device for the call and copied back once at the end.  Device memory used is
+ *     the device for the call and copied back once at the end when that takes at most
+ *     1/16 of the budget (always without one), else copied back per unit block, one
+ *     copy per head.  Device memory used is
  *     the workspace (<= budget).  Synchronous: returns after all work is complete.  If
  *     the library must allocate the workspace and the device is out of memory, the
  *     call re-plans one level deeper (cqsa_plan_fallback, budget = free memory minus

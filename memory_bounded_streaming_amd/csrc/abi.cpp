@@ -197,6 +197,7 @@ void cqsa_plan_destroy(cqsa_plan* plan) {
   if (plan == nullptr) return;
   try {
     cqsa::free_device_tables(plan->p);
+    cqsa::free_host_cache(plan->p);
   } catch (...) {
   }
   delete plan;

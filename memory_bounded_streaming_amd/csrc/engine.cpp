@@ -244,18 +244,17 @@ cqsa_status device_tables(const Plan& p, DeviceTables& out, std::string& why) {
   return CQSA_OK;
 }
 
-int64_t table_bytes(const Plan& p) {
-  return align_up(int64_t(p.dev_items.size()) * sizeof(WorkItem)) + align_up(int64_t(p.dev_runs.size()) * sizeof(KeyRun)) +
-         align_up(int64_t(p.stream_items.size()) * sizeof(WorkItem)) +
-         align_up(int64_t(p.stream_runs.size()) * sizeof(KeyRun)) +
-         align_up(int64_t(p.dev_kitems.size()) * sizeof(WorkItem)) +
-         align_up(int64_t(p.dev_kruns.size()) * sizeof(KeyRun)) +
-         align_up(int64_t(p.bstream_items.size()) * sizeof(WorkItem)) +
-         align_up(int64_t(p.bstream_kitems.size()) * sizeof(WorkItem)) +
-         align_up(int64_t(p.bstream_kruns.size()) * sizeof(KeyRun));
-}
+int64_t table_bytes(const Plan& p) { return descriptor_bytes(p); }
 
 void set_fail_allocations(int count) { g_fail_allocs.store(count); }
+
+void free_host_cache(const Plan& p) {
+  std::lock_guard<std::mutex> lock(p.host_mu);
+  if (p.host_acc_cache) (void)hipHostFree(p.host_acc_cache);
+  p.host_acc_cache = nullptr;
+  p.host_acc_cache_bytes = 0;
+  p.host_acc_busy = false;
+}
 
 void free_device_tables(const Plan& p) {
   std::lock_guard<std::mutex> lock(p.dev_mu);
@@ -401,6 +400,7 @@ struct StreamRes {
   void* ws = nullptr;
   bool own_ws = false;
   float* host_acc = nullptr;
+  const Plan* acc_plan = nullptr;  // host_acc is the plan's cached accumulator, lent for the call
   ~StreamRes() {
     (void)hipStreamSynchronize(caller);
     for (hipStream_t x : s)
@@ -409,7 +409,34 @@ struct StreamRes {
     for (hipStream_t x : s)
       if (x) (void)hipStreamDestroy(x);
     if (own_ws && ws) (void)hipFree(ws);
-    if (host_acc) (void)hipHostFree(host_acc);
+    if (acc_plan) {
+      std::lock_guard<std::mutex> lock(acc_plan->host_mu);
+      acc_plan->host_acc_busy = false;
+    } else if (host_acc) {
+      (void)hipHostFree(host_acc);
+    }
+  }
+  // The pinned host accumulator: the plan's cached one when it is free and large enough
+  // (allocated on the first call), else one of this call's own.
+  hipError_t lend_host_acc(const Plan& p, int64_t bytes) {
+    {
+      std::lock_guard<std::mutex> lock(p.host_mu);
+      if (!p.host_acc_busy) {
+        if (p.host_acc_cache == nullptr || p.host_acc_cache_bytes < bytes) {
+          if (p.host_acc_cache) (void)hipHostFree(p.host_acc_cache);
+          p.host_acc_cache = nullptr;
+          p.host_acc_cache_bytes = 0;
+          hipError_t e = hipHostMalloc(&p.host_acc_cache, static_cast<size_t>(bytes), hipHostMallocDefault);
+          if (e != hipSuccess) return e;
+          p.host_acc_cache_bytes = bytes;
+        }
+        p.host_acc_busy = true;
+        acc_plan = &p;
+        host_acc = static_cast<float*>(p.host_acc_cache);
+        return hipSuccess;
+      }
+    }
+    return hipHostMalloc(reinterpret_cast<void**>(&host_acc), static_cast<size_t>(bytes), hipHostMallocDefault);
   }
   hipError_t event(hipEvent_t& e) {
     hipError_t r = hipEventCreateWithFlags(&e, hipEventDisableTiming);
@@ -531,8 +558,7 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
   float* host_n = nullptr;
   float* host_ml = nullptr;
   if (!fp.acc_on_device) {
-    HIP_TRY(hipHostMalloc(reinterpret_cast<void**>(&res.host_acc), N * (nrow_f + mlrow_f) * sizeof(float),
-                          hipHostMallocDefault));
+    HIP_TRY(res.lend_host_acc(p, N * (nrow_f + mlrow_f) * int64_t(sizeof(float))));
     host_n = res.host_acc;
     host_ml = res.host_acc + N * nrow_f;
   }
@@ -846,13 +872,19 @@ cqsa_status forward_stream_recover(const Plan& p, const char* q, const char* k, 
       why += "; no deeper plan fits the " + std::to_string(budget) + " bytes the device has free: " + w;
       return st;
     }
-    if (fb) free_device_tables(*fb);
+    if (fb) {
+      free_device_tables(*fb);
+      free_host_cache(*fb);
+    }
     fb = std::move(next);
     ++replans;
     why.clear();
     st = forward_stream(*fb, q, k, v, o, lse, ws, ws_bytes, caller, stats, mw, dev_oom, why);
   }
-  if (fb) free_device_tables(*fb);
+  if (fb) {
+    free_device_tables(*fb);
+    free_host_cache(*fb);
+  }
   if (st == CQSA_OK && stats) {
     stats->observed_peak_bytes = mw.peak();
     stats->device_free_at_entry = static_cast<int64_t>(mw.free0);

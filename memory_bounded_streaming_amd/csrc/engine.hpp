@@ -26,6 +26,8 @@ struct DeviceTables {
 // Descriptor tables of the plan on the current device (uploaded on first use).
 cqsa_status device_tables(const Plan& p, DeviceTables& out, std::string& why);
 void free_device_tables(const Plan& p);
+// Free the pinned host accumulator a plan keeps between streamed forward calls.
+void free_host_cache(const Plan& p);
 // Bytes of the plan's descriptor tables on a device.
 int64_t table_bytes(const Plan& p);
 // Make the next `count` device allocations of the library fail as out of memory.

@@ -350,6 +350,8 @@ void build_descriptors(Plan& p) {
                    [](const WorkItem& x, const WorkItem& y) { return x.keys > y.keys; });
 }
 
+}  // namespace
+
 int64_t descriptor_bytes(const Plan& p) {
   return align_up(int64_t(p.dev_items.size()) * sizeof(WorkItem)) +
          align_up(int64_t(p.dev_runs.size()) * sizeof(KeyRun)) +
@@ -362,27 +364,34 @@ int64_t descriptor_bytes(const Plan& p) {
          align_up(int64_t(p.stream_runs.size()) * sizeof(KeyRun));
 }
 
+namespace {
+
+// The one budget test of every staging layout (forward and backward, plan and dry run):
+// the layout's workspace plus the plan's descriptor tables fit the budget.
+bool fits_budget(const Plan& p, int64_t workspace_bytes) {
+  return p.budget == 0 || workspace_bytes + descriptor_bytes(p) <= p.budget;
+}
+
 cqsa_status choose_mode(Plan& p, std::string& why) {
   struct Cand {
     bool dev;
     int kv;
   };
   const Cand order[4] = {{true, 2}, {false, 2}, {true, 1}, {false, 1}};
-  const int64_t desc = descriptor_bytes(p);
   int64_t smallest = -1;
   for (const Cand& c : order) {
     if ((p.flags & CQSA_FLAG_HOST_ACC) && c.dev) continue;
     if ((p.flags & CQSA_FLAG_KV_SINGLE) && c.kv != 1) continue;
     const int64_t bytes = stream_layout(p, c.dev, c.kv).total;
     if (smallest < 0 || bytes < smallest) smallest = bytes;
-    if (p.budget == 0 || bytes + desc <= p.budget) {
+    if (fits_budget(p, bytes)) {
       p.stream_fp = {c.dev, c.kv, bytes};
       p.host_acc_bytes = c.dev ? 0 : p.n * p.row_part_bytes();
       return CQSA_OK;
     }
   }
   why = "no staging mode fits the budget of " + std::to_string(p.budget) + " bytes (smallest needs " +
-        std::to_string(smallest + desc) + ")";
+        std::to_string(smallest + descriptor_bytes(p)) + ")";
   return CQSA_EBUDGET;
 }
 
@@ -463,7 +472,7 @@ cqsa_status build_fixed(int64_t n, int heads, int d, cqsa_dtype dtype, const std
     if ((flags & CQSA_FLAG_HOST_ACC) && m.first) continue;
     if ((flags & CQSA_FLAG_KV_SINGLE) && m.second != 1) continue;
     const int64_t bytes = bwd_stream_layout(p, m.first, m.second).total;
-    if (budget == 0 || bytes + descriptor_bytes(p) <= budget) {
+    if (fits_budget(p, bytes)) {
       p.bwd_stream_fp = {m.first, m.second, bytes};
       break;
     }
@@ -570,23 +579,49 @@ cqsa_status build_plan(int64_t n, int heads, int d, cqsa_dtype dtype, const int3
 // ----------------------------------------------------------------------------------
 namespace {
 
-// First staging mode (in cqsa_mode order, respecting the flags) whose workspace fits.
-bool fit_mode(const Plan& p, Footprint& fp) {
+// Upper bound of descriptor_bytes from the plan's shape alone: at most one work item per
+// (task, unit) in each of the five item tables and one key run per (task, query unit, key
+// unit) in each of the four run tables.
+int64_t descriptor_bound(const Plan& p) {
+  const int64_t items = p.n_units * p.task_units, runs = items * p.task_units;
+  return 5 * align_up(items * int64_t(sizeof(WorkItem))) + 4 * align_up(runs * int64_t(sizeof(KeyRun)));
+}
+
+// First staging mode (in cqsa_mode order, respecting the flags) whose workspace fits, by
+// the budget test of cqsa_plan_create.  For a plan that cqsa_plan_create would build, the
+// descriptor tables are built here when the shape bound leaves the test open, so the dry
+// run and the plan agree at every budget; a larger plan is estimated with its tables off
+// the device (they would have to be streamed per task, a few KiB each).
+cqsa_status fit_mode(Plan& p, Footprint& fp, bool& fits, std::string& why) {
   struct Cand {
     bool dev;
     int kv;
   };
   const Cand order[4] = {{true, 2}, {false, 2}, {true, 1}, {false, 1}};
+  const bool buildable = materializable(p);
+  bool built = false;
+  fits = false;
   for (const Cand& c : order) {
     if ((p.flags & CQSA_FLAG_HOST_ACC) && c.dev) continue;
     if ((p.flags & CQSA_FLAG_KV_SINGLE) && c.kv != 1) continue;
     const int64_t bytes = stream_layout(p, c.dev, c.kv).total;
-    if (p.budget == 0 || bytes <= p.budget) {
+    bool ok = p.budget == 0 || (bytes <= p.budget && (!buildable || bytes + descriptor_bound(p) <= p.budget));
+    if (!ok && buildable && bytes <= p.budget) {
+      if (!built) {
+        const cqsa_status st = build_tasks(p, why);
+        if (st != CQSA_OK) return st;
+        build_descriptors(p);
+        built = true;
+      }
+      ok = fits_budget(p, bytes);
+    }
+    if (ok) {
       fp = {c.dev, c.kv, bytes};
-      return true;
+      fits = true;
+      return CQSA_OK;
     }
   }
-  return false;
+  return CQSA_OK;
 }
 
 }  // namespace
@@ -612,8 +647,10 @@ cqsa_status estimate_plan(int64_t n, int heads, int d, cqsa_dtype dtype, const i
         return CQSA_EINVAL;
       }
     st = plan_shape(n, heads, d, dtype, levels, budget, flags, p, why);
+    bool fits = false;
+    if (st == CQSA_OK) st = fit_mode(p, fp, fits, why);
     if (st != CQSA_OK) return st;
-    if (!fit_mode(p, fp)) {
+    if (!fits) {
       why = "no staging mode fits the budget";
       return CQSA_EBUDGET;
     }
@@ -629,7 +666,9 @@ cqsa_status estimate_plan(int64_t n, int heads, int d, cqsa_dtype dtype, const i
       if (k >= 1) levels.push_back(l);
       std::string w;
       st = plan_shape(n, heads, d, dtype, levels, budget, flags, p, w);
-      if (st == CQSA_OK && fit_mode(p, fp)) break;
+      bool fits = false;
+      if (st == CQSA_OK) st = fit_mode(p, fp, fits, w);
+      if (st == CQSA_OK && fits) break;
       if (st == CQSA_OK) st = CQSA_EBUDGET;
       why = w.empty() ? "no level count fits the budget" : w;
       if (st != CQSA_EBUDGET) {

@@ -87,6 +87,12 @@ struct Plan {
   // device copies of the descriptor tables, uploaded lazily per device
   mutable std::mutex dev_mu;
   mutable std::vector<std::pair<int, void*>> dev_tables;  // (device, allocation)
+  // pinned host accumulator of the streamed forward, kept between calls; a call that finds
+  // it in use (another thread's call on the same plan) allocates its own
+  mutable std::mutex host_mu;
+  mutable void* host_acc_cache = nullptr;
+  mutable int64_t host_acc_cache_bytes = 0;
+  mutable bool host_acc_busy = false;
 
   int64_t elem_bytes() const { return dtype == CQSA_BF16 ? 2 : 4; }
   int64_t row_in_bytes() const { return int64_t(heads) * d * elem_bytes(); }
@@ -141,6 +147,10 @@ StreamLayout stream_layout(const Plan& p, bool acc_on_device, int kv_buffers);
 
 constexpr int64_t kAlign = 256;
 inline int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Device bytes of a built plan's descriptor tables (0 for a plan whose tasks were not
+// built); every budget test adds them to the layout's workspace.
+int64_t descriptor_bytes(const Plan& p);
 
 // Build a plan; on failure returns the status and fills why.
 cqsa_status build_plan(int64_t n, int heads, int d, cqsa_dtype dtype, const int32_t* ls,

@@ -361,3 +361,66 @@ def test_last_error_is_per_thread(lib):
         t.join()
     assert "l=7" in results[0] and results[2] == results[0]
     assert "1..10" in results[1] and results[3] == results[1]
+
+
+def _create_or_none(n, h, d, levels, budget, n_levels=None):
+    try:
+        with cqsa.Plan(n, h, d, cqsa.CQSA_BF16, levels, n_levels=n_levels, budget_bytes=budget,
+                       flags=cqsa.CQSA_FLAG_PAD) as p:
+            return p.info["levels"], p.info["stream_mode"], p.info["stream_workspace_bytes"]
+    except cqsa.CqsaError as e:
+        assert e.status in (-4, -6)  # over the budget, or too deep a plan to build
+        return None if e.status == -4 else "unbuildable"
+
+
+def _estimate_or_none(n, h, d, levels, budget, n_levels=None):
+    try:
+        e = cqsa.cqsa_plan_estimate(n, h, d, cqsa.CQSA_BF16, levels, n_levels=n_levels, budget_bytes=budget,
+                                    flags=cqsa.CQSA_FLAG_PAD, rates=RATES)
+        return e["levels"], e["stream_mode"], e["stream_workspace_bytes"]
+    except cqsa.CqsaError as e:
+        assert e.status == -4
+        return None
+
+
+def _built(made, field):
+    """A field of a built plan's (levels, mode, workspace); 99 when there is none."""
+    return made[field] if isinstance(made, tuple) else 99
+
+
+def _first_budget(pred, lo=1, hi=64 * GiB):
+    """Smallest budget in (lo, hi] for which pred holds (pred monotonic in the budget)."""
+    assert pred(hi)
+    while hi - lo > 1:
+        mid = (lo + hi) // 2
+        if pred(mid):
+            hi = mid
+        else:
+            lo = mid
+    return hi
+
+
+@pytest.mark.parametrize("n,h,d,levels,n_levels", [
+    (57344, 8, 128, [3], None), (212992, 16, 128, [4], None), (7 * 13 * 40 + 5, 2, 64, [3, 4], None),
+    (1376256, 8, 128, [5], None), (7 * 7 * 64 * 4, 2, 64, [3], 0), (7 * 7 * 7 * 30, 1, 128, [3], 0)])
+def test_estimate_and_plan_agree_at_budget_edges(n, h, d, levels, n_levels):
+    """cqsa_plan_estimate applies cqsa_plan_create's budget test (workspace + descriptor
+    tables), so at every budget where the plan's choice changes -- the smallest budget it
+    fits, each staging mode's threshold, each depth of the automatic recursion -- both
+    give the same depth, mode and workspace one byte below and at the edge."""
+    edges = set()
+    for mode in (1, 2, 3, 4):
+        pred = lambda b, m=mode: _built(_create_or_none(n, h, d, levels, b, n_levels), 1) <= m  # noqa: E731
+        if pred(64 * GiB):
+            edges.add(_first_budget(pred))
+    if n_levels == 0:
+        for depth in (1, 2, 3):
+            pred = lambda b, k=depth: _built(_create_or_none(n, h, d, levels, b, n_levels), 0) <= k  # noqa: E731
+            if pred(64 * GiB):
+                edges.add(_first_budget(pred))
+    assert edges
+    for b in sorted(edges):
+        for budget in (b - 1, b):
+            made = _create_or_none(n, h, d, levels, budget, n_levels)
+            if made != "unbuildable":
+                assert _estimate_or_none(n, h, d, levels, budget, n_levels) == made, budget
