@@ -19,6 +19,7 @@
 #include <algorithm>
 #include <atomic>
 #include <chrono>
+#include <deque>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -389,6 +390,12 @@ cqsa_status forward_device(const Plan& p, const void* q, const void* k, const vo
   return CQSA_OK;
 }
 
+// How many tasks the host may enqueue ahead of the one the device is finishing.
+#ifndef CQSA_TASKS_AHEAD
+#define CQSA_TASKS_AHEAD 2
+#endif
+constexpr int kTasksAhead = CQSA_TASKS_AHEAD;
+
 // RAII holder of the stream engine's HIP objects.
 // The engine adds three streams (K/V copies, Q copies, D2H) to the caller's stream,
 // which runs the kernels: with four hardware queues per process (the runtime's
@@ -566,10 +573,11 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
   for (auto& s : res.s) HIP_TRY(hipStreamCreateWithFlags(&s, hipStreamNonBlocking));
   mw.poll();
   hipStream_t s_kv = res.s[0], s_q = res.s[1], s_c = caller, s_d = res.s[2];
-  hipEvent_t start, kv_ready[2], kv_free[2], q_ready[2], c_done[2], slot_free[2], task_done[3], all_merged;
+  hipEvent_t start, kv_ready[2], kv_free[2], q_ready[2], c_done[2], slot_free[2], task_done[kTasksAhead + 1],
+      all_merged;
   HIP_TRY(res.event(start));
   HIP_TRY(res.event(all_merged));
-  for (int i = 0; i < 3; ++i) HIP_TRY(res.event(task_done[i]));
+  for (int i = 0; i <= kTasksAhead; ++i) HIP_TRY(res.event(task_done[i]));
   for (int i = 0; i < 2; ++i) {
     HIP_TRY(res.event(kv_ready[i]));
     HIP_TRY(res.event(kv_free[i]));
@@ -609,14 +617,67 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
                  static_cast<long long>(n_tasks), s);
     std::fflush(stderr);
   };
+  // Device-to-host copies are enqueued only once the kernels they wait for have finished:
+  // a copy enqueued behind a wait on another stream's event, long before that event
+  // completes, ran at a fraction of the link's rate (12.8 against 56.8 GB/s, more often the
+  // further ahead the host ran).  The host therefore stays two blocks ahead of the device:
+  // before block k's inputs it waits for block k-2's kernels and enqueues that block's
+  // copies, which frees the ring slot block k reuses.
+  struct PendingD2H {
+    int64_t blk;
+    int j;
+    int64_t pu, R;
+    bool first, last;
+  };
+  std::deque<PendingD2H> pending;
+  hipEvent_t last_free = nullptr;  // recorded after the last device-to-host copy enqueued
+  auto flush_d2h = [&](int64_t upto) -> hipError_t {
+    while (!pending.empty() && pending.front().blk <= upto) {
+      const PendingD2H r = pending.front();
+      pending.pop_front();
+      const Slot& S = slot[r.j];
+      hipError_t err = hipEventSynchronize(c_done[r.j]);
+      if (err == hipSuccess) err = hipStreamWaitEvent(s_d, c_done[r.j], 0);
+      if (err != hipSuccess) return err;
+      if (r.last) {
+        err = copy(PH_D2H, o + r.pu * U * H * D * e, S.o, r.R * H * D * e, hipMemcpyDeviceToHost, s_d);
+        if (err != hipSuccess) return err;
+        bytes_d2h += r.R * H * D * e;
+        ++n_d2h;
+        if (lse != nullptr && lse_dev == nullptr) {
+          // LSE is [H][N] on the host and [H][U] in the block: one contiguous copy per head
+          for (int64_t hh = 0; hh < H && err == hipSuccess; ++hh)
+            err = copy(PH_D2H, lse + hh * N + r.pu * U, S.lse + hh * U, r.R * 4, hipMemcpyDeviceToHost, s_d);
+          if (err != hipSuccess) return err;
+          bytes_d2h += H * r.R * 4;
+          n_d2h += H;
+        }
+      } else if (!fp.acc_on_device) {
+        const float* sn = r.first ? S.n : S.an;
+        const float* sml = r.first ? S.ml : S.aml;
+        err = copy(PH_D2H, host_n + r.pu * U * nrow_f, sn, r.R * nrow_f * 4, hipMemcpyDeviceToHost, s_d);
+        if (err == hipSuccess)
+          err = copy(PH_D2H, host_ml + r.pu * U * mlrow_f, sml, r.R * mlrow_f * 4, hipMemcpyDeviceToHost, s_d);
+        if (err != hipSuccess) return err;
+        bytes_d2h += r.R * (nrow_f + mlrow_f) * 4;
+        n_d2h += 2;
+      }
+      err = hipEventRecord(slot_free[r.j], s_d);
+      last_free = slot_free[r.j];
+      if (err == hipSuccess) err = step();
+      if (err != hipSuccess) return err;
+      mw.poll();
+    }
+    return hipSuccess;
+  };
   for (size_t ti = 0; ti < p.tasks.size(); ++ti) {
     const Task& task = p.tasks[ti];
     const int b = static_cast<int>(ti % fp.kv_buffers);
     // keep the host at most two tasks ahead of the GPU
-    if (ti >= 2) {
-      HIP_TRY(hipEventSynchronize(task_done[(ti - 2) % 3]));
+    if (ti >= kTasksAhead) {
+      HIP_TRY(hipEventSynchronize(task_done[(ti - kTasksAhead) % (kTasksAhead + 1)]));
       mw.poll();
-      if (progress) report(static_cast<int64_t>(ti) - 2);
+      if (progress) report(static_cast<int64_t>(ti) - kTasksAhead);
     }
     if (static_cast<int64_t>(ti) >= fp.kv_buffers) HIP_TRY(hipStreamWaitEvent(s_kv, kv_free[b], 0));
     // Chunk reuse: consecutive tasks of one outer task share exactly one inner chunk
@@ -675,9 +736,13 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
       if (R == 0) continue;               // a unit of padding only: nothing to compute or copy
       const int visit = task.slot[a];
       const bool first = visit == 0, last = visit == p.visits - 1;
-      if (blk >= 2) HIP_TRY(hipStreamWaitEvent(s_q, slot_free[j], 0));
-      if (!fp.acc_on_device && !first && last_block[pu] == blk - 1)
-        HIP_TRY(hipStreamWaitEvent(s_q, slot_free[(blk - 1) % 2], 0));
+      // the slot's previous block must be copied out first, and so must the previous block
+      // when it held this unit's accumulator
+      const bool needs_prev = !fp.acc_on_device && !first && last_block[pu] == blk - 1;
+      HIP_TRY(flush_d2h(needs_prev ? blk - 1 : blk - 2));
+      // the copies stay ordered on their stream: waiting for the last one enqueued covers
+      // this slot's previous block and every earlier accumulator block
+      if (last_free != nullptr) HIP_TRY(hipStreamWaitEvent(s_q, last_free, 0));
       // H2D: Q block (+ accumulator block)
       HIP_TRY(copy(PH_H2D, S.q, q + pu * U * row_in, R * row_in, hipMemcpyHostToDevice, s_q));
       bytes_h2d += R * row_in;
@@ -768,34 +833,14 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
       HIP_TRY(hipEventRecord(c_done[j], s_c));
       HIP_TRY(step());
 
-      // D2H: finished output block, or the accumulator block back to host memory
-      HIP_TRY(hipStreamWaitEvent(s_d, c_done[j], 0));
-      if (last) {
-        HIP_TRY(copy(PH_D2H, o + pu * U * H * D * e, S.o, R * H * D * e, hipMemcpyDeviceToHost, s_d));
-        bytes_d2h += R * H * D * e;
-        ++n_d2h;
-        if (lse != nullptr && lse_dev == nullptr) {
-          // LSE is [H][N] on the host and [H][U] in the block: one contiguous copy per head
-          for (int64_t hh = 0; hh < H; ++hh)
-            HIP_TRY(copy(PH_D2H, lse + hh * N + pu * U, S.lse + hh * U, R * 4, hipMemcpyDeviceToHost, s_d));
-          bytes_d2h += H * R * 4;
-          n_d2h += H;
-        }
-      } else if (!fp.acc_on_device) {
-        const float* sn = first ? S.n : S.an;
-        const float* sml = first ? S.ml : S.aml;
-        HIP_TRY(copy(PH_D2H, host_n + pu * U * nrow_f, sn, R * nrow_f * 4, hipMemcpyDeviceToHost, s_d));
-        HIP_TRY(copy(PH_D2H, host_ml + pu * U * mlrow_f, sml, R * mlrow_f * 4, hipMemcpyDeviceToHost, s_d));
-        bytes_d2h += R * (nrow_f + mlrow_f) * 4;
-        n_d2h += 2;
-        last_block[pu] = blk;
-      }
-      HIP_TRY(hipEventRecord(slot_free[j], s_d));
-      HIP_TRY(step());
+      // D2H of this block: enqueued later, once its kernels have finished (flush_d2h)
+      pending.push_back({blk, j, pu, R, first, last});
+      if (!fp.acc_on_device && !last) last_block[pu] = blk;
     }
     HIP_TRY(hipEventRecord(kv_free[b], s_c));  // after the task's last launch on s_c
-    HIP_TRY(hipEventRecord(task_done[ti % 3], s_c));
+    HIP_TRY(hipEventRecord(task_done[ti % (kTasksAhead + 1)], s_c));
   }
+  HIP_TRY(flush_d2h(blk));
   // LSE of every row, in one copy once the last merge has written it
   if (lse != nullptr && lse_dev != nullptr) {
     HIP_TRY(hipEventRecord(all_merged, s_c));
@@ -808,7 +853,7 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
   for (hipStream_t s : res.s) HIP_TRY(hipStreamSynchronize(s));
   mw.poll();
   if (progress)
-    for (int64_t t = std::max<int64_t>(0, n_tasks - 2); t < n_tasks; ++t) report(t);
+    for (int64_t t = std::max<int64_t>(0, n_tasks - kTasksAhead); t < n_tasks; ++t) report(t);
   HIP_TRY(hipGetLastError());
   if (canary.on) {
     const std::string bad = canary.check();
