@@ -397,11 +397,12 @@ cqsa_status forward_device(const Plan& p, const void* q, const void* k, const vo
 constexpr int kTasksAhead = CQSA_TASKS_AHEAD;
 
 // RAII holder of the stream engine's HIP objects.
-// The engine adds three streams (K/V copies, Q copies, D2H) to the caller's stream,
-// which runs the kernels: with four hardware queues per process (the runtime's
-// default), a fifth stream would share a queue with another and serialize behind it.
+// The engine adds two streams (K/V staging copies; query-unit copies in and out) to the
+// caller's stream, which runs the kernels.  Copies out share the stream of the copies in:
+// on a stream of their own, behind a wait for another stream's event, the runtime ran
+// them at a fraction of the link's rate or as copy kernels on the compute units.
 struct StreamRes {
-  hipStream_t s[3] = {nullptr, nullptr, nullptr};  // kv, q, d2h
+  hipStream_t s[2] = {nullptr, nullptr};  // kv, io
   hipStream_t caller = nullptr;
   std::vector<hipEvent_t> events;
   void* ws = nullptr;
@@ -572,9 +573,11 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
   res.caller = caller;
   for (auto& s : res.s) HIP_TRY(hipStreamCreateWithFlags(&s, hipStreamNonBlocking));
   mw.poll();
-  hipStream_t s_kv = res.s[0], s_q = res.s[1], s_c = caller, s_d = res.s[2];
-  hipEvent_t start, kv_ready[2], kv_free[2], q_ready[2], c_done[2], slot_free[2], task_done[kTasksAhead + 1],
-      all_merged;
+  // K/V staging copies on one stream; the query-unit copies in (Q and accumulator blocks)
+  // and out (accumulator, O and LSE blocks) on another, in the order they are needed; the
+  // kernels on the caller's stream
+  hipStream_t s_kv = res.s[0], s_io = res.s[1], s_c = caller;
+  hipEvent_t start, kv_ready[2], kv_free[2], q_ready[2], c_done[2], task_done[kTasksAhead + 1], all_merged;
   HIP_TRY(res.event(start));
   HIP_TRY(res.event(all_merged));
   for (int i = 0; i <= kTasksAhead; ++i) HIP_TRY(res.event(task_done[i]));
@@ -583,14 +586,14 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
     HIP_TRY(res.event(kv_free[i]));
     HIP_TRY(res.event(q_ready[i]));
     HIP_TRY(res.event(c_done[i]));
-    HIP_TRY(res.event(slot_free[i]));
   }
   PhaseTimer tm;
   tm.on = stats != nullptr;
   HIP_TRY(tm.start(caller));
   if (canary.on) HIP_TRY(canary.fill(caller));
   HIP_TRY(hipEventRecord(start, caller));
-  for (hipStream_t s : res.s) HIP_TRY(hipStreamWaitEvent(s, start, 0));
+  HIP_TRY(hipStreamWaitEvent(s_kv, start, 0));
+  HIP_TRY(hipStreamWaitEvent(s_io, start, 0));
   auto step = [&]() -> hipError_t { return sync ? hipDeviceSynchronize() : hipSuccess; };
 
   hipEvent_t tev;
@@ -617,12 +620,13 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
                  static_cast<long long>(n_tasks), s);
     std::fflush(stderr);
   };
-  // Device-to-host copies are enqueued only once the kernels they wait for have finished:
-  // a copy enqueued behind a wait on another stream's event, long before that event
-  // completes, ran at a fraction of the link's rate (12.8 against 56.8 GB/s, more often the
-  // further ahead the host ran).  The host therefore stays two blocks ahead of the device:
-  // before block k's inputs it waits for block k-2's kernels and enqueues that block's
-  // copies, which frees the ring slot block k reuses.
+  // Device-to-host copies are enqueued only once the kernels they wait for have finished,
+  // on the stream that then carries the next inputs: a copy enqueued behind a wait on
+  // another stream's event, long before that event completes, ran at a fraction of the
+  // link's rate (12.8 against 56.8 GB/s, more often the further ahead the host ran).  The
+  // host therefore stays two blocks ahead of the device: before block k's inputs it waits
+  // for block k-2's kernels and enqueues that block's copies, which precede block k's
+  // inputs into the same ring slot on the stream.
   struct PendingD2H {
     int64_t blk;
     int j;
@@ -630,24 +634,23 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
     bool first, last;
   };
   std::deque<PendingD2H> pending;
-  hipEvent_t last_free = nullptr;  // recorded after the last device-to-host copy enqueued
   auto flush_d2h = [&](int64_t upto) -> hipError_t {
     while (!pending.empty() && pending.front().blk <= upto) {
       const PendingD2H r = pending.front();
       pending.pop_front();
       const Slot& S = slot[r.j];
+      // the host has seen the block's kernels finish, so the copies need no wait on the device
       hipError_t err = hipEventSynchronize(c_done[r.j]);
-      if (err == hipSuccess) err = hipStreamWaitEvent(s_d, c_done[r.j], 0);
       if (err != hipSuccess) return err;
       if (r.last) {
-        err = copy(PH_D2H, o + r.pu * U * H * D * e, S.o, r.R * H * D * e, hipMemcpyDeviceToHost, s_d);
+        err = copy(PH_D2H, o + r.pu * U * H * D * e, S.o, r.R * H * D * e, hipMemcpyDeviceToHost, s_io);
         if (err != hipSuccess) return err;
         bytes_d2h += r.R * H * D * e;
         ++n_d2h;
         if (lse != nullptr && lse_dev == nullptr) {
           // LSE is [H][N] on the host and [H][U] in the block: one contiguous copy per head
           for (int64_t hh = 0; hh < H && err == hipSuccess; ++hh)
-            err = copy(PH_D2H, lse + hh * N + r.pu * U, S.lse + hh * U, r.R * 4, hipMemcpyDeviceToHost, s_d);
+            err = copy(PH_D2H, lse + hh * N + r.pu * U, S.lse + hh * U, r.R * 4, hipMemcpyDeviceToHost, s_io);
           if (err != hipSuccess) return err;
           bytes_d2h += H * r.R * 4;
           n_d2h += H;
@@ -655,16 +658,14 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
       } else if (!fp.acc_on_device) {
         const float* sn = r.first ? S.n : S.an;
         const float* sml = r.first ? S.ml : S.aml;
-        err = copy(PH_D2H, host_n + r.pu * U * nrow_f, sn, r.R * nrow_f * 4, hipMemcpyDeviceToHost, s_d);
+        err = copy(PH_D2H, host_n + r.pu * U * nrow_f, sn, r.R * nrow_f * 4, hipMemcpyDeviceToHost, s_io);
         if (err == hipSuccess)
-          err = copy(PH_D2H, host_ml + r.pu * U * mlrow_f, sml, r.R * mlrow_f * 4, hipMemcpyDeviceToHost, s_d);
+          err = copy(PH_D2H, host_ml + r.pu * U * mlrow_f, sml, r.R * mlrow_f * 4, hipMemcpyDeviceToHost, s_io);
         if (err != hipSuccess) return err;
         bytes_d2h += r.R * (nrow_f + mlrow_f) * 4;
         n_d2h += 2;
       }
-      err = hipEventRecord(slot_free[r.j], s_d);
-      last_free = slot_free[r.j];
-      if (err == hipSuccess) err = step();
+      err = step();
       if (err != hipSuccess) return err;
       mw.poll();
     }
@@ -739,21 +740,19 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
       // the slot's previous block must be copied out first, and so must the previous block
       // when it held this unit's accumulator
       const bool needs_prev = !fp.acc_on_device && !first && last_block[pu] == blk - 1;
+      // (the same stream carries this block's inputs, so they follow those copies)
       HIP_TRY(flush_d2h(needs_prev ? blk - 1 : blk - 2));
-      // the copies stay ordered on their stream: waiting for the last one enqueued covers
-      // this slot's previous block and every earlier accumulator block
-      if (last_free != nullptr) HIP_TRY(hipStreamWaitEvent(s_q, last_free, 0));
       // H2D: Q block (+ accumulator block)
-      HIP_TRY(copy(PH_H2D, S.q, q + pu * U * row_in, R * row_in, hipMemcpyHostToDevice, s_q));
+      HIP_TRY(copy(PH_H2D, S.q, q + pu * U * row_in, R * row_in, hipMemcpyHostToDevice, s_io));
       bytes_h2d += R * row_in;
       ++n_h2d;
       if (!fp.acc_on_device && !first) {
-        HIP_TRY(copy(PH_H2D, S.an, host_n + pu * U * nrow_f, R * nrow_f * 4, hipMemcpyHostToDevice, s_q));
-        HIP_TRY(copy(PH_H2D, S.aml, host_ml + pu * U * mlrow_f, R * mlrow_f * 4, hipMemcpyHostToDevice, s_q));
+        HIP_TRY(copy(PH_H2D, S.an, host_n + pu * U * nrow_f, R * nrow_f * 4, hipMemcpyHostToDevice, s_io));
+        HIP_TRY(copy(PH_H2D, S.aml, host_ml + pu * U * mlrow_f, R * mlrow_f * 4, hipMemcpyHostToDevice, s_io));
         bytes_h2d += R * (nrow_f + mlrow_f) * 4;
         n_h2d += 2;
       }
-      HIP_TRY(hipEventRecord(q_ready[j], s_q));
+      HIP_TRY(hipEventRecord(q_ready[j], s_io));
       HIP_TRY(hipStreamWaitEvent(s_c, q_ready[j], 0));
       HIP_TRY(step());
 
@@ -844,8 +843,8 @@ cqsa_status forward_stream(const Plan& p, const char* q, const char* k, const ch
   // LSE of every row, in one copy once the last merge has written it
   if (lse != nullptr && lse_dev != nullptr) {
     HIP_TRY(hipEventRecord(all_merged, s_c));
-    HIP_TRY(hipStreamWaitEvent(s_d, all_merged, 0));
-    HIP_TRY(copy(PH_D2H, lse, lse_dev, H * N * 4, hipMemcpyDeviceToHost, s_d));
+    HIP_TRY(hipEventSynchronize(all_merged));
+    HIP_TRY(copy(PH_D2H, lse, lse_dev, H * N * 4, hipMemcpyDeviceToHost, s_io));
     bytes_d2h += H * N * 4;
     ++n_d2h;
   }
