@@ -955,7 +955,7 @@ cqsa_status forward_stream_recover(const Plan& p, const char* q, const char* k, 
 namespace {
 
 struct BwdStreamRes {
-  hipStream_t s[2] = {nullptr, nullptr};  // h2d, d2h
+  hipStream_t s[2] = {nullptr, nullptr};  // staging, io
   hipStream_t caller = nullptr;
   std::vector<hipEvent_t> events;
   void* ws = nullptr;
@@ -1059,15 +1059,17 @@ cqsa_status backward_stream(const Plan& p, const char* q, const char* k, const c
 
   for (auto& s : R.s) HIP_TRY(hipStreamCreateWithFlags(&s, hipStreamNonBlocking));
   mw.poll();
-  hipStream_t s_h = R.s[0], s_d = R.s[1], s_c = caller;
-  hipEvent_t start, staged, stage_free[2], acc_ready[2], c_done[2], slot_free[2];
+  // task staging (and the Delta pass) on one stream; a unit's accumulator blocks in and its
+  // gradient or accumulator blocks out on another, in the order they are needed; the
+  // kernels on the caller's stream
+  hipStream_t s_h = R.s[0], s_io = R.s[1], s_c = caller;
+  hipEvent_t start, staged, stage_free[2], acc_ready[2], c_done[2];
   HIP_TRY(R.event(start));
   HIP_TRY(R.event(staged));
   for (int i = 0; i < 2; ++i) {
     HIP_TRY(R.event(stage_free[i]));
     HIP_TRY(R.event(acc_ready[i]));
     HIP_TRY(R.event(c_done[i]));
-    HIP_TRY(R.event(slot_free[i]));
   }
   PhaseTimer tm;
   tm.on = stats != nullptr;
@@ -1113,6 +1115,40 @@ cqsa_status backward_stream(const Plan& p, const char* q, const char* k, const c
   const float scale = static_cast<float>(1.0 / std::sqrt(double(p.d)));
   std::vector<int64_t> last_block(p.n_units, -4);
   int64_t blk = 0;
+  // As in the forward: a block's copies out are enqueued once its kernels have finished
+  // (the host stays two blocks ahead), on the stream that then carries the next block's
+  // accumulator blocks in.
+  struct PendingOut {
+    int64_t blk;
+    int j;
+    int64_t pu, rows;
+    bool last;
+  };
+  std::deque<PendingOut> pending;
+  auto flush_out = [&](int64_t upto) -> hipError_t {
+    while (!pending.empty() && pending.front().blk <= upto) {
+      const PendingOut r = pending.front();
+      pending.pop_front();
+      hipError_t err = hipEventSynchronize(c_done[r.j]);
+      if (err != hipSuccess) return err;
+      if (!r.last && dev_acc) continue;
+      const Slot& S = slot[r.j];
+      err = tm.begin(PH_D2H, s_io, tev);
+      for (int g = 0; g < 3 && err == hipSuccess; ++g) {
+        if (r.last) {
+          err = hipMemcpyAsync(outs[g] + r.pu * U * hd * e, S.out[g], r.rows * hd * e, hipMemcpyDeviceToHost, s_io);
+          bytes_d2h += r.rows * hd * e;
+        } else {
+          err = hipMemcpyAsync(host_acc[g] + r.pu * U * hd, S.temp[g], r.rows * hd * 4, hipMemcpyDeviceToHost, s_io);
+          bytes_d2h += r.rows * hd * 4;
+        }
+        ++n_d2h;
+      }
+      if (err == hipSuccess) err = tm.end(PH_D2H, s_io);
+      if (err != hipSuccess) return err;
+    }
+    return hipSuccess;
+  };
   for (size_t ti = 0; ti < p.tasks.size(); ++ti) {
     const Task& task = p.tasks[ti];
     // stage the task into its set, once the kernels of the set's previous task are done
@@ -1164,20 +1200,22 @@ cqsa_status backward_stream(const Plan& p, const char* q, const char* k, const c
       if (rows == 0) continue;
       const int visit = task.slot[a];
       const bool first = visit == 0, last = visit == p.visits - 1;
-      if (blk >= 2) HIP_TRY(hipStreamWaitEvent(s_c, slot_free[j], 0));
+      // the slot's previous block is copied out first, and so is the previous block when it
+      // held this unit's accumulator; this block's kernels wait for those copies (they
+      // rewrite the slot) and for its own accumulator blocks in
+      const bool needs_prev = !dev_acc && !first && last_block[pu] == blk - 1;
+      HIP_TRY(flush_out(needs_prev ? blk - 1 : blk - 2));
       if (!dev_acc && !first) {
         // the unit's accumulator blocks back from host memory
-        if (blk >= 2) HIP_TRY(hipStreamWaitEvent(s_h, slot_free[j], 0));
-        if (last_block[pu] == blk - 1) HIP_TRY(hipStreamWaitEvent(s_h, slot_free[(blk - 1) % 2], 0));
-        HIP_TRY(tm.begin(PH_H2D, s_h, tev));
+        HIP_TRY(tm.begin(PH_H2D, s_io, tev));
         for (int g = 0; g < 3; ++g)
-          HIP_TRY(hipMemcpyAsync(S.temp[g], host_acc[g] + pu * U * hd, rows * hd * 4, hipMemcpyHostToDevice, s_h));
-        HIP_TRY(tm.end(PH_H2D, s_h));
+          HIP_TRY(hipMemcpyAsync(S.temp[g], host_acc[g] + pu * U * hd, rows * hd * 4, hipMemcpyHostToDevice, s_io));
+        HIP_TRY(tm.end(PH_H2D, s_io));
         bytes_h2d += 3 * rows * hd * 4;
         n_h2d += 3;
-        HIP_TRY(hipEventRecord(acc_ready[j], s_h));
-        HIP_TRY(hipStreamWaitEvent(s_c, acc_ready[j], 0));
       }
+      HIP_TRY(hipEventRecord(acc_ready[j], s_io));
+      HIP_TRY(hipStreamWaitEvent(s_c, acc_ready[j], 0));
       BwdLaunch b{};
       b.dtype = p.dtype;
       b.d = p.d;
@@ -1224,26 +1262,13 @@ cqsa_status backward_stream(const Plan& p, const char* q, const char* k, const c
       }
       HIP_TRY(tm.end(PH_MERGE, s_c));
       HIP_TRY(hipEventRecord(c_done[j], s_c));
-      HIP_TRY(hipStreamWaitEvent(s_d, c_done[j], 0));
-      HIP_TRY(tm.begin(PH_D2H, s_d, tev));
-      for (int g = 0; g < 3; ++g) {
-        if (last) {
-          HIP_TRY(hipMemcpyAsync(outs[g] + pu * U * hd * e, S.out[g], rows * hd * e, hipMemcpyDeviceToHost, s_d));
-          bytes_d2h += rows * hd * e;
-          ++n_d2h;
-        } else if (!dev_acc) {
-          HIP_TRY(hipMemcpyAsync(host_acc[g] + pu * U * hd, S.temp[g], rows * hd * 4, hipMemcpyDeviceToHost, s_d));
-          bytes_d2h += rows * hd * 4;
-          ++n_d2h;
-        }
-      }
+      pending.push_back({blk, j, pu, rows, last});
       if (!dev_acc && !last) last_block[pu] = blk;
-      HIP_TRY(tm.end(PH_D2H, s_d));
-      HIP_TRY(hipEventRecord(slot_free[j], s_d));
     }
     HIP_TRY(hipEventRecord(stage_free[sb], s_c));
     mw.poll();
   }
+  HIP_TRY(flush_out(blk));
   HIP_TRY(hipStreamSynchronize(s_c));
   for (hipStream_t s : R.s) HIP_TRY(hipStreamSynchronize(s));
   mw.poll();
