@@ -11,9 +11,10 @@
 // cannot hold the accumulator).  Tasks run in ascending id.  For each task the K/V
 // segments are gathered into a staging buffer on the K/V copy stream; query units are
 // streamed through a two-slot ring (Q block, partial block, accumulator block, output
-// block) on the Q copy stream; the caller's stream runs the partial kernel and the
-// merge; the D2H stream returns accumulator or output blocks.  Events order every reuse of a
-// staging buffer or ring slot.
+// block) on the unit copy stream, which also returns each unit's accumulator or output
+// blocks once its kernels have finished; the caller's stream runs the partial kernel and
+// the merge.  Events order every reuse of a staging buffer; the unit stream's own order,
+// behind the host's wait for a block's kernels, orders every reuse of a ring slot.
 #include "engine.hpp"
 
 #include <algorithm>
