@@ -11,8 +11,8 @@
  *     N tokens -> c = l(l-1)+1 chunks -> c subsequences of l chunks, every chunk
  *     pair exactly once; section "The Recursive Benefit": divide again until a
  *     task fits the memory budget; section "Implementation: From High-Level Logic
- *     to GPU Kernels": CQS Mask, stream Q_i/K_i/V_i to the GPU, local numerators
- *     and denominators, aggregation in host memory.
+ *     to GPU Kernels": the CQS Mask, each task's Q, K and V moved to the device,
+ *     per-task softmax sums, aggregation in host memory.
  *   - Lattice summary of arXiv:2604.20819: subproblems that fit arbitrary memory
  *     budgets; recomposition equals full-sequence attention.
  *
@@ -171,8 +171,8 @@ const char* cqsa_version(void);
 
 /*
  * Perfect difference set of size l (the cyclic quorum behind CQS Divide; "Stream-CQSA:
- * Exact Out-of-Memory Recovery for Attention", abstract: "derived from the theory of
- * cyclic quorum sets").  Writes the lexicographically smallest sorted set D of l
+ * Exact Out-of-Memory Recovery for Attention", abstract: the division rests on cyclic
+ * quorum sets).  Writes the lexicographically smallest sorted set D of l
  * residues mod c = l(l-1)+1 with {0,1} in D whose nonzero differences cover 1..c-1
  * exactly once (l = 1 gives {0}).  out: host array of >= l int32 (cap = its length).
  * Errors: EINVAL (l outside 1..CQSA_MAX_L, out NULL, cap < l), ENOSET (l = 7).
@@ -237,7 +237,7 @@ cqsa_status cqsa_workspace_size(const cqsa_plan* plan, cqsa_residency res, int64
 
 /*
  * Masked attention partials of every task, device-resident ("Implementation" section
- * of the wispaper explainer: compute the local numerators and denominators; the CQS
+ * of the wispaper explainer: per-task softmax numerator and denominator sums; the CQS
  * Mask selects the keys).  For every task t and every query row i of t:
  *     s_ij = (1/sqrt(d)) <q_i, k_j> over the keys j that t admits for i,
  *     m = a reference with  M - 8 <= m <= M,  M = log2(e) * max_j s_ij
@@ -275,7 +275,7 @@ cqsa_status cqsa_merge(const cqsa_plan* plan, const float* n_in, const float* ml
  * Out-of-Memory Recovery for Attention", abstract: independent subsequence tasks whose
  * local statistics recompose into the full output; "Stream-CQSA: Breaking the
  * Billion-Token Barrier on a Single GPU", section "Implementation: From High-Level Logic
- * to GPU Kernels": Q_i, K_i, V_i streamed to the GPU, local numerators and denominators,
+ * to GPU Kernels": each task's Q, K, V moved to the device, per-task softmax sums,
  * aggregation in host memory; Lattice summary: subproblems within a memory budget.
  *   CQSA_RES_DEVICE: q, k, v, o, lse are device pointers; runs cqsa_partials then
  *     cqsa_merge on stream using `workspace` (>= cqsa_workspace_size bytes) for the

@@ -6,8 +6,8 @@
 //
 // Host-pinned path (the stream engine): "Stream-CQSA: Breaking the Billion-Token
 // Barrier on a Single GPU" (wispaper explainer), section "Implementation: From
-// High-Level Logic to GPU Kernels": decompose, stream Q_i/K_i/V_i to the GPU, compute
-// the local numerators and denominators, aggregate (in host memory when the device
+// High-Level Logic to GPU Kernels": divide, move each task's queries, keys and values to
+// the device, form the task's softmax sums, aggregate them (in host memory when the device
 // cannot hold the accumulator).  Tasks run in ascending id.  For each task the K/V
 // segments are gathered into a staging buffer on the K/V copy stream; query units are
 // streamed through a two-slot ring (Q block, partial block, accumulator block, output

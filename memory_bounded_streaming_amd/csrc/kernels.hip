@@ -3,7 +3,7 @@
 //
 // What they compute follows "Stream-CQSA: Breaking the Billion-Token Barrier on a
 // Single GPU" (wispaper explainer), section "Implementation: From High-Level Logic to
-// GPU Kernels" (local numerators and denominators of the softmax per task, the CQS Mask
+// GPU Kernels" (each task's softmax numerator and denominator sums, the CQS Mask
 // selecting the keys) and the abstract of arXiv 2604.20819 (recompose the local
 // statistics).  The running-max form of the partials is the online normaliser of
 // "Online normalizer calculation for softmax" (cited by title on the arXiv page).

@@ -5,8 +5,8 @@
 // (c = l(l-1)+1 chunks, c subsequences of l chunks, every chunk pair exactly once),
 // section "The Recursive Benefit" (divide a task again), and section "Implementation:
 // From High-Level Logic to GPU Kernels" (a CQS Mask removes the redundant overlapping
-// regions).  The construction rule of the quorum ("derived from the theory of cyclic
-// quorum sets", abstract of arXiv 2604.20819) and the owner of each diagonal block are
+// regions).  The construction rule of the quorum (cyclic quorum sets, per the abstract of
+// arXiv 2604.20819) and the owner of each diagonal block are
 // readings: the smallest perfect difference set containing {0,1}, and "chunk x owns its
 // diagonal block in task t = x".
 #include "plan.hpp"

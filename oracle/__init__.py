@@ -16,10 +16,9 @@ Sources (the pages that define the method):
   explainer), sections "The 'CQS Divide': Attention as a Steiner System",
   "The Recursive Benefit" and "Implementation: From High-Level Logic to GPU
   Kernels" -- c = l(l-1)+1 chunks, c subsequences of l chunks, every chunk
-  pair exactly once (S(2,l,c)), recursion, the CQS Mask, local numerators and
-  denominators.
-* Lattice summary page of arXiv:2604.20819 -- recomposition gives exactly the
-  same result as full-sequence attention.
+  pair exactly once (S(2,l,c)), recursion, the CQS Mask, per-task softmax sums.
+* Lattice summary page of arXiv:2604.20819 -- the recomposed output equals that of
+  undivided attention.
 
 Modules
 -------

@@ -1,9 +1,9 @@
 """Dense exact softmax attention in float64 (oracle; test infrastructure only).
 
 Follows the definition the method reproduces exactly: "Stream-CQSA: Exact
-Out-of-Memory Recovery for Attention" (arXiv 2604.20819), abstract, measures
-against "a dense float64 reference"; the Lattice summary of arXiv:2604.20819
-states that recomposition gives "exactly the same result" as full-sequence
+Out-of-Memory Recovery for Attention" (arXiv 2604.20819), abstract, measures its
+error against dense attention computed in float64; the Lattice summary of
+arXiv:2604.20819 states that the recomposed output equals that of undivided
 attention.  So the oracle for outputs is the definition itself, not the
 method's algorithm:
 

@@ -5,9 +5,9 @@ What the pages fix
 "Stream-CQSA: Breaking the Billion-Token Barrier on a Single GPU" (wispaper
 explainer):
   * section "The 'CQS Divide': Attention as a Steiner System": N tokens are cut
-    into c chunks; with c = l(l-1)+1 one can form c subsequences of l chunks
-    each such that every pair of chunks is interacted with exactly once (a
-    Steiner system S(2,l,c));
+    into c chunks; when c = l(l-1)+1 there are c subsequences of l chunks each
+    in which any two chunks appear together in one subsequence and no other
+    (a Steiner system S(2,l,c));
   * section "The Recursive Benefit": a subsequence that is still too large is
     divided again with CQS Divide;
   * section "Implementation: From High-Level Logic to GPU Kernels": a CQS Mask

@@ -3,8 +3,8 @@
 These follow the method's own steps, in the order the pages give them:
 "Stream-CQSA: Breaking the Billion-Token Barrier on a Single GPU" (wispaper
 explainer), section "Implementation: From High-Level Logic to GPU Kernels":
-decompose into subsequences, move each task's Q, K, V, compute the local
-numerators and denominators of the softmax, aggregate.  The abstract of
+divide into subsequences, move each task's Q, K, V, form each task's softmax
+numerator and denominator sums, aggregate them.  The abstract of
 "Stream-CQSA: Exact Out-of-Memory Recovery for Attention" (arXiv 2604.20819)
 says the local statistics are recomposed into the full output; the merge rule
 for (max, denominator, numerator) triples is the one of "Online normalizer

@@ -8,9 +8,9 @@ taken per (row, head) against the row's largest reference magnitude:
 
 because an elementwise |dO|/|O_ref| is ill-posed: non-causal attention over
 N(0,1) data gives outputs that cross zero.  The pages ("Stream-CQSA: Exact
-Out-of-Memory Recovery for Attention", abstract) compare 16-bit forward output
-against a dense float64 reference without naming a norm; this row-wise norm is
-the reading taken.
+Out-of-Memory Recovery for Attention", abstract) compare the 16-bit forward
+output with dense attention computed in float64 and name no norm; this row-wise
+norm is the reading taken.
 """
 from __future__ import annotations
 
