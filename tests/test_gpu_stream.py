@@ -160,3 +160,29 @@ def test_concurrent_first_calls_on_one_plan():
         o_seq, _ = _device_forward(p, q, k, v, n, h, d, "bf16")
     for o in outs:
         assert np.array_equal(to_numpy(o, "bf16"), o_seq)
+
+
+@pytest.mark.parametrize("flags", [cqsa.CQSA_FLAG_HOST_ACC, cqsa.CQSA_FLAG_HOST_ACC | cqsa.CQSA_FLAG_KV_SINGLE],
+                         ids=["hostacc-kv2", "hostacc-kv1"])
+def test_repeated_calls_reuse_the_host_accumulator(flags):
+    """A plan keeps its pinned host accumulator between streamed calls: a second call with
+    other inputs must not see what the first left in it (every block is written before it
+    is read back), and each call equals the device path bit for bit."""
+    torch = pytest.importorskip("torch")
+    levels, u, h, d, dtype = [3, 2], 64, 2, 128, "bf16"
+    n = 7 * 3 * u
+    log(f"repeated streamed calls {levels} u={u} flags={flags}")
+    with cqsa.Plan(n, h, d, DT[dtype], levels, flags=flags) as p:
+        tq, qa = pinned((n, h, d), dtype)
+        tk, ka = pinned((n, h, d), dtype)
+        tv, va = pinned((n, h, d), dtype)
+        to, oa = pinned((n, h, d), dtype)
+        tl = torch.empty((h, n), dtype=torch.float32, pin_memory=True)
+        for seed in (301, 302, 301):
+            q, k, v = gen_qkv(seed, n, h, d, dtype)
+            o_dev, lse_dev = _device_forward(p, q, k, v, n, h, d, dtype)
+            qa[...], ka[...], va[...] = q, k, v
+            oa[...] = 0
+            p.forward(tq, tk, tv, to, tl, residency=cqsa.CQSA_RES_HOST_PINNED)
+            assert np.array_equal(oa, o_dev), f"seed {seed}: streamed output equals the device path"
+            assert np.array_equal(tl.numpy(), lse_dev), f"seed {seed}: LSE equals the device path"
