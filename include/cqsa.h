@@ -382,14 +382,18 @@ cqsa_status cqsa_backward(const cqsa_plan* plan, const void* q, const void* k, c
 /*
  * Dry run of the streamed forward for any N ("The Recursive Benefit" and "Precise
  * Scaling" sections of the wispaper explainer: recursion depth for very long
- * sequences): the same levels, footprint model and mode choice as cqsa_plan_create
- * (n_levels = 0: undivided first, then l_levels[0] repeated, up to CQSA_MAX_LEVELS),
- * but in closed form -- no task is built, so itr up to CQSA_MAX_LEVELS and billions of
- * tokens cost nothing.  Bytes and FLOP are exact for the stream engine (with LSE
- * returned); times come from `rates` (measured by the caller), overlapping copies
+ * sequences): the same levels, footprint model, budget test and mode choice as
+ * cqsa_plan_create (n_levels = 0: undivided first, then l_levels[0] repeated, up to
+ * CQSA_MAX_LEVELS), in closed form.  The budget test is cqsa_plan_create's: workspace
+ * plus descriptor tables.  For a plan cqsa_plan_create would build, the tables are
+ * built here (host time and memory grow with tasks x units^2: seconds for millions of
+ * items) when a shape bound cannot settle the test; a plan too large to build is
+ * estimated without them (they would have to be streamed per task;
+ * per_task_descriptor_bytes bounds one task's share), so itr up to CQSA_MAX_LEVELS and
+ * billions of tokens stay cheap.  Bytes and FLOP are exact for the stream engine (with
+ * LSE returned); times come from `rates` (measured by the caller), overlapping copies
  * with compute as the engine does (a single-buffered K/V stage is not overlapped).
- * The descriptor tables are excluded from stream_workspace_bytes (the materialized
- * engine holds them for all tasks; per_task_descriptor_bytes bounds one task's share).
+ * stream_workspace_bytes excludes the descriptor tables.
  * Host-only.  Errors: EINVAL, ENOSET, EDIVIDE, EBUDGET (no mode fits at any depth).
  */
 cqsa_status cqsa_plan_estimate(int64_t n, int32_t heads, int32_t head_dim, cqsa_dtype dtype,
