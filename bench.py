@@ -350,6 +350,45 @@ def pcie_achievable(torch, nbytes=512 << 20, reps=5):
     return out
 
 
+def box_ceilings(torch, reps=10):
+    """What plain library work reaches on this machine, beside the published peaks: a 1 GiB
+    device-to-device copy (bytes read + written per second), and the best of two large
+    bf16 matrix products through torch.matmul (the vendor GEMM, fp32 accumulation) on
+    N(0,1) data, contiguous operands: 16384 x 16384 x 16384 and 8192 x 8192 x 32768."""
+    out = {}
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    out["hbm_copy_gbs"] = reps * 2 * (1 << 30) / (time.perf_counter() - t0) / 1e9
+    del src, dst
+    g = torch.Generator(device="cuda").manual_seed(0)
+    best = {}
+    for m, n, k in ((16384, 16384, 16384), (8192, 8192, 32768)):
+        a = torch.randn((m, k), device="cuda", generator=g).to(torch.bfloat16).contiguous()
+        b = torch.randn((k, n), device="cuda", generator=g).to(torch.bfloat16).contiguous()
+        for _ in range(3):
+            c = torch.matmul(a, b)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            c = torch.matmul(a, b)
+        torch.cuda.synchronize()
+        rate = reps * 2.0 * m * n * k / (time.perf_counter() - t0) / 1e12
+        if rate > best.get("tflops", 0.0):
+            best = {"tflops": rate, "shape": f"{m}x{n}x{k}"}
+        del a, b, c
+    out["bf16_gemm_tflops"] = best["tflops"]
+    out["bf16_gemm_shape"] = best["shape"]
+    out["note"] = ("measured on this box after the timed calls: 1 GiB device copy (read + written bytes); "
+                   "best torch.matmul rate of two large contiguous bf16 products on N(0,1) data")
+    return out
+
+
 def pinned_inputs(torch, seed, n, h, d, count=3):
     """Q, K, V (and dO for count=4) drawn straight into pinned host memory."""
     from memory_bounded_streaming_amd.inputs import gen_tensor
@@ -547,6 +586,10 @@ def main():
     log("bench: headline, the streamed N=1376256 workload under 8 GiB")
     head = run_headline(args, torch, cqsa)
     log(f"bench: {head['value']:.1f} TFLOP/s end-to-end, partial kernel {head['attn_tflops']:.1f} TFLOP/s")
+    ceil = guarded("box ceilings", lambda: box_ceilings(torch))
+    if "error" not in ceil:
+        log(f"bench: box ceilings {ceil['bf16_gemm_tflops']:.1f} TFLOP/s bf16 GEMM, "
+            f"{ceil['hbm_copy_gbs']:.1f} GB/s device copy")
     dres = None
     if not args.no_device:
         log("bench: device-resident workload")
@@ -615,7 +658,9 @@ def main():
                          "achieved": round(dres["attn_tflops"], 3), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(dres["attn_tflops"] / BF16_MFMA_PEAK_TFLOPS, 4),
                          "traffic": measured_traffic(khash, "device_n57344"),
-                         "flop_per_launch": dres["plan"]["useful_flop"], "avg_launch_ms": round(dres["attn_ms"], 4)},
+                         "flop_per_launch": dres["plan"]["useful_flop"], "avg_launch_ms": round(dres["attn_ms"], 4),
+                         "frac_of_measured_ceiling": (round(dres["attn_tflops"] / ceil["bf16_gemm_tflops"], 4)
+                                                      if "error" not in ceil else None)},
             "merge": {"bound": "hbm", "achieved": round(dres["merge_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                       "frac": round(dres["merge_gbs"] / HBM_PEAK_GBS, 4), "bytes_per_launch": dres["merge_bytes"],
                       "avg_launch_ms": round(dres["merge_ms"], 4)},
@@ -650,11 +695,18 @@ def main():
             "launches_per_step": head["attn_launches"],
             "flop_per_launch": flop / head["attn_launches"],
             "avg_launch_ms": round(head["attn_ms"] / head["attn_launches"], 4),
+            "measured_ceiling": round(ceil["bf16_gemm_tflops"], 1) if "error" not in ceil else None,
+            "frac_of_measured_ceiling": (round(head["attn_tflops"] / ceil["bf16_gemm_tflops"], 4)
+                                         if "error" not in ceil else None),
         },
         "merge": {"bound": "hbm", "achieved": round(head["merge_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                   "frac": round(head["merge_gbs"] / HBM_PEAK_GBS, 4), "bytes_per_step": head["merge_bytes"],
                   "launches_per_step": head["merge_launches"],
-                  "avg_launch_ms": round(head["merge_ms"] / head["merge_launches"], 4)},
+                  "avg_launch_ms": round(head["merge_ms"] / head["merge_launches"], 4),
+                  "measured_ceiling": round(ceil["hbm_copy_gbs"], 1) if "error" not in ceil else None,
+                  "frac_of_measured_ceiling": (round(head["merge_gbs"] / ceil["hbm_copy_gbs"], 4)
+                                               if "error" not in ceil else None)},
+        "ceilings": ceil,
         "stream": head["stream"],
         "memory": head["memory"],
         "error": head.get("error"),
