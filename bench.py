@@ -534,6 +534,8 @@ def main():
     ap.add_argument("--headline-only", action="store_true", help="run the headline workload and nothing else")
     ap.add_argument("--device-only", action="store_true",
                     help="run only the device-resident N=57344 leg (its kernel trace and counters)")
+    ap.add_argument("--with-ceilings", action="store_true",
+                    help="with --device-only: also run the box ceilings (device copy, vendor bf16 GEMMs)")
     ap.add_argument("--cpu-rows", type=int, default=256)
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one plain device copy of 1 GiB first (reference for HBM traffic counters)")
@@ -580,7 +582,10 @@ def main():
     if args.device_only:
         log("bench: device-resident workload only")
         dres = run_device(args, torch, cqsa)
-        print(json.dumps({"device_resident": dres}), flush=True)
+        out = {"device_resident": dres}
+        if args.with_ceilings:
+            out["ceilings"] = box_ceilings(torch)
+        print(json.dumps(out), flush=True)
         return
 
     log("bench: headline, the streamed N=1376256 workload under 8 GiB")
