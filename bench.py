@@ -198,12 +198,15 @@ def oracle_check(q, k, v, o_bits, lse, rows_wanted, seed):
     return cpu, err
 
 
-def run_device(args, torch, cqsa):
+def run_device(args, torch, cqsa, causal=False):
+    """The device-resident workload (N=57344, H=8, d=128, l=3): partials then merge per
+    step, each timed with HIP events on its stream.  causal=True runs the plan with
+    CQSA_FLAG_CAUSAL (row i attends keys j <= i; useful FLOP 2 N (N+1) d H)."""
     from memory_bounded_streaming_amd.inputs import gen_qkv
     n, h, d, levels, _, _ = WORKLOADS["device_n57344"]
     q, k, v = gen_qkv(args.seed, n, h, d, "bf16")
     dev = [torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda() for x in (q, k, v)]
-    plan = cqsa.Plan(n, h, d, cqsa.CQSA_BF16, levels)
+    plan = cqsa.Plan(n, h, d, cqsa.CQSA_BF16, levels, flags=cqsa.CQSA_FLAG_CAUSAL if causal else 0)
     V = plan.info["visits"]
     ws_n = torch.empty((V, n, h, d), dtype=torch.float32, device="cuda")
     ws_ml = torch.empty((V, n, h, 2), dtype=torch.float32, device="cuda")
@@ -604,6 +607,13 @@ def main():
         else:
             log(f"bench: device-resident {dres['value']:.1f} TFLOP/s, partial kernel "
                 f"{dres['attn_tflops']:.1f} TFLOP/s")
+    dcausal = None
+    if not args.no_device:
+        log("bench: device-resident workload, causal")
+        dcausal = guarded("device-resident causal leg", lambda: run_device(args, torch, cqsa, causal=True))
+        if "error" not in dcausal:
+            log(f"bench: device-resident causal {dcausal['value']:.1f} useful TFLOP/s, partial kernel "
+                f"{dcausal['attn_tflops']:.1f}")
     bwd = None
     if not args.no_backward and dres is not None:
         log("bench: backward of the device-resident workload")
@@ -670,6 +680,19 @@ def main():
                       "frac": round(dres["merge_gbs"] / HBM_PEAK_GBS, 4), "bytes_per_launch": dres["merge_bytes"],
                       "avg_launch_ms": round(dres["merge_ms"], 4)},
         }
+    device_causal = None
+    if dcausal is not None:
+        device_causal = dcausal if "error" in dcausal else {
+            "workload": "the N=57344, 8-head, d=128 bf16 l=3 device-resident workload with CQSA_FLAG_CAUSAL "
+                        "(row i attends keys j <= i)",
+            "tflops_useful": round(dcausal["value"], 3), "ms_per_step": round(dcausal["ms_per_step"], 4),
+            "useful_flop": dcausal["plan"]["useful_flop"],
+            "roofline": {"bound": "mfma", "kernel": "attn_partial_bf16<128>",
+                         "achieved": round(dcausal["attn_tflops"], 3), "peak": BF16_MFMA_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(dcausal["attn_tflops"] / BF16_MFMA_PEAK_TFLOPS, 4),
+                         "avg_launch_ms": round(dcausal["attn_ms"], 4),
+                         "note": "achieved = useful FLOP 2 N (N+1) d H / partial-kernel time"},
+        }
     line = {
         "metric": METRIC,
         "value": round(head["value"], 3),
@@ -718,6 +741,7 @@ def main():
         "cpu_baseline": head.get("cpu_baseline"),
         "calls_s": head["calls_s"],
         "device_resident": device_resident,
+        "device_resident_causal": device_causal,
         "streamed_16gib": stream_res,
         "backward": bwd,
         "streamed_backward": sbwd,
