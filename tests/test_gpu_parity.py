@@ -36,6 +36,11 @@ SMALL = [
     ([2, 3], 8, 1, 64, "f32"),
     ([1], 1, 1, 64, "f32"),           # a single token: O = V
     ([3], 1, 1, 128, "bf16"),         # units of one token
+    ([5], 70, 2, 64, "f32"),          # l = 5 .. 10: 21 .. 91 tasks of 5 .. 10 units
+    ([6], 50, 1, 128, "bf16"),
+    ([8], 33, 1, 64, "bf16"),
+    ([9], 24, 1, 64, "f32"),
+    ([10], 20, 2, 128, "bf16"),
 ]
 
 
