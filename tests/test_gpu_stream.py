@@ -25,6 +25,8 @@ CASES = [  # levels, unit, heads, d, dtype
     ([2, 2], 100, 1, 128, "bf16"),
     ([3], 96, 2, 64, "f32"),
     ([1], 500, 1, 128, "bf16"),
+    ([8], 24, 1, 128, "bf16"),       # 57 tasks of 8 units: consecutive tasks share one chunk
+    ([10], 16, 2, 64, "f32"),        # 91 tasks of 10 units
 ]
 
 
