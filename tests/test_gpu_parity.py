@@ -41,6 +41,8 @@ SMALL = [
     ([8], 33, 1, 64, "bf16"),
     ([9], 24, 1, 64, "f32"),
     ([10], 20, 2, 128, "bf16"),
+    ([3], 40, 32, 128, "bf16"),       # many heads: row stride 4096 elements
+    ([4], 20, 40, 64, "bf16"),        # a head count that is not a power of two
 ]
 
 
