@@ -33,6 +33,8 @@ CASES = [  # levels, N, heads, head_dim, dtype, pad
     ([2, 3], 21 * 8, 1, 64, "f32", False),
     ([3], 7 * 33 - 5, 1, 64, "f32", True),
     ([2, 3], 21 * 9 + 2, 1, 128, "f32", True),  # fp32 d=128 dQ (once wrong while its kernel spilled)
+    ([8], 57 * 24, 1, 128, "bf16", False),      # 57 tasks of 8 units
+    ([10], 91 * 12 + 5, 1, 64, "f32", True),    # 91 tasks of 10 units, padded N
 ]
 
 

@@ -31,6 +31,8 @@ CASES = [  # levels, N, heads, head_dim, dtype
     ([1], 333, 2, 128, "bf16"),           # undivided: one task, one diagonal run
     ([3], 7 * 64, 1, 64, "f32"),
     ([2, 3], 21 * 9 + 2, 1, 128, "f32"),  # padded
+    ([8], 57 * 24, 1, 128, "bf16"),       # 57 tasks of 8 units
+    ([6], 31 * 30 + 3, 2, 64, "f32"),     # 31 tasks of 6 units, padded
 ]
 
 
