@@ -40,7 +40,17 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* The enums of this header are int-sized in C.  Compiled as C++ they take int as their
+ * fixed underlying type, so every int a caller passes is a value of the enum type (a
+ * value outside the listed ones is then rejected with CQSA_EINVAL rather than being a
+ * value the type cannot hold); the layout and the calling convention are the same. */
+#ifdef __cplusplus
+#define CQSA_INT_ENUM(tag) enum tag : int
+#else
+#define CQSA_INT_ENUM(tag) enum tag
+#endif
+
+typedef CQSA_INT_ENUM(cqsa_status_e) {
   CQSA_OK = 0,
   CQSA_EINVAL = -1,   /* bad argument (null pointer, size, unsupported d/dtype/flag) */
   CQSA_ENOSET = -2,   /* no perfect difference set for this l (l = 7) */
@@ -51,13 +61,13 @@ typedef enum {
   CQSA_ESMALL = -7    /* a caller buffer or workspace is smaller than required */
 } cqsa_status;
 
-typedef enum { CQSA_BF16 = 0, CQSA_F32 = 1 } cqsa_dtype;
+typedef CQSA_INT_ENUM(cqsa_dtype_e) { CQSA_BF16 = 0, CQSA_F32 = 1 } cqsa_dtype;
 
 /* Where q, k, v, o and lse live for cqsa_forward. */
-typedef enum { CQSA_RES_DEVICE = 0, CQSA_RES_HOST_PINNED = 1 } cqsa_residency;
+typedef CQSA_INT_ENUM(cqsa_residency_e) { CQSA_RES_DEVICE = 0, CQSA_RES_HOST_PINNED = 1 } cqsa_residency;
 
 /* Staging mode of the host-pinned path, chosen by the footprint model. */
-typedef enum {
+typedef CQSA_INT_ENUM(cqsa_mode_e) {
   CQSA_MODE_DEVICE_ACC_KV2 = 1, /* K/V of two tasks staged (double buffer), accumulator on device */
   CQSA_MODE_HOST_ACC_KV2 = 2,   /* K/V double buffer, accumulator in pinned host memory */
   CQSA_MODE_DEVICE_ACC_KV1 = 3, /* one task's K/V resident at a time, accumulator on device */
