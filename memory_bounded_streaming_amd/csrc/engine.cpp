@@ -210,18 +210,20 @@ cqsa_status device_tables(const Plan& p, DeviceTables& out, std::string& why) {
     if (e.first == dev) base = static_cast<char*>(e.second);
   if (base == nullptr) {
     std::vector<char> host(b0 + b1 + b2 + b3 + b4 + b5 + b6 + b7 + b8, 0);
-    std::memcpy(host.data(), p.dev_items.data(), p.dev_items.size() * sizeof(WorkItem));
-    std::memcpy(host.data() + b0, p.dev_runs.data(), p.dev_runs.size() * sizeof(KeyRun));
-    std::memcpy(host.data() + b0 + b1, p.stream_items.data(), p.stream_items.size() * sizeof(WorkItem));
-    std::memcpy(host.data() + b0 + b1 + b2, p.stream_runs.data(), p.stream_runs.size() * sizeof(KeyRun));
-    std::memcpy(host.data() + b0 + b1 + b2 + b3, p.dev_kitems.data(), p.dev_kitems.size() * sizeof(WorkItem));
-    std::memcpy(host.data() + b0 + b1 + b2 + b3 + b4, p.dev_kruns.data(), p.dev_kruns.size() * sizeof(KeyRun));
-    std::memcpy(host.data() + b0 + b1 + b2 + b3 + b4 + b5, p.bstream_items.data(),
-                p.bstream_items.size() * sizeof(WorkItem));
-    std::memcpy(host.data() + b0 + b1 + b2 + b3 + b4 + b5 + b6, p.bstream_kitems.data(),
-                p.bstream_kitems.size() * sizeof(WorkItem));
-    std::memcpy(host.data() + b0 + b1 + b2 + b3 + b4 + b5 + b6 + b7, p.bstream_kruns.data(),
-                p.bstream_kruns.size() * sizeof(KeyRun));
+    // tables a plan does not use are empty (their data() may be null, which memcpy may
+    // not receive even for zero bytes)
+    auto put = [&](int64_t at, const auto& v) {
+      if (!v.empty()) std::memcpy(host.data() + at, v.data(), v.size() * sizeof(v[0]));
+    };
+    put(0, p.dev_items);
+    put(b0, p.dev_runs);
+    put(b0 + b1, p.stream_items);
+    put(b0 + b1 + b2, p.stream_runs);
+    put(b0 + b1 + b2 + b3, p.dev_kitems);
+    put(b0 + b1 + b2 + b3 + b4, p.dev_kruns);
+    put(b0 + b1 + b2 + b3 + b4 + b5, p.bstream_items);
+    put(b0 + b1 + b2 + b3 + b4 + b5 + b6, p.bstream_kitems);
+    put(b0 + b1 + b2 + b3 + b4 + b5 + b6 + b7, p.bstream_kruns);
     void* mem = nullptr;
     HIP_TRY(dev_malloc(&mem, static_cast<int64_t>(host.size())));
     hipError_t e = hipMemcpy(mem, host.data(), host.size(), hipMemcpyHostToDevice);
