@@ -60,14 +60,24 @@ cqsa_status difference_set(int l, std::vector<int>& out, std::string& why) {
     return CQSA_OK;
   }
   const int c = l * (l - 1) + 1;
-  std::vector<char> used(c, 0);
-  std::vector<int> chosen{0, 1};
-  used[1] = used[c - 1] = 1;
-  if (!dfs_extend(l, c, chosen, used, 2)) {
+  // The search is deterministic and takes tens of milliseconds for l = 10, so each l is
+  // searched once per process and its result kept.
+  static std::mutex mu;
+  static std::vector<int> found[CQSA_MAX_L + 1];
+  static int state[CQSA_MAX_L + 1] = {};  // 0 not searched, 1 found, -1 none exists
+  std::lock_guard<std::mutex> lock(mu);
+  if (state[l] == 0) {
+    std::vector<char> used(c, 0);
+    std::vector<int> chosen{0, 1};
+    used[1] = used[c - 1] = 1;
+    state[l] = dfs_extend(l, c, chosen, used, 2) ? 1 : -1;
+    if (state[l] == 1) found[l] = chosen;
+  }
+  if (state[l] < 0) {
     why = "no perfect difference set exists for l=" + std::to_string(l) + " (c=" + std::to_string(c) + ")";
     return CQSA_ENOSET;
   }
-  out = chosen;
+  out = found[l];
   return CQSA_OK;
 }
 
