@@ -4,7 +4,7 @@ tables live in the library's static device array.
 GPU: two calls in a row (the second with a smaller plan, another dtype and the causal
 mask), then the first plan once more, each compared bit for bit with cqsa_forward
 (CQSA_RES_DEVICE, caller workspace) on the same inputs, and on sampled rows with the
-fp64 oracle.  CPU: the argument checks and the size limit, which return before any
+fp64 oracle; and the call captured into a HIP graph, whose replays equal the eager call.  CPU: the argument checks and the size limit, which return before any
 device work.
 """
 import numpy as np
@@ -81,6 +81,42 @@ def test_noalloc_matches_forward_on_two_calls_in_a_row():
     _check_against_forward(torch, CALLS[0], p, host, dev, o, lse)
     for item in (first, second):
         item[0].close()
+
+
+@pytest.mark.gpu
+def test_noalloc_captured_in_a_graph_replays_the_eager_result():
+    """The call captured into a HIP graph (what callers that cannot allocate often do),
+    replayed three times with eager calls and synchronisations between the replays; every
+    replay equals the eager call bit for bit."""
+    torch = pytest.importorskip("torch")
+    n, h, d = 7 * 256, 4, 128
+    log(f"no-alloc forward under graph capture N={n} H={h} d={d} bf16")
+    q, k, v = gen_qkv(73, n, h, d, "bf16")
+    dev = [to_device(x, "bf16") for x in (q, k, v)]
+    with cqsa.Plan(n, h, d, cqsa.CQSA_BF16, [3]) as p:
+        o_ref = empty_device((n, h, d), "bf16")
+        lse_ref = torch.empty((h, n), device="cuda")
+        p.forward_noalloc(*dev, o_ref, lse_ref)
+        torch.cuda.synchronize()
+        want_o, want_l = o_ref.view(torch.int16).clone(), lse_ref.clone()
+        o = empty_device((n, h, d), "bf16")
+        lse = torch.empty((h, n), device="cuda")
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.graph(graph, stream=side):
+            p.forward_noalloc(*dev, o, lse, stream=torch.cuda.current_stream())
+        for i in range(3):
+            o.view(torch.int16).fill_(-1)
+            lse.fill_(float("nan"))
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(o.view(torch.int16), want_o), f"replay {i}: O"
+            assert torch.equal(lse.view(torch.int32), want_l.view(torch.int32)), f"replay {i}: LSE"
+            p.forward_noalloc(*dev, o_ref, lse_ref)   # eager work on the same array between replays
+            torch.cuda.synchronize()
+        del graph
 
 
 def test_noalloc_rejects_a_plan_larger_than_the_array():
