@@ -15,6 +15,7 @@
 #include <cmath>
 #include <cstring>
 #include <numeric>
+#include <thread>
 
 namespace cqsa {
 
@@ -160,60 +161,83 @@ cqsa_status build_tasks(Plan& p, std::string& why) {
   }
   const int64_t n_tasks = p.n_units;  // prod(c)
   p.tasks.assign(n_tasks, Task{});
-  std::vector<int32_t> seen(p.n_units, 0);
   const int64_t tu = p.task_units;
-  std::vector<int32_t> chunk_of(static_cast<size_t>(levels) * tu);
-  for (int64_t tid = 0; tid < n_tasks; ++tid) {
-    Task& task = p.tasks[tid];
-    task.tid = tid;
-    task.ids.assign(levels, 0);
-    int64_t rem = tid;
-    for (int k = levels - 1; k >= 0; --k) {
-      task.ids[k] = static_cast<int>(rem % p.cs[k]);
-      rem /= p.cs[k];
-    }
-    task.units.resize(tu);
-    for (int64_t a = 0; a < tu; ++a) {
-      int64_t x = a;  // index in the level-k task list, walking outward
+  // Every task is built independently (its units, the CQS Mask over its unit pairs, its
+  // segments); large plans spread the tasks over host threads.  Only the visit slots
+  // depend on the task order, so they are numbered afterwards in ascending task id.
+  auto build_range = [&](int64_t t0, int64_t t1) {
+    std::vector<int32_t> chunk_of(static_cast<size_t>(levels) * tu);
+    for (int64_t tid = t0; tid < t1; ++tid) {
+      Task& task = p.tasks[tid];
+      task.tid = tid;
+      task.ids.assign(levels, 0);
+      int64_t rem = tid;
       for (int k = levels - 1; k >= 0; --k) {
-        const int chunk = members[k][task.ids[k]][x / chunk_len[k]];
-        chunk_of[static_cast<size_t>(k) * tu + a] = chunk;
-        x = chunk * chunk_len[k] + x % chunk_len[k];
+        task.ids[k] = static_cast<int>(rem % p.cs[k]);
+        rem /= p.cs[k];
       }
-      task.units[a] = x;
-    }
-    // CQS Mask: admitted iff at every level the chunks differ or equal the task's own index
-    task.runs.assign(tu, {});
-    for (int64_t a = 0; a < tu; ++a) {
-      auto& runs = task.runs[a];
-      for (int64_t b = 0; b < tu; ++b) {
-        bool ok = true;
-        for (int k = 0; k < levels && ok; ++k) {
-          const int ca = chunk_of[static_cast<size_t>(k) * tu + a];
-          const int cb = chunk_of[static_cast<size_t>(k) * tu + b];
-          ok = (ca != cb) || (ca == task.ids[k]);
+      task.units.resize(tu);
+      for (int64_t a = 0; a < tu; ++a) {
+        int64_t x = a;  // index in the level-k task list, walking outward
+        for (int k = levels - 1; k >= 0; --k) {
+          const int chunk = members[k][task.ids[k]][x / chunk_len[k]];
+          chunk_of[static_cast<size_t>(k) * tu + a] = chunk;
+          x = chunk * chunk_len[k] + x % chunk_len[k];
         }
-        if (!ok || (causal && b > a)) continue;
-        ++task.admitted_units;
-        if (!runs.empty() && runs.back().start + runs.back().count == b)
-          ++runs.back().count;
-        else
-          runs.push_back({static_cast<int32_t>(b), 1});
+        task.units[a] = x;
       }
+      // CQS Mask: admitted iff at every level the chunks differ or equal the task's own index
+      task.runs.assign(tu, {});
+      for (int64_t a = 0; a < tu; ++a) {
+        auto& runs = task.runs[a];
+        for (int64_t b = 0; b < tu; ++b) {
+          bool ok = true;
+          for (int k = 0; k < levels && ok; ++k) {
+            const int ca = chunk_of[static_cast<size_t>(k) * tu + a];
+            const int cb = chunk_of[static_cast<size_t>(k) * tu + b];
+            ok = (ca != cb) || (ca == task.ids[k]);
+          }
+          if (!ok || (causal && b > a)) continue;
+          ++task.admitted_units;
+          if (!runs.empty() && runs.back().start + runs.back().count == b)
+            ++runs.back().count;
+          else
+            runs.push_back({static_cast<int32_t>(b), 1});
+        }
+      }
+      for (int64_t a = 0; a < tu; ++a) {
+        const int64_t g = task.units[a];
+        if (!task.segments.empty() &&
+            task.segments.back().global_start + task.segments.back().length == g * p.unit)
+          task.segments.back().length += p.unit;
+        else
+          task.segments.push_back({g * p.unit, p.unit, a * p.unit});
+      }
+      // padding (CQSA_FLAG_PAD): cut every segment at N, drop those that start past it
+      std::vector<Segment> real;
+      for (const Segment& g : task.segments)
+        if (g.global_start < p.n) real.push_back({g.global_start, std::min(g.length, p.n - g.global_start), g.local_offset});
+      task.segments.swap(real);
     }
-    for (int64_t a = 0; a < tu; ++a) {
-      const int64_t g = task.units[a];
-      if (!task.segments.empty() &&
-          task.segments.back().global_start + task.segments.back().length == g * p.unit)
-        task.segments.back().length += p.unit;
-      else
-        task.segments.push_back({g * p.unit, p.unit, a * p.unit});
+  };
+  const int64_t cells = n_tasks * tu * tu * levels;
+  const int64_t workers = cells < (int64_t(1) << 24)
+                              ? 1
+                              : std::max<int64_t>(1, std::min<int64_t>({16, int64_t(std::thread::hardware_concurrency()),
+                                                                        n_tasks}));
+  if (workers == 1) {
+    build_range(0, n_tasks);
+  } else {
+    std::vector<std::thread> pool;
+    const int64_t per = (n_tasks + workers - 1) / workers;
+    for (int64_t w = 0; w < workers; ++w) {
+      const int64_t t0 = w * per, t1 = std::min(n_tasks, t0 + per);
+      if (t0 < t1) pool.emplace_back(build_range, t0, t1);
     }
-    // padding (CQSA_FLAG_PAD): cut every segment at N, drop those that start past it
-    std::vector<Segment> real;
-    for (const Segment& g : task.segments)
-      if (g.global_start < p.n) real.push_back({g.global_start, std::min(g.length, p.n - g.global_start), g.local_offset});
-    task.segments.swap(real);
+    for (auto& th : pool) th.join();
+  }
+  std::vector<int32_t> seen(p.n_units, 0);
+  for (Task& task : p.tasks) {
     task.slot.resize(tu);
     for (int64_t a = 0; a < tu; ++a) task.slot[a] = seen[task.units[a]]++;
   }

@@ -53,6 +53,18 @@ int main() {
     });
   }
   for (auto& th : pool) th.join();
+  // a plan large enough that its tasks are built on several host threads, twice at once
+  std::thread big[2];
+  for (auto& th : big)
+    th = std::thread([&created]() {
+      const int32_t l4[] = {3, 3, 3, 3};
+      cqsa_plan* p = nullptr;
+      if (cqsa_plan_create(2401, 1, 64, CQSA_BF16, l4, 4, 0, 0, &p) == CQSA_OK) {
+        ++created;
+        cqsa_plan_destroy(p);
+      }
+    });
+  for (auto& th : big) th.join();
   std::printf("plans created %d\n", created.load());
   return 0;
 }

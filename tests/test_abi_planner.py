@@ -53,7 +53,8 @@ def test_difference_sets_match_oracle(lib):
 
 SMALL_PLANS = [([1], 1), ([1], 37), ([2], 3), ([3], 7), ([3], 21), ([4], 13), ([5], 42), ([6], 31),
                ([2, 2], 9), ([3, 2], 21), ([2, 3], 42), ([3, 3], 49), ([4, 2], 39), ([2, 2, 2], 27),
-               ([8], 57), ([8], 114), ([9], 73), ([10], 91), ([6, 2], 93)]
+               ([8], 57), ([8], 114), ([9], 73), ([10], 91), ([6, 2], 93),
+               ([3, 3, 3, 3], 2401)]  # 2,401 tasks of 81 units: built on several host threads
 
 
 @pytest.mark.parametrize("levels,n", SMALL_PLANS + [(v[4], v[0]) for v in CONFIGS.values()])
