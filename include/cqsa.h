@@ -328,6 +328,7 @@ cqsa_status cqsa_forward(const cqsa_plan* plan, const void* q, const void* k, co
  * each device the library runs on, held from this call's first use on the device until
  * the process ends.  The plan must need at most that much:
  *     align256(V*N*H*d*4) + align256(V*N*H*2*4) + align256(items*32) + align256(runs*16)
+ *     (+ align256(4 * blocks) for a causal plan's dispatch order of the launch)
  * (V = visits; e.g. N = 14,336, H = 8, d = 128 with one level of l = 3 needs 179 MB);
  * a larger plan gets ESMALL and nothing is enqueued.  Nothing is allocated or freed, and
  * the plan's own device tables are not used: each call copies the forward descriptor

@@ -27,6 +27,16 @@ struct WorkItem {
   int32_t keys;      // total admitted keys (for ordering only)
 };
 
+// Launch shape of the attention-partial kernel, shared by the kernel and the planner's
+// dispatch order: query rows and keys per workgroup tile (bf16 / float32), and the most
+// workgroups of one (item, head) group that go to one XCD together (one round of its 32 CUs).
+constexpr int kAttnQueryTileBf16 = 256, kAttnQueryTileF32 = 64;
+constexpr int kAttnKeyTileBf16 = 64, kAttnKeyTileF32 = 32;
+constexpr int kDispatchChunk = 32;
+// Largest dispatch table the planner builds (entries of 4 bytes); a launch with more
+// workgroups keeps the arithmetic order.
+constexpr int64_t kMaxDispatchEntries = int64_t(1) << 20;
+
 static_assert(sizeof(KeyRun) == 16, "KeyRun layout");
 static_assert(sizeof(WorkItem) == 32, "WorkItem layout");
 

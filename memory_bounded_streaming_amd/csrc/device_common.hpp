@@ -23,7 +23,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // XCDs, which balances their work.  The grid is 8 * chunk_tiles * ceil(chunks / 8); the
 // workgroups past the last chunk, or past the last tile of a shorter final chunk of a
 // group, return at once.
-constexpr int kChunk = 32;
+constexpr int kChunk = kDispatchChunk;
 
 __host__ __device__ inline int chunks_per_group(int tiles) { return (tiles + kChunk - 1) / kChunk; }
 __host__ __device__ inline int chunk_tiles(int tiles) {

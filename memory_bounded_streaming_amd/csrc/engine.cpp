@@ -204,12 +204,13 @@ cqsa_status device_tables(const Plan& p, DeviceTables& out, std::string& why) {
   const int64_t b6 = align_up(int64_t(p.bstream_items.size()) * sizeof(WorkItem));
   const int64_t b7 = align_up(int64_t(p.bstream_kitems.size()) * sizeof(WorkItem));
   const int64_t b8 = align_up(int64_t(p.bstream_kruns.size()) * sizeof(KeyRun));
+  const int64_t b9 = align_up(int64_t(p.dev_order.size()) * int64_t(sizeof(int32_t)));
   std::lock_guard<std::mutex> lock(p.dev_mu);
   char* base = nullptr;
   for (auto& e : p.dev_tables)
     if (e.first == dev) base = static_cast<char*>(e.second);
   if (base == nullptr) {
-    std::vector<char> host(b0 + b1 + b2 + b3 + b4 + b5 + b6 + b7 + b8, 0);
+    std::vector<char> host(b0 + b1 + b2 + b3 + b4 + b5 + b6 + b7 + b8 + b9, 0);
     // tables a plan does not use are empty (their data() may be null, which memcpy may
     // not receive even for zero bytes)
     auto put = [&](int64_t at, const auto& v) {
@@ -224,6 +225,7 @@ cqsa_status device_tables(const Plan& p, DeviceTables& out, std::string& why) {
     put(b0 + b1 + b2 + b3 + b4 + b5, p.bstream_items);
     put(b0 + b1 + b2 + b3 + b4 + b5 + b6, p.bstream_kitems);
     put(b0 + b1 + b2 + b3 + b4 + b5 + b6 + b7, p.bstream_kruns);
+    put(b0 + b1 + b2 + b3 + b4 + b5 + b6 + b7 + b8, p.dev_order);
     void* mem = nullptr;
     HIP_TRY(dev_malloc(&mem, static_cast<int64_t>(host.size())));
     hipError_t e = hipMemcpy(mem, host.data(), host.size(), hipMemcpyHostToDevice);
@@ -244,7 +246,10 @@ cqsa_status device_tables(const Plan& p, DeviceTables& out, std::string& why) {
   out.bstream_items = reinterpret_cast<const WorkItem*>(base + b0 + b1 + b2 + b3 + b4 + b5);
   out.bstream_kitems = reinterpret_cast<const WorkItem*>(base + b0 + b1 + b2 + b3 + b4 + b5 + b6);
   out.bstream_kruns = reinterpret_cast<const KeyRun*>(base + b0 + b1 + b2 + b3 + b4 + b5 + b6 + b7);
-  out.bytes = b0 + b1 + b2 + b3 + b4 + b5 + b6 + b7 + b8;
+  out.dev_order = p.dev_order.empty() ? nullptr
+                                      : reinterpret_cast<const int32_t*>(base + b0 + b1 + b2 + b3 + b4 + b5 + b6 + b7 + b8);
+  out.dev_order_len = static_cast<int64_t>(p.dev_order.size());
+  out.bytes = b0 + b1 + b2 + b3 + b4 + b5 + b6 + b7 + b8 + b9;
   return CQSA_OK;
 }
 
@@ -280,12 +285,12 @@ cqsa_status run_partials(const Plan& p, const void* q, const void* k, const void
   DeviceTables t{};
   cqsa_status st = device_tables(p, t, why);
   if (st != CQSA_OK) return st;
-  return run_partials_with(p, q, k, v, n_out, ml_out, t.dev_items, t.dev_runs, stream, why);
+  return run_partials_with(p, q, k, v, n_out, ml_out, t.dev_items, t.dev_runs, t.dev_order, stream, why);
 }
 
 cqsa_status run_partials_with(const Plan& p, const void* q, const void* k, const void* v, float* n_out,
-                              float* ml_out, const WorkItem* items, const KeyRun* runs, hipStream_t stream,
-                              std::string& why) {
+                              float* ml_out, const WorkItem* items, const KeyRun* runs, const int32_t* order,
+                              hipStream_t stream, std::string& why) {
   AttnLaunch a{};
   a.dtype = p.dtype;
   a.d = p.d;
@@ -299,6 +304,8 @@ cqsa_status run_partials_with(const Plan& p, const void* q, const void* k, const
   a.runs = runs;
   a.n_items = static_cast<int>(p.dev_items.size());
   a.q_len = static_cast<int>(p.unit);
+  a.order = order;
+  a.order_len = order != nullptr ? static_cast<int64_t>(p.dev_order.size()) : 0;
   a.scale_log2 = scale_log2(p);
   HIP_TRY(launch_attn(a, stream));
   return CQSA_OK;

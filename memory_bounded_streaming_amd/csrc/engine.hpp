@@ -20,6 +20,8 @@ struct DeviceTables {
   const WorkItem* bstream_items;  // streamed backward items (rows in the task staging)
   const WorkItem* bstream_kitems; // causal streamed dK/dV items and runs (task staging rows)
   const KeyRun* bstream_kruns;
+  const int32_t* dev_order;       // dispatch order of the device-resident launch, or null
+  int64_t dev_order_len;
   int64_t bytes;
 };
 
@@ -35,11 +37,11 @@ void set_fail_allocations(int count);
 
 cqsa_status run_partials(const Plan& p, const void* q, const void* k, const void* v, float* n_out,
                          float* ml_out, hipStream_t stream, std::string& why);
-// The same launch with the forward descriptor tables (the plan's dev_items and dev_runs)
-// already on the device at items and runs.
+// The same launch with the forward descriptor tables (the plan's dev_items and dev_runs,
+// and its dispatch order dev_order when it has one) already on the device.
 cqsa_status run_partials_with(const Plan& p, const void* q, const void* k, const void* v, float* n_out,
-                              float* ml_out, const WorkItem* items, const KeyRun* runs, hipStream_t stream,
-                              std::string& why);
+                              float* ml_out, const WorkItem* items, const KeyRun* runs, const int32_t* order,
+                              hipStream_t stream, std::string& why);
 cqsa_status run_merge(const Plan& p, const float* n_in, const float* ml_in, void* o, float* lse,
                       hipStream_t stream, std::string& why);
 // Gradients dQ, dK, dV of the forward for upstream gradient d_o (device-resident).

@@ -34,11 +34,26 @@ struct AttnParams {
   float* ml_out;
   const WorkItem* items;
   const KeyRun* runs;
+  const int32_t* order;  // dispatch order, or null
   int64_t n_items;
   int tiles_per_item;
   int heads;
   float scale_log2;
 };
+
+// The (item, head, tile) this workgroup computes: from the planner's dispatch order when
+// the launch has one (block b runs entry b; -1 marks a block with nothing to do), else
+// the arithmetic order of group_coord.
+__device__ __forceinline__ bool attn_coord(const AttnParams& P, GroupCoord& c) {
+  if (P.order == nullptr) return group_coord(blockIdx.x, P.tiles_per_item, P.heads, P.n_items, c);
+  const int v = P.order[blockIdx.x];
+  if (v < 0) return false;
+  c.tile = v % P.tiles_per_item;
+  const int g = v / P.tiles_per_item;
+  c.head = g % P.heads;
+  c.item = g / P.heads;
+  return true;
+}
 
 
 // ---------------------------------------------------------------------------------
@@ -96,7 +111,7 @@ __global__ __launch_bounds__(512) void attn_partial_bf16(AttnParams P) {
   const int lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, col = lane & 31;
   GroupCoord gc;
-  if (!group_coord(blockIdx.x, P.tiles_per_item, P.heads, P.n_items, gc)) return;
+  if (!attn_coord(P, gc)) return;
   const int tile = gc.tile;
   const int head = gc.head;
   const WorkItem it = P.items[gc.item];
@@ -312,13 +327,13 @@ __global__ __launch_bounds__(512) void attn_partial_bf16(AttnParams P) {
 // ---------------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(64) void attn_partial_f32(AttnParams P) {
-  constexpr int QT = 64;
-  constexpr int KT = 32;
+  constexpr int QT = kAttnQueryTileF32;
+  constexpr int KT = kAttnKeyTileF32;
   __shared__ __attribute__((aligned(16))) float kf[KT * D];
   __shared__ __attribute__((aligned(16))) float vf[KT * D];
   const int lane = threadIdx.x;
   GroupCoord gc;
-  if (!group_coord(blockIdx.x, P.tiles_per_item, P.heads, P.n_items, gc)) return;
+  if (!attn_coord(P, gc)) return;
   const int tile = gc.tile;
   const int head = gc.head;
   const WorkItem it = P.items[gc.item];
@@ -464,7 +479,11 @@ __global__ __launch_bounds__(256) void merge_partials(MergeParams P) {
 
 }  // namespace
 
-int attn_query_tile(cqsa_dtype dtype) { return dtype == CQSA_BF16 ? Bf16Tile<128>::QT : 64; }
+static_assert(Bf16Tile<128>::QT == kAttnQueryTileBf16 && Bf16Tile<64>::QT == kAttnQueryTileBf16 &&
+                  Bf16Tile<128>::KT == kAttnKeyTileBf16 && Bf16Tile<64>::KT == kAttnKeyTileBf16,
+              "the planner's dispatch order uses the kernel's tile shape");
+
+int attn_query_tile(cqsa_dtype dtype) { return dtype == CQSA_BF16 ? kAttnQueryTileBf16 : kAttnQueryTileF32; }
 
 hipError_t launch_attn(const AttnLaunch& a, hipStream_t stream) {
   if (a.n_items <= 0 || a.q_len <= 0) return hipSuccess;
@@ -478,10 +497,11 @@ hipError_t launch_attn(const AttnLaunch& a, hipStream_t stream) {
   p.runs = a.runs;
   p.heads = a.heads;
   p.scale_log2 = a.scale_log2;
+  p.order = a.order;
   const int qt = attn_query_tile(a.dtype);
   p.tiles_per_item = (a.q_len + qt - 1) / qt;
   p.n_items = a.n_items;
-  const int64_t blocks = group_grid(int64_t(a.n_items) * a.heads, p.tiles_per_item);
+  const int64_t blocks = a.order != nullptr ? a.order_len : group_grid(int64_t(a.n_items) * a.heads, p.tiles_per_item);
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const dim3 grid(static_cast<unsigned>(blocks));
   if (a.dtype == CQSA_BF16) {

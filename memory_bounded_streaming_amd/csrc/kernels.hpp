@@ -24,6 +24,9 @@ struct AttnLaunch {
   int n_items;
   int q_len;            // rows of every item in this launch
   float scale_log2;     // softmax scale * log2(e)
+  const int32_t* order; // device: dispatch order (block b runs entry b: (item * heads + head)
+                        // * tiles + tile, or -1), or null for the arithmetic order
+  int64_t order_len;    // blocks of the launch when order is given
 };
 
 // Merge of (m, l, n) triples: input a, then nb further inputs at b + s*stride,

@@ -64,7 +64,8 @@ int64_t static_scratch_capacity() { return kStaticScratchBytes; }
 
 int64_t static_scratch_need(const Plan& p) {
   return align_up(p.visits * p.n * p.heads * int64_t(p.d) * 4) + align_up(p.visits * p.n * p.heads * int64_t(2) * 4) +
-         align_up(int64_t(p.dev_items.size()) * sizeof(WorkItem)) + align_up(int64_t(p.dev_runs.size()) * sizeof(KeyRun));
+         align_up(int64_t(p.dev_items.size()) * sizeof(WorkItem)) + align_up(int64_t(p.dev_runs.size()) * sizeof(KeyRun)) +
+         align_up(int64_t(p.dev_order.size()) * int64_t(sizeof(int32_t)));
 }
 
 cqsa_status forward_static(const Plan& p, const void* q, const void* k, const void* v, void* o, float* lse,
@@ -78,28 +79,32 @@ cqsa_status forward_static(const Plan& p, const void* q, const void* k, const vo
   void* base = nullptr;
   cqsa_status st = scratch_address(base, why);
   if (st != CQSA_OK) return st;
-  // layout: n slots | (m, l) slots | work items | key runs
+  // layout: n slots | (m, l) slots | work items | key runs | dispatch order
   char* b = static_cast<char*>(base);
   const int64_t n_bytes = align_up(p.visits * p.n * p.heads * int64_t(p.d) * 4);
   const int64_t ml_bytes = align_up(p.visits * p.n * p.heads * int64_t(2) * 4);
   const int64_t it_bytes = align_up(int64_t(p.dev_items.size()) * sizeof(WorkItem));
+  const int64_t run_bytes = align_up(int64_t(p.dev_runs.size()) * sizeof(KeyRun));
   float* n_slots = reinterpret_cast<float*>(b);
   float* ml_slots = reinterpret_cast<float*>(b + n_bytes);
   WorkItem* items = reinterpret_cast<WorkItem*>(b + n_bytes + ml_bytes);
   KeyRun* runs = reinterpret_cast<KeyRun*>(b + n_bytes + ml_bytes + it_bytes);
+  int32_t* order = p.dev_order.empty() ? nullptr : reinterpret_cast<int32_t*>(b + n_bytes + ml_bytes + it_bytes + run_bytes);
   // The tables are rewritten on every call, in stream order: a call on another stream that
   // still runs reads the same array (calls that overlap on one device race).
   hipError_t e = hipMemcpyAsync(items, p.dev_items.data(), p.dev_items.size() * sizeof(WorkItem),
                                 hipMemcpyHostToDevice, stream);
   if (e == hipSuccess && !p.dev_runs.empty())
     e = hipMemcpyAsync(runs, p.dev_runs.data(), p.dev_runs.size() * sizeof(KeyRun), hipMemcpyHostToDevice, stream);
+  if (e == hipSuccess && order != nullptr)
+    e = hipMemcpyAsync(order, p.dev_order.data(), p.dev_order.size() * sizeof(int32_t), hipMemcpyHostToDevice, stream);
   if (e != hipSuccess) {
     why = std::string("hipMemcpyAsync(descriptor tables): ") + hipGetErrorString(e);
     return CQSA_EHIP;
   }
   // Every visit slot of every row is written by the partial kernel before the merge
   // reads it, so nothing left in the array by an earlier call is read.
-  st = run_partials_with(p, q, k, v, n_slots, ml_slots, items, runs, stream, why);
+  st = run_partials_with(p, q, k, v, n_slots, ml_slots, items, runs, order, stream, why);
   if (st != CQSA_OK) return st;
   return run_merge(p, n_slots, ml_slots, o, lse, stream, why);
 }

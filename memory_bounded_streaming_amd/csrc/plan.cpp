@@ -287,6 +287,71 @@ bool admitted_pair(const Plan& p, const Task& t, int64_t a, int64_t b) {
   return false;
 }
 
+// Dispatch order of a causal plan's device-resident partial launch.  Its workgroups
+// differ in work (a query tile sees its diagonal run only up to its own rows, so the
+// later tiles of an item see more keys), and the hardware deals workgroup b to XCD b % 8;
+// with whole chunks dealt round-robin, the chunk count and their uneven work leave some
+// XCDs idle at the end.  Here the chunks (the kernel's cut of each (item, head) group into
+// chunks of at most kDispatchChunk tiles, which keeps a chunk's K/V stream in one L2) go
+// heaviest first to the XCD with the least work, and inside a chunk the heavier tiles go
+// first.  Entry 8k + x is the k-th workgroup of XCD x.  Work of a tile: its 64-key (bf16)
+// or 32-key tiles after the causal cut, plus four for the workgroup's fixed cost.  The
+// order changes no result, only which workgroup runs where and when.
+void build_dispatch(Plan& p) {
+  p.dev_order.clear();
+  const bool bf = p.dtype == CQSA_BF16;
+  const int64_t qt = bf ? kAttnQueryTileBf16 : kAttnQueryTileF32, kt = bf ? kAttnKeyTileBf16 : kAttnKeyTileF32;
+  const int64_t tiles = (p.unit + qt - 1) / qt, items = static_cast<int64_t>(p.dev_items.size());
+  const int64_t wgs = items * p.heads * tiles;
+  if (wgs == 0 || wgs + 8 * kDispatchChunk > kMaxDispatchEntries) return;  // arithmetic order
+  const int64_t per = (tiles + kDispatchChunk - 1) / kDispatchChunk, ct = (tiles + per - 1) / per;
+  std::vector<int64_t> work(items * tiles);
+  for (int64_t i = 0; i < items; ++i) {
+    const WorkItem& it = p.dev_items[i];
+    for (int64_t t = 0; t < tiles; ++t) {
+      const int64_t qhi = std::min<int64_t>(it.q_len, (t + 1) * qt);
+      int64_t w = 4;
+      for (int32_t r = it.run0; r < it.run0 + it.nrun; ++r) {
+        const KeyRun& run = p.dev_runs[r];
+        const int64_t len = run.diag >= 0 ? std::min<int64_t>(run.len, run.diag + qhi) : run.len;
+        if (len > 0) w += (len + kt - 1) / kt;
+      }
+      work[i * tiles + t] = w;
+    }
+  }
+  struct Chunk {
+    int64_t work, group, first, count;
+  };
+  std::vector<Chunk> chunks;
+  for (int64_t g = 0; g < items * p.heads; ++g)
+    for (int64_t c = 0; c < per; ++c) {
+      const int64_t first = c * ct, count = std::min(tiles, first + ct) - first;
+      if (count <= 0) continue;
+      int64_t w = 0;
+      for (int64_t t = first; t < first + count; ++t) w += work[(g / p.heads) * tiles + t];
+      chunks.push_back({w, g, first, count});
+    }
+  std::stable_sort(chunks.begin(), chunks.end(), [](const Chunk& a, const Chunk& b) { return a.work > b.work; });
+  std::vector<std::vector<int32_t>> seq(8);
+  int64_t load[8] = {};
+  std::vector<int64_t> order;
+  for (const Chunk& ch : chunks) {
+    const int x = static_cast<int>(std::min_element(load, load + 8) - load);
+    load[x] += ch.work;
+    order.clear();
+    for (int64_t t = ch.first; t < ch.first + ch.count; ++t) order.push_back(t);
+    const int64_t item = ch.group / p.heads;
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int64_t a, int64_t b) { return work[item * tiles + a] > work[item * tiles + b]; });
+    for (int64_t t : order) seq[x].push_back(static_cast<int32_t>(ch.group * tiles + t));
+  }
+  size_t rounds = 0;
+  for (const auto& q : seq) rounds = std::max(rounds, q.size());
+  p.dev_order.assign(8 * rounds, -1);
+  for (int x = 0; x < 8; ++x)
+    for (size_t k = 0; k < seq[x].size(); ++k) p.dev_order[8 * k + x] = seq[x][k];
+}
+
 // Kernel descriptor tables.  Key runs are split wherever the task's local order is not
 // globally contiguous, in both tables, so device-resident and streamed execution walk
 // identical key tiles and give identical bits.
@@ -336,6 +401,8 @@ void build_descriptors(Plan& p) {
   // heaviest query blocks first in the one-launch device path (load balance only)
   std::stable_sort(p.dev_items.begin(), p.dev_items.end(),
                    [](const WorkItem& x, const WorkItem& y) { return x.keys > y.keys; });
+  p.dev_order.clear();
+  if (causal) build_dispatch(p);
 
   p.dev_kitems.clear();
   p.dev_kruns.clear();
@@ -387,7 +454,8 @@ void build_descriptors(Plan& p) {
 }  // namespace
 
 int64_t descriptor_bytes(const Plan& p) {
-  return align_up(int64_t(p.dev_items.size()) * sizeof(WorkItem)) +
+  return align_up(int64_t(p.dev_order.size()) * int64_t(sizeof(int32_t))) +
+         align_up(int64_t(p.dev_items.size()) * sizeof(WorkItem)) +
          align_up(int64_t(p.dev_runs.size()) * sizeof(KeyRun)) +
          align_up(int64_t(p.dev_kitems.size()) * sizeof(WorkItem)) +
          align_up(int64_t(p.dev_kruns.size()) * sizeof(KeyRun)) +
@@ -614,11 +682,12 @@ cqsa_status build_plan(int64_t n, int heads, int d, cqsa_dtype dtype, const int3
 namespace {
 
 // Upper bound of descriptor_bytes from the plan's shape alone: at most one work item per
-// (task, unit) in each of the five item tables and one key run per (task, query unit, key
-// unit) in each of the four run tables.
+// (task, unit) in each of the five item tables, one key run per (task, query unit, key
+// unit) in each of the four run tables, and for a causal plan the largest dispatch table.
 int64_t descriptor_bound(const Plan& p) {
   const int64_t items = p.n_units * p.task_units, runs = items * p.task_units;
-  return 5 * align_up(items * int64_t(sizeof(WorkItem))) + 4 * align_up(runs * int64_t(sizeof(KeyRun)));
+  const int64_t order = (p.flags & CQSA_FLAG_CAUSAL) ? align_up(kMaxDispatchEntries * int64_t(sizeof(int32_t))) : 0;
+  return 5 * align_up(items * int64_t(sizeof(WorkItem))) + 4 * align_up(runs * int64_t(sizeof(KeyRun))) + order;
 }
 
 // First staging mode (in cqsa_mode order, respecting the flags) whose workspace fits, by

@@ -64,6 +64,9 @@ struct Plan {
   // kernel descriptors
   std::vector<WorkItem> dev_items;      // all (task, unit) items, global coordinates
   std::vector<KeyRun> dev_runs;
+  // causal plans: dispatch order of the device-resident partial launch (entry b = the
+  // workgroup block b runs, (item * heads + head) * tiles + tile, or -1); empty otherwise
+  std::vector<int32_t> dev_order;
   std::vector<WorkItem> stream_items;   // item (t, a) at index t*task_units + a, block coordinates
   std::vector<KeyRun> stream_runs;
   // causal dK/dV: (task, key unit) items whose runs are the admitted query units at or

@@ -4,7 +4,7 @@
 #include "../../memory_bounded_streaming_amd/csrc/kernels.hpp"
 #include "../../memory_bounded_streaming_amd/csrc/engine.hpp"
 namespace cqsa {
-int attn_query_tile(cqsa_dtype dtype) { return dtype == CQSA_BF16 ? 256 : 64; }
+int attn_query_tile(cqsa_dtype dtype) { return dtype == CQSA_BF16 ? kAttnQueryTileBf16 : kAttnQueryTileF32; }
 hipError_t launch_attn(const AttnLaunch&, hipStream_t) { std::abort(); }
 hipError_t launch_merge(const MergeLaunch&, hipStream_t) { std::abort(); }
 int bwd_key_tile(cqsa_dtype) { return 128; }
