@@ -16,7 +16,9 @@ peak device memory (modelled and observed) against the budget, the forward error
 sampled rows against the fp64 oracle, and the oracle itself timed on those rows on the
 host's cores.  Secondary keys: the device-resident N=57,344 workload, its backward, the
 16 GiB streamed workload (N=212,992, 16 heads) and its backward, and the billion-token
-dry run priced with this run's rates.
+dry run priced with this run's rates.  For reference, measured on the same box after the
+timed calls: a device copy and the vendor bf16 GEMM (`ceilings`), and the vendor's fused
+attention (torch scaled_dot_product_attention) on the device-resident workload's inputs.
 """
 import argparse
 import hashlib
@@ -392,6 +394,57 @@ def box_ceilings(torch, reps=10):
     return out
 
 
+def vendor_attention(args, torch, reps=5):
+    """The vendor's fused attention on the device-resident workload's inputs (the same
+    seeded bf16 Q/K/V, N=57344, 8 heads, d=128, scale 1/sqrt(d)): torch's
+    scaled_dot_product_attention restricted to its flash backend (else its memory-efficient
+    one; never the unfused math path), non-causal and causal, timed with HIP events.  A
+    reference measured on the same box, like the GEMM ceiling: undivided attention with no
+    memory budget, so it bounds nothing about the CQS path and is not part of it."""
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    from memory_bounded_streaming_amd.inputs import gen_qkv
+    n, h, d, _, _, _ = WORKLOADS["device_n57344"]
+    q, k, v = gen_qkv(args.seed, n, h, d, "bf16")
+    # [N, H, d] -> [1, H, N, d], contiguous, outside the timed region
+    dev = [torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda().view(n, h, d).permute(1, 0, 2)
+           .contiguous().unsqueeze(0) for x in (q, k, v)]
+    sdpa = torch.nn.functional.scaled_dot_product_attention
+    out = {"workload": "N=57344, 8 heads, d=128, bf16, the device-resident workload's inputs, undivided",
+           "call": "torch.nn.functional.scaled_dot_product_attention"}
+    for name, causal in (("noncausal", False), ("causal", True)):
+        res = None
+        for backend in (SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION):
+            try:
+                with sdpa_kernel([backend]):
+                    o = sdpa(*dev, is_causal=causal)
+                    torch.cuda.synchronize()
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    for _ in range(reps):
+                        o = sdpa(*dev, is_causal=causal)
+                    e1.record()
+                    torch.cuda.synchronize()
+                ms = e0.elapsed_time(e1) / reps
+                flop = 2.0 * n * (n + 1) * d * h if causal else 4.0 * n * n * d * h
+                res = {"backend": backend.name.lower(), "ms": round(ms, 4), "tflops": round(flop / (ms / 1e3) / 1e12, 1)}
+                del o
+                break
+            except RuntimeError as ex:
+                res = {"error": f"{backend.name.lower()}: {str(ex)[:160]}"}
+        out[name] = res
+    del dev
+    torch.cuda.empty_cache()
+    return out
+
+
+def vendor_ratio(value, vendor, key):
+    """A whole CQS forward step's useful TFLOP/s over the vendor attention's on the same
+    inputs (None when the vendor call was not measured)."""
+    if not vendor or "error" in vendor or not vendor.get(key) or "tflops" not in vendor[key]:
+        return None
+    return round(value / vendor[key]["tflops"], 3)
+
+
 def pinned_inputs(torch, seed, n, h, d, count=3):
     """Q, K, V (and dO for count=4) drawn straight into pinned host memory."""
     from memory_bounded_streaming_amd.inputs import gen_tensor
@@ -614,6 +667,13 @@ def main():
         if "error" not in dcausal:
             log(f"bench: device-resident causal {dcausal['value']:.1f} useful TFLOP/s, partial kernel "
                 f"{dcausal['attn_tflops']:.1f}")
+    vendor = None
+    if not args.no_device:
+        log("bench: vendor fused attention on the device-resident workload's inputs")
+        vendor = guarded("vendor attention", lambda: vendor_attention(args, torch))
+        if "error" not in vendor:
+            log("bench: vendor attention " + ", ".join(
+                f"{k} {vendor[k].get('tflops', vendor[k].get('error'))}" for k in ("noncausal", "causal")))
     bwd = None
     if not args.no_backward and dres is not None:
         log("bench: backward of the device-resident workload")
@@ -679,6 +739,7 @@ def main():
             "merge": {"bound": "hbm", "achieved": round(dres["merge_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                       "frac": round(dres["merge_gbs"] / HBM_PEAK_GBS, 4), "bytes_per_launch": dres["merge_bytes"],
                       "avg_launch_ms": round(dres["merge_ms"], 4)},
+            "vs_vendor_attention": vendor_ratio(dres["value"], vendor, "noncausal"),
         }
     device_causal = None
     if dcausal is not None:
@@ -692,6 +753,7 @@ def main():
                          "unit": "TFLOP/s", "frac": round(dcausal["attn_tflops"] / BF16_MFMA_PEAK_TFLOPS, 4),
                          "avg_launch_ms": round(dcausal["attn_ms"], 4),
                          "note": "achieved = useful FLOP 2 N (N+1) d H / partial-kernel time"},
+            "vs_vendor_attention": vendor_ratio(dcausal["value"], vendor, "causal"),
         }
     line = {
         "metric": METRIC,
@@ -735,6 +797,7 @@ def main():
                   "frac_of_measured_ceiling": (round(head["merge_gbs"] / ceil["hbm_copy_gbs"], 4)
                                                if "error" not in ceil else None)},
         "ceilings": ceil,
+        "vendor_attention": vendor,
         "stream": head["stream"],
         "memory": head["memory"],
         "error": head.get("error"),
