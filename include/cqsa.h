@@ -314,7 +314,7 @@ cqsa_status cqsa_merge(const cqsa_plan* plan, const float* n_in, const float* ml
  *   after every step the host-pinned path enqueues (streams effectively serialised);
  *   CQSA_CANARY=1 surrounds every piece of the host-pinned workspace with guard words
  *   and checks them after the call (EHIP naming the piece if one was overwritten).
- * Errors: EINVAL, ESMALL, EBUDGET (device path over budget), EHIP, ENOMEM.
+ * Errors: EINVAL, ESMALL, EBUDGET (device path: workspace plus descriptor tables over the budget), EHIP, ENOMEM.
  */
 cqsa_status cqsa_forward(const cqsa_plan* plan, const void* q, const void* k, const void* v,
                          void* o, float* lse, cqsa_residency res, void* workspace,
@@ -383,7 +383,7 @@ cqsa_status cqsa_backward_workspace_size(const cqsa_plan* plan, cqsa_residency r
  *   stats: optional; t_attn_ms = the two gradient kernels, t_merge_ms = the Delta /
  *     transpose pass and the slot sums, useful_flop = 2.5 times the forward's
  *     (10 N^2 d H; 5 N (N+1) d H with CQSA_FLAG_CAUSAL).
- * Errors: EINVAL, ESMALL, EBUDGET (workspace over the plan's budget), EHIP, ENOMEM.
+ * Errors: EINVAL, ESMALL, EBUDGET (workspace plus the plan's descriptor tables over its budget), EHIP, ENOMEM.
  */
 cqsa_status cqsa_backward(const cqsa_plan* plan, const void* q, const void* k, const void* v,
                           const void* o, const float* lse, const void* d_o, void* dq, void* dk,

@@ -29,6 +29,8 @@ CQSA_BF16, CQSA_F32 = 0, 1
 CQSA_RES_DEVICE, CQSA_RES_HOST_PINNED = 0, 1
 CQSA_FLAG_HOST_ACC, CQSA_FLAG_KV_SINGLE, CQSA_FLAG_PAD, CQSA_FLAG_CAUSAL = 0x1, 0x2, 0x4, 0x8
 CQSA_FLAG_FREE_BUDGET = 0x10
+(CQSA_OK, CQSA_EINVAL, CQSA_ENOSET, CQSA_EDIVIDE, CQSA_EBUDGET, CQSA_EHIP, CQSA_ENOMEM,
+ CQSA_ESMALL) = 0, -1, -2, -3, -4, -5, -6, -7
 MODE_NAMES = {1: "device_acc_kv2", 2: "host_acc_kv2", 3: "device_acc_kv1", 4: "host_acc_kv1"}
 MAX_LEVELS = 12
 

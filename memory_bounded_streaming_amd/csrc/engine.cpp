@@ -1322,8 +1322,9 @@ cqsa_status run_backward(const Plan& p, const void* q, const void* k, const void
     why = "unknown residency";
     return CQSA_EINVAL;
   }
-  if (p.budget > 0 && p.bwd_device_ws > p.budget) {
-    why = "device-resident backward needs " + std::to_string(p.bwd_device_ws) + " workspace bytes, over the budget";
+  if (p.budget > 0 && p.bwd_device_ws + table_bytes(p) > p.budget) {
+    why = "device-resident backward needs " + std::to_string(p.bwd_device_ws) + " workspace bytes and " +
+          std::to_string(table_bytes(p)) + " descriptor bytes, over the budget";
     return CQSA_EBUDGET;
   }
   MemWatch mw;

@@ -86,3 +86,26 @@ def test_fault_injection_arguments():
         cqsa.cqsa_debug_fail_allocations(-1)
     assert e.value.status == -1
     cqsa.cqsa_debug_fail_allocations(0)
+
+
+@pytest.mark.skipif(__import__("torch").cuda.device_count() > 0,
+                    reason="passes placeholder device pointers; the budget test must reject the call before any "
+                           "HIP call, which only a host without a GPU shows safely")
+def test_device_paths_count_descriptor_tables_against_the_budget():
+    """A budget that holds a device-resident call's workspace exactly, but not the plan's
+    descriptor tables beside it, is rejected with EBUDGET before any HIP call, by the
+    forward and the backward alike (the tables are uploaded to the device with the
+    workspace, so both count against the budget the plan was made for)."""
+    placeholder = 1 << 20  # 16-byte aligned, never dereferenced: the call ends at the budget test
+    with cqsa.Plan(57344, 8, 128, cqsa.CQSA_BF16, [3]) as free:
+        fwd_ws = free.workspace_size(cqsa.CQSA_RES_DEVICE)
+        bwd_ws = free.backward_workspace_size(cqsa.CQSA_RES_DEVICE)
+    for budget, call in ((fwd_ws, "forward"), (bwd_ws, "backward")):
+        with cqsa.Plan(57344, 8, 128, cqsa.CQSA_BF16, [3], budget_bytes=budget) as p:
+            with pytest.raises(cqsa.CqsaError) as exc:
+                if call == "forward":
+                    p.forward(placeholder, placeholder, placeholder, placeholder, placeholder)
+                else:
+                    p.backward(*([placeholder] * 9))  # q, k, v, o, lse, dO, dQ, dK, dV
+            assert exc.value.status == cqsa.CQSA_EBUDGET, (call, exc.value)
+            assert "descriptor bytes" in str(exc.value), (call, str(exc.value))
