@@ -20,7 +20,7 @@ from oracle.plan import make_plan
 from oracle.stream_bytes import stream_traffic
 from oracle.tolerance import BF16_LSE_TOL, BF16_REL_TOL, error_report
 
-from gpu_util import as_f64, log, oracle_rows, pinned, pinned_qkv
+from gpu_util import as_f64, init_device_runtime, log, oracle_rows, pinned, pinned_qkv
 
 pytestmark = pytest.mark.gpu
 GiB = 1 << 30
@@ -38,6 +38,9 @@ def test_streamed_workload_sampled_rows(name):
     torch = pytest.importorskip("torch")
     n, h, d, levels, budget, r_count, mode = WORKLOADS[name]
     os.environ["CQSA_PROGRESS"] = "1"
+    # the runtime's one-time device set-up is not the call's: make it happen first, so the
+    # observed peak below is the call's own whichever case runs first in the process
+    log(f"{name}: runtime first-use set-up took {init_device_runtime() / (1 << 20):.0f} MiB")
     log(f"{name}: drawing inputs into pinned memory")
     t0 = time.time()
     (tq, tk, tv), (q, k, v) = pinned_qkv(0, n, h, d, "bf16")

@@ -22,7 +22,7 @@ from memory_bounded_streaming_amd.inputs import gen_qkv
 from oracle.attention import attention_fp64
 from oracle.tolerance import BF16_LSE_TOL, BF16_REL_TOL, rowwise_rel_err
 
-from gpu_util import as_f64, log, pinned
+from gpu_util import as_f64, init_device_runtime, log, pinned
 
 pytestmark = pytest.mark.gpu
 MiB = 1 << 20
@@ -91,6 +91,7 @@ def test_budget_from_free_device_memory():
     n, h, d = 7 * 2048, 4, 128
     q, k, v = gen_qkv(8, n, h, d, "bf16")
     (tq, tk, tv), to, oa, tl = _pinned_inputs(q, k, v, n, h, d)
+    init_device_runtime()  # the runtime's one-time device set-up is not the call's
     torch.cuda.synchronize()
     free, _ = torch.cuda.mem_get_info()
     margin = free - 64 * MiB  # leaves a 64 MiB budget: the undivided plan does not fit
