@@ -134,12 +134,14 @@ def traffic_record(fetch_csv, write_csv, kernel_hash, workload=TRAFFIC_WORKLOADS
     }
 
 
-def copy_summary(trace_csv):
+def copy_summary(trace_csv, streams=None):
     """Host-to-device and device-to-host busy time from a rocprofv3 memory-copy trace.
 
     For each direction: the number of copies, the union of their [start, end] intervals
     (copies on several streams at once count once) and the span from the first start to
     the last end, in ms.  Byte counts are not in the trace; the engine's counters give them.
+    streams: if given, only copies on these rocprofv3 stream ids count (the engine's copy
+    streams, leaving out the bench's own set-up and pinned-rate copies on other streams).
     """
     import csv
     iv = {"h2d": [], "d2h": []}
@@ -147,7 +149,7 @@ def copy_summary(trace_csv):
         for row in csv.DictReader(f):
             direction = (row.get("Direction") or "").upper()
             key = "h2d" if "HOST_TO_DEVICE" in direction else "d2h" if "DEVICE_TO_HOST" in direction else None
-            if key is None:
+            if key is None or (streams is not None and row.get("Stream_Id") not in streams):
                 continue
             iv[key].append((int(row["Start_Timestamp"]), int(row["End_Timestamp"])))
     out = {}
@@ -629,6 +631,8 @@ def main():
                     help="which workload's record --traffic-record writes")
     ap.add_argument("--copy-summary", metavar="TRACE_CSV",
                     help="print the copy busy times of a rocprofv3 memory-copy trace and exit (no GPU use)")
+    ap.add_argument("--copy-streams", metavar="IDS",
+                    help="with --copy-summary: comma-separated rocprofv3 stream ids to count (default: all)")
     args = ap.parse_args()
     if args.traffic_record:
         rec = traffic_record(args.traffic_record[0], args.traffic_record[1], kernel_source_hash(),
@@ -639,7 +643,8 @@ def main():
         print(json.dumps(rec))
         return
     if args.copy_summary:
-        print(json.dumps(copy_summary(args.copy_summary)))
+        streams = set(args.copy_streams.split(",")) if args.copy_streams else None
+        print(json.dumps(copy_summary(args.copy_summary, streams)))
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path",
