@@ -64,3 +64,23 @@ def test_copy_summary_takes_the_union_of_copy_intervals(tmp_path):
     out = bench.copy_summary(str(path))
     assert out["h2d"] == {"copies": 3, "busy_ms": 7.0, "span_ms": 11.0}
     assert out["d2h"] == {"copies": 2, "busy_ms": 3.0, "span_ms": 5.0}
+
+
+def test_copy_summary_counts_only_the_given_streams(tmp_path):
+    # copies on stream 0 (the bench's own) are left out when the engine's streams are named
+    path = tmp_path / "copies.csv"
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kind", "Direction", "Stream_Id", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for d, sid, b, e in [("MEMORY_COPY_HOST_TO_DEVICE", "0", 0, 5_000_000),
+                             ("MEMORY_COPY_HOST_TO_DEVICE", "1", 1_000_000, 3_000_000),
+                             ("MEMORY_COPY_HOST_TO_DEVICE", "2", 2_000_000, 4_000_000),
+                             ("MEMORY_COPY_DEVICE_TO_HOST", "2", 6_000_000, 7_000_000),
+                             ("MEMORY_COPY_DEVICE_TO_HOST", "0", 8_000_000, 12_000_000)]:
+            w.writerow({"Kind": "MEMORY_COPY", "Direction": d, "Stream_Id": sid, "Start_Timestamp": b,
+                        "End_Timestamp": e})
+    out = bench.copy_summary(str(path), {"1", "2"})
+    assert out["h2d"] == {"copies": 2, "busy_ms": 3.0, "span_ms": 3.0}
+    assert out["d2h"] == {"copies": 1, "busy_ms": 1.0, "span_ms": 1.0}
+    every = bench.copy_summary(str(path))
+    assert every["h2d"]["busy_ms"] == 5.0 and every["d2h"]["busy_ms"] == 5.0
