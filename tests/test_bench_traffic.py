@@ -84,3 +84,13 @@ def test_copy_summary_counts_only_the_given_streams(tmp_path):
     assert out["d2h"] == {"copies": 1, "busy_ms": 1.0, "span_ms": 1.0}
     every = bench.copy_summary(str(path))
     assert every["h2d"]["busy_ms"] == 5.0 and every["d2h"]["busy_ms"] == 5.0
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The bench runs on one GPU: --gpus 2 exits with status 2 and says why, before any
+    GPU or torch use."""
+    import subprocess
+    proc = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                          capture_output=True, text=True, timeout=120)
+    assert proc.returncode == 2
+    assert "one GPU" in proc.stderr and proc.stdout == ""
