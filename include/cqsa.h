@@ -55,7 +55,8 @@ typedef CQSA_INT_ENUM(cqsa_status_e) {
   CQSA_EINVAL = -1,   /* bad argument (null pointer, size, unsupported d/dtype/flag) */
   CQSA_ENOSET = -2,   /* no perfect difference set for this l (l = 7) */
   CQSA_EDIVIDE = -3,  /* N is not a multiple of prod(c_k) (and CQSA_FLAG_PAD unset) or N < prod(c_k) */
-  CQSA_EBUDGET = -4,  /* no staging mode fits the memory budget */
+  CQSA_EBUDGET = -4,  /* no staging mode fits the memory budget, or a device-resident call's
+                         workspace and descriptor tables exceed it */
   CQSA_EHIP = -5,     /* a HIP runtime call failed */
   CQSA_ENOMEM = -6,   /* a host or device allocation failed */
   CQSA_ESMALL = -7    /* a caller buffer or workspace is smaller than required */
