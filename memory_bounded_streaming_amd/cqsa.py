@@ -19,7 +19,8 @@ import numpy as np
 __all__ = [
     "CqsaError", "load", "CQSA_BF16", "CQSA_F32", "CQSA_RES_DEVICE", "CQSA_RES_HOST_PINNED",
     "CQSA_FLAG_HOST_ACC", "CQSA_FLAG_KV_SINGLE", "CQSA_FLAG_PAD", "CQSA_FLAG_CAUSAL", "CQSA_FLAG_FREE_BUDGET",
-    "MODE_NAMES", "cqsa_plan_fallback", "cqsa_debug_fail_allocations",
+    "CQSA_OK", "CQSA_EINVAL", "CQSA_ENOSET", "CQSA_EDIVIDE", "CQSA_EBUDGET", "CQSA_EHIP", "CQSA_ENOMEM",
+    "CQSA_ESMALL", "MODE_NAMES", "cqsa_plan_fallback", "cqsa_debug_fail_allocations",
     "cqsa_version", "cqsa_difference_set", "cqsa_plan_create", "cqsa_plan_info_get", "cqsa_plan_schedule",
     "cqsa_plan_coverage", "cqsa_plan_destroy", "cqsa_workspace_size", "cqsa_partials", "cqsa_merge",
     "cqsa_forward", "cqsa_forward_noalloc", "cqsa_backward_workspace_size", "cqsa_backward", "cqsa_plan_estimate", "cqsa_status_string", "cqsa_last_error", "Plan",
