@@ -120,6 +120,11 @@ typedef struct {
   int64_t host_acc_bytes;       /* pinned host accumulator the host-pinned path allocates (0 if on device) */
   double useful_flop;           /* 4 * N^2 * d * H; 2 * N * (N+1) * d * H with CQSA_FLAG_CAUSAL */
   int64_t padded_tokens;        /* N_pad = unit_tokens * n_units (== n_tokens unless padded) */
+  int32_t bwd_stream_mode;      /* cqsa_mode of the host-pinned backward, 0 if none fits the budget */
+  int32_t bwd_host_stats;       /* 1: that backward keeps L and Delta of every row in pinned host
+                                   memory and gathers each task's rows with its staging (chosen
+                                   only when no layout with them on the device fits) */
+  int64_t bwd_stream_workspace_bytes; /* device bytes of that backward, -1 if none fits */
 } cqsa_plan_info;
 
 typedef struct {

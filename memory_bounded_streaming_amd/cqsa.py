@@ -56,7 +56,8 @@ class PlanInfo(ctypes.Structure):
         ("stream_mode", ctypes.c_int32), ("kv_buffers", ctypes.c_int32),
         ("stream_workspace_bytes", ctypes.c_int64), ("device_workspace_bytes", ctypes.c_int64),
         ("host_acc_bytes", ctypes.c_int64), ("useful_flop", ctypes.c_double),
-        ("padded_tokens", ctypes.c_int64),
+        ("padded_tokens", ctypes.c_int64), ("bwd_stream_mode", ctypes.c_int32), ("bwd_host_stats", ctypes.c_int32),
+        ("bwd_stream_workspace_bytes", ctypes.c_int64),
     ]
 
 

@@ -157,6 +157,12 @@ cqsa_status cqsa_plan_info_get(const cqsa_plan* plan, cqsa_plan_info* out) {
     out->host_acc_bytes = p.host_acc_bytes;
     out->useful_flop = p.useful_flop();
     out->padded_tokens = p.n_pad;
+    const cqsa::Footprint& b = p.bwd_stream_fp;
+    out->bwd_stream_mode = b.bytes < 0 ? 0
+                           : b.acc_on_device ? (b.kv_buffers == 2 ? CQSA_MODE_DEVICE_ACC_KV2 : CQSA_MODE_DEVICE_ACC_KV1)
+                                             : (b.kv_buffers == 2 ? CQSA_MODE_HOST_ACC_KV2 : CQSA_MODE_HOST_ACC_KV1);
+    out->bwd_host_stats = p.bwd_host_stats ? 1 : 0;
+    out->bwd_stream_workspace_bytes = b.bytes;
     return ok();
   });
 }

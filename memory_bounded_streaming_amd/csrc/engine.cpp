@@ -971,6 +971,7 @@ struct BwdStreamRes {
   void* ws = nullptr;
   bool own_ws = false;
   float* host_acc = nullptr;
+  float* host_delta = nullptr;  // Delta [H][N] in pinned host memory (host-statistics layouts)
   ~BwdStreamRes() {
     (void)hipStreamSynchronize(caller);
     for (hipStream_t x : s)
@@ -980,6 +981,7 @@ struct BwdStreamRes {
       if (x) (void)hipStreamDestroy(x);
     if (own_ws && ws) (void)hipFree(ws);
     if (host_acc) (void)hipHostFree(host_acc);
+    if (host_delta) (void)hipHostFree(host_delta);
   }
   hipError_t event(hipEvent_t& e) {
     hipError_t r = hipEventCreateWithFlags(&e, hipEventDisableTiming);
@@ -1007,7 +1009,8 @@ cqsa_status backward_stream(const Plan& p, const char* q, const char* k, const c
   if (stats) mw.begin();
   const bool dev_acc = p.bwd_stream_fp.acc_on_device;
   const int nset = p.bwd_stream_fp.kv_buffers;
-  const BwdStreamLayout L = bwd_stream_layout(p, dev_acc, nset);
+  const bool host_stats = p.bwd_host_stats;
+  const BwdStreamLayout L = bwd_stream_layout(p, dev_acc, nset, host_stats);
   DeviceTables tabs{};
   cqsa_status st = device_tables(p, tabs, why);
   if (st != CQSA_OK) return st;
@@ -1031,8 +1034,10 @@ cqsa_status backward_stream(const Plan& p, const char* q, const char* k, const c
   };
   const int64_t H = p.heads, D = p.d, U = p.unit, N = p.n, T = p.task_tokens(), e = p.elem_bytes();
   const int64_t row_in = p.row_in_bytes(), hd = H * D;
-  float* lse_d = reinterpret_cast<float*>(take(L.lse));
-  float* delta_d = reinterpret_cast<float*>(take(L.delta));
+  // L and Delta of every row: on the device for the call, or (host_stats) L where the caller
+  // keeps it and Delta in pinned host memory of the call's own
+  float* lse_d = host_stats ? nullptr : reinterpret_cast<float*>(take(L.lse));
+  float* delta_d = host_stats ? nullptr : reinterpret_cast<float*>(take(L.delta));
   struct Stage {
     char* t[4];      // Q, K, V, dO of the task
     char* tr[3];     // Q^T, K^T, dO^T
@@ -1066,6 +1071,8 @@ cqsa_status backward_stream(const Plan& p, const char* q, const char* k, const c
     for (int g = 0; g < 3; ++g) host_acc[g] = R.host_acc + g * N * hd;
   }
   char* outs[3] = {dq, dk, dv};
+  if (host_stats)
+    HIP_TRY(hipHostMalloc(reinterpret_cast<void**>(&R.host_delta), H * N * sizeof(float), hipHostMallocDefault));
 
   for (auto& s : R.s) HIP_TRY(hipStreamCreateWithFlags(&s, hipStreamNonBlocking));
   mw.poll();
@@ -1089,12 +1096,16 @@ cqsa_status backward_stream(const Plan& p, const char* q, const char* k, const c
   hipEvent_t tev;
   int64_t bytes_h2d = 0, bytes_d2h = 0, n_attn = 0, n_merge = 0, n_h2d = 0, n_d2h = 0;
 
-  // phase 0: LSE to the device, Delta of every row from O and dO in unit blocks
-  HIP_TRY(tm.begin(PH_H2D, s_h, tev));
-  HIP_TRY(hipMemcpyAsync(lse_d, lse, H * N * sizeof(float), hipMemcpyHostToDevice, s_h));
-  HIP_TRY(tm.end(PH_H2D, s_h));
-  bytes_h2d += H * N * 4;
-  ++n_h2d;
+  // phase 0: LSE to the device, Delta of every row from O and dO in unit blocks (with
+  // host_stats each block of Delta goes back to pinned host memory, through the first
+  // staging set's Delta rows, which no task uses yet)
+  if (!host_stats) {
+    HIP_TRY(tm.begin(PH_H2D, s_h, tev));
+    HIP_TRY(hipMemcpyAsync(lse_d, lse, H * N * sizeof(float), hipMemcpyHostToDevice, s_h));
+    HIP_TRY(tm.end(PH_H2D, s_h));
+    bytes_h2d += H * N * 4;
+    ++n_h2d;
+  }
   for (int64_t r0 = 0; r0 < N; r0 += U) {
     const int64_t rows = std::min(U, N - r0);
     if (r0 > 0) HIP_TRY(hipStreamWaitEvent(s_h, stage_free[0], 0));
@@ -1113,11 +1124,19 @@ cqsa_status backward_stream(const Plan& p, const char* q, const char* k, const c
     pr.n = rows;
     pr.o = stg[0];
     pr.d_o = stg[3];
-    pr.delta = delta_d + r0;
-    pr.dpitch = N;
+    pr.delta = host_stats ? set[0].ds : delta_d + r0;
+    pr.dpitch = host_stats ? U : N;
     HIP_TRY(tm.begin(PH_MERGE, s_c, tev));
     HIP_TRY(launch_bwd_prep(pr, s_c));
     HIP_TRY(tm.end(PH_MERGE, s_c));
+    if (host_stats) {
+      // rows [r0, r0 + rows) of every head: [H][U] on the device to [H][N] on the host
+      HIP_TRY(tm.begin(PH_D2H, s_c, tev));
+      HIP_TRY(hipMemcpy2DAsync(R.host_delta + r0, N * 4, set[0].ds, U * 4, rows * 4, H, hipMemcpyDeviceToHost, s_c));
+      HIP_TRY(tm.end(PH_D2H, s_c));
+      bytes_d2h += H * rows * 4;
+      ++n_d2h;
+    }
     HIP_TRY(hipEventRecord(stage_free[0], s_c));
   }
 
@@ -1174,17 +1193,31 @@ cqsa_status backward_stream(const Plan& p, const char* q, const char* k, const c
         bytes_h2d += g.length * row_in;
         ++n_h2d;
       }
+    if (host_stats) {
+      // the task's L and Delta rows, [H][T], from pinned host memory with the staging; the
+      // host Delta is complete: this stream waited for the first set's release, recorded
+      // after the last Delta block went back, before staging the first task
+      for (const Segment& g : task.segments) {
+        HIP_TRY(hipMemcpy2DAsync(G.ls + g.local_offset, T * 4, lse + g.global_start, N * 4, g.length * 4, H,
+                                 hipMemcpyHostToDevice, s_h));
+        HIP_TRY(hipMemcpy2DAsync(G.ds + g.local_offset, T * 4, R.host_delta + g.global_start, N * 4, g.length * 4,
+                                 H, hipMemcpyHostToDevice, s_h));
+        bytes_h2d += 2 * H * g.length * 4;
+        n_h2d += 2;
+      }
+    }
     HIP_TRY(tm.end(PH_H2D, s_h));
     HIP_TRY(hipEventRecord(staged, s_h));
     HIP_TRY(hipStreamWaitEvent(s_c, staged, 0));
     // the task's L and Delta rows, [H][T]
     HIP_TRY(tm.begin(PH_MERGE, s_c, tev));
-    for (const Segment& g : task.segments) {
-      HIP_TRY(hipMemcpy2DAsync(G.ls + g.local_offset, T * 4, lse_d + g.global_start, N * 4, g.length * 4, H,
-                               hipMemcpyDeviceToDevice, s_c));
-      HIP_TRY(hipMemcpy2DAsync(G.ds + g.local_offset, T * 4, delta_d + g.global_start, N * 4, g.length * 4, H,
-                               hipMemcpyDeviceToDevice, s_c));
-    }
+    if (!host_stats)
+      for (const Segment& g : task.segments) {
+        HIP_TRY(hipMemcpy2DAsync(G.ls + g.local_offset, T * 4, lse_d + g.global_start, N * 4, g.length * 4, H,
+                                 hipMemcpyDeviceToDevice, s_c));
+        HIP_TRY(hipMemcpy2DAsync(G.ds + g.local_offset, T * 4, delta_d + g.global_start, N * 4, g.length * 4, H,
+                                 hipMemcpyDeviceToDevice, s_c));
+      }
     if (L.trans) {
       PrepLaunch pr{};
       pr.dtype = p.dtype;

@@ -112,12 +112,13 @@ BwdLayout bwd_layout(const Plan& p) {
   return b;
 }
 
-BwdStreamLayout bwd_stream_layout(const Plan& p, bool acc_on_device, int stage_sets) {
+BwdStreamLayout bwd_stream_layout(const Plan& p, bool acc_on_device, int stage_sets, bool host_stats) {
   BwdStreamLayout b{};
   b.sets = stage_sets;
+  b.host_stats = host_stats;
   const int64_t h = p.heads, d = p.d, e = p.elem_bytes(), T = p.task_tokens(), U = p.unit;
   b.tnp = (T + 63) / 64 * 64;
-  b.lse = align_up(h * p.n * 4);
+  b.lse = host_stats ? 0 : align_up(h * p.n * 4);
   b.delta = b.lse;
   b.stage = align_up(T * h * d * e);
   b.trans = p.dtype == CQSA_BF16 ? align_up(h * d * b.tnp * 2) : 0;
@@ -567,18 +568,22 @@ cqsa_status build_fixed(int64_t n, int heads, int d, cqsa_dtype dtype, const std
   p.bwd_np = (n + 63) / 64 * 64;
   p.bwd_device_ws = bwd_layout(p).total;
   // streamed backward: the forward's mode order (device accumulators and two staging
-  // sets first), restricted by the same flags
+  // sets first), restricted by the same flags; L and Delta of every row resident on the
+  // device in every mode first, then kept in pinned host memory
   p.bwd_stream_fp = {false, 1, -1};
+  p.bwd_host_stats = false;
   const std::pair<bool, int> bwd_order[4] = {{true, 2}, {false, 2}, {true, 1}, {false, 1}};
-  for (const auto& m : bwd_order) {
-    if ((flags & CQSA_FLAG_HOST_ACC) && m.first) continue;
-    if ((flags & CQSA_FLAG_KV_SINGLE) && m.second != 1) continue;
-    const int64_t bytes = bwd_stream_layout(p, m.first, m.second).total;
-    if (fits_budget(p, bytes)) {
-      p.bwd_stream_fp = {m.first, m.second, bytes};
-      break;
+  for (int hs = 0; hs < 2 && p.bwd_stream_fp.bytes < 0; ++hs)
+    for (const auto& m : bwd_order) {
+      if ((flags & CQSA_FLAG_HOST_ACC) && m.first) continue;
+      if ((flags & CQSA_FLAG_KV_SINGLE) && m.second != 1) continue;
+      const int64_t bytes = bwd_stream_layout(p, m.first, m.second, hs == 1).total;
+      if (fits_budget(p, bytes)) {
+        p.bwd_stream_fp = {m.first, m.second, bytes};
+        p.bwd_host_stats = hs == 1;
+        break;
+      }
     }
-  }
   return choose_mode(p, why);
 }
 

@@ -85,6 +85,7 @@ struct Plan {
   int64_t bwd_np = 0;                   // row pitch (tokens) of the backward's transposed copies
   int64_t bwd_device_ws = 0;            // workspace bytes of the device-resident backward
   Footprint bwd_stream_fp{};            // streamed backward mode (bytes < 0: none fits the budget)
+  bool bwd_host_stats = false;          // streamed backward keeps L and Delta in pinned host memory
   int64_t host_acc_bytes = 0;
 
   // device copies of the descriptor tables, uploaded lazily per device
@@ -122,7 +123,7 @@ BwdLayout bwd_layout(const Plan& p);
 
 // Byte size of each piece of the streamed backward's workspace, in carve order.
 struct BwdStreamLayout {
-  int64_t lse, delta;     // [H][N] fp32 each, resident for the call
+  int64_t lse, delta;     // [H][N] fp32 each, resident for the call (0 with host_stats)
   int64_t stage;          // one staged tensor of a task (Q, K, V or dO): task_tokens rows
   int64_t trans;          // one transposed staged tensor [H][d][tnp] bf16 (0 for fp32)
   int64_t tstat;          // the task's L or Delta rows [H][task_tokens] fp32
@@ -132,9 +133,11 @@ struct BwdStreamLayout {
   int64_t acc;            // one device accumulator [N][H][d] fp32 (0 with the host one)
   int64_t tnp;            // row pitch of the transposed staging (tokens)
   int sets;               // task staging sets (2: the next task is staged during this one)
+  bool host_stats;        // L and Delta of every row stay in pinned host memory; each task's
+                          // rows are gathered from there with its staging
   int64_t total;
 };
-BwdStreamLayout bwd_stream_layout(const Plan& p, bool acc_on_device, int stage_sets);
+BwdStreamLayout bwd_stream_layout(const Plan& p, bool acc_on_device, int stage_sets, bool host_stats = false);
 
 // Byte size of each piece of the streamed path's workspace, in the order it is carved.
 struct StreamLayout {

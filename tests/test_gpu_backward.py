@@ -209,3 +209,70 @@ def test_streamed_backward_respects_budget():
     with cqsa.Plan(n, h, d, cqsa.CQSA_BF16, [4], budget_bytes=need_dev // 2) as p:
         ws = p.backward_workspace_size(cqsa.CQSA_RES_HOST_PINNED)
         assert ws <= need_dev // 2  # the accumulators moved to pinned host memory
+
+
+def _smallest_budget_with_backward(n, h, d, dtype, levels, flags):
+    """The smallest budget at which the plan builds and has a streamed backward layout
+    (bisection over plan creation; host-side only)."""
+    def ok(b):
+        try:
+            with cqsa.Plan(n, h, d, DT[dtype], levels, budget_bytes=b, flags=flags) as p:
+                return p.info["bwd_stream_mode"] != 0
+        except cqsa.CqsaError:
+            return False
+    lo, hi = 1, 1 << 20
+    while not ok(hi):
+        lo, hi = hi, hi * 2
+    while hi - lo > 1:
+        mid = (lo + hi) // 2
+        lo, hi = (lo, mid) if ok(mid) else (mid, hi)
+    return hi
+
+
+HOST_STATS_CASES = [  # levels, N, heads, head_dim, dtype, flags
+    ([3], 7 * 2048, 4, 128, "bf16", 0),
+    ([4], 13 * 100 + 9, 2, 64, "bf16", cqsa.CQSA_FLAG_PAD),
+    ([2, 2], 9 * 40, 2, 128, "bf16", cqsa.CQSA_FLAG_CAUSAL),
+    ([3], 7 * 64, 1, 64, "f32", cqsa.CQSA_FLAG_KV_SINGLE),
+]
+
+
+@pytest.mark.parametrize("case", HOST_STATS_CASES,
+                         ids=lambda c: f"l{'x'.join(map(str, c[0]))}-n{c[1]}-h{c[2]}-d{c[3]}-{c[4]}-f{c[5]}")
+def test_streamed_backward_with_host_statistics_equals_device_backward(case):
+    """Under the smallest budget that admits a streamed backward, L and Delta of every row
+    stay in pinned host memory (no layout with them on the device fits) and each task's
+    rows are gathered with its staging; the gradients equal the device-resident
+    backward's bit for bit, and the device memory stays within the budget."""
+    from gpu_util import init_device_runtime, pinned
+    torch = pytest.importorskip("torch")
+    levels, n, h, d, dtype, flags = case
+    budget = _smallest_budget_with_backward(n, h, d, dtype, levels, flags)
+    log(f"streamed backward with host statistics {case}: budget {budget}")
+    init_device_runtime()
+    q, k, v = gen_qkv(171 + n, n, h, d, dtype)
+    do = gen_tensor(171 + n, 3, n, h, d, dtype)
+    with cqsa.Plan(n, h, d, DT[dtype], levels, flags=flags) as p:
+        qd, kd, vd, dod = (to_device(x, dtype) for x in (q, k, v, do))
+        o = empty_device((n, h, d), dtype)
+        lse = torch.empty((h, n), device="cuda")
+        p.forward(qd, kd, vd, o, lse)
+        want = _run_backward(p, [qd, kd, vd, o, lse, dod], dtype, n, h, d)
+    hosts = []
+    for x in (q, k, v, to_numpy(o, dtype), do):
+        t, a = pinned((n, h, d), dtype)
+        a[...] = x
+        hosts.append(t)
+    lse_h = lse.cpu().pin_memory()
+    outs = [pinned((n, h, d), dtype) for _ in range(3)]
+    with cqsa.Plan(n, h, d, DT[dtype], levels, budget_bytes=budget, flags=flags) as p:
+        info = p.info
+        assert info["bwd_host_stats"] == 1, info
+        assert 0 < info["bwd_stream_workspace_bytes"] <= budget
+        st = p.backward(*hosts[:4], lse_h, hosts[4], *(t for t, _ in outs), residency=cqsa.CQSA_RES_HOST_PINNED,
+                        stats=True)
+        log(f"  modelled {st['peak_device_bytes']} observed {st['observed_peak_bytes']} of {budget}")
+        assert st["peak_device_bytes"] <= budget
+        got = [as_f64(a, dtype) for _, a in outs]
+    for name, g, w in zip(("dQ", "dK", "dV"), got, want):
+        assert np.array_equal(g, w), f"{name} differs from the device path"
