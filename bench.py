@@ -745,7 +745,14 @@ def main():
                         "host_pinned_bytes": e["host_pinned_bytes"], "bytes_h2d": e["bytes_h2d"],
                         "bytes_d2h": e["bytes_d2h"], "est_hours": round(e["t_est_s"] / 3600, 2),
                         "attn_hours": round(e["t_attn_s"] / 3600, 2), "h2d_hours": round(e["t_h2d_s"] / 3600, 2),
-                        "t_est_s": e["t_est_s"]}
+                        "t_est_s": e["t_est_s"],
+                        "backward_footprint": {
+                            "levels": e["bwd_levels"], "task_tokens": e["bwd_task_tokens"],
+                            "mode": cqsa.MODE_NAMES.get(e["bwd_stream_mode"]),
+                            "stats_in_host_memory": bool(e["bwd_host_stats"]),
+                            "stream_workspace_bytes": e["bwd_stream_workspace_bytes"],
+                            "note": "device workspace of the host-pinned backward under this budget, at the "
+                                    "fewest levels of l=3 where one of its layouts fits (plan-only)"}}
             dry.append(guarded(f"dry run at {budget // GiB} GiB", one))
             ok = "error" not in dry[-1]
             if ok and sbwd is not None and "error" not in sbwd and "error" not in stream_res:

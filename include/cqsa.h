@@ -180,6 +180,16 @@ typedef struct {
   double t_attn_s, t_merge_s, t_h2d_s, t_d2h_s;
   double t_est_s;               /* max(attn + merge (+ unoverlapped K/V loads), h2d, d2h) */
   int32_t materializable;       /* 1 if cqsa_plan_create builds this plan */
+  /* The host-pinned backward (cqsa_backward) under the same budget: the levels it needs
+   * (these levels, or with n_levels = 0 the innermost l repeated further until one of its
+   * layouts fits; 0 if none does), its staging mode, whether it keeps L and Delta in
+   * pinned host memory, its task size and its device workspace (-1 if none fits). */
+  int32_t bwd_levels;
+  int32_t bwd_stream_mode;
+  int32_t bwd_host_stats;
+  int32_t bwd_reserved;         /* 0 */
+  int64_t bwd_task_tokens;
+  int64_t bwd_stream_workspace_bytes;
 } cqsa_estimate;
 
 /* Library version string. */

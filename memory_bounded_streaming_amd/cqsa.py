@@ -91,6 +91,9 @@ class Estimate(ctypes.Structure):
         ("merge_bytes", ctypes.c_int64), ("useful_flop", ctypes.c_double),
         ("t_attn_s", ctypes.c_double), ("t_merge_s", ctypes.c_double), ("t_h2d_s", ctypes.c_double),
         ("t_d2h_s", ctypes.c_double), ("t_est_s", ctypes.c_double), ("materializable", ctypes.c_int32),
+        ("bwd_levels", ctypes.c_int32), ("bwd_stream_mode", ctypes.c_int32), ("bwd_host_stats", ctypes.c_int32),
+        ("bwd_reserved", ctypes.c_int32), ("bwd_task_tokens", ctypes.c_int64),
+        ("bwd_stream_workspace_bytes", ctypes.c_int64),
     ]
 
 

@@ -732,6 +732,44 @@ cqsa_status fit_mode(Plan& p, Footprint& fp, bool& fits, std::string& why) {
   return CQSA_OK;
 }
 
+// First streamed-backward layout in the order cqsa_plan_create tries them (L and Delta on
+// the device in every staging mode first, then in pinned host memory), by fit_mode's
+// budget test.
+cqsa_status fit_bwd(Plan& p, Footprint& fp, bool& host_stats, bool& fits, std::string& why) {
+  const std::pair<bool, int> order[4] = {{true, 2}, {false, 2}, {true, 1}, {false, 1}};
+  const bool buildable = materializable(p);
+  bool built = !p.tasks.empty();
+  fits = false;
+  for (int hs = 0; hs < 2; ++hs)
+    for (const auto& m : order) {
+      if ((p.flags & CQSA_FLAG_HOST_ACC) && m.first) continue;
+      if ((p.flags & CQSA_FLAG_KV_SINGLE) && m.second != 1) continue;
+      const int64_t bytes = bwd_stream_layout(p, m.first, m.second, hs == 1).total;
+      bool ok = p.budget == 0 || (bytes <= p.budget && (!buildable || bytes + descriptor_bound(p) <= p.budget));
+      if (!ok && buildable && bytes <= p.budget) {
+        if (!built) {
+          const cqsa_status st = build_tasks(p, why);
+          if (st != CQSA_OK) return st;
+          build_descriptors(p);
+          built = true;
+        }
+        ok = fits_budget(p, bytes);
+      }
+      if (ok) {
+        fp = {m.first, m.second, bytes};
+        host_stats = hs == 1;
+        fits = true;
+        return CQSA_OK;
+      }
+    }
+  return CQSA_OK;
+}
+
+int32_t mode_of(const Footprint& fp) {
+  return fp.acc_on_device ? (fp.kv_buffers == 2 ? CQSA_MODE_DEVICE_ACC_KV2 : CQSA_MODE_DEVICE_ACC_KV1)
+                          : (fp.kv_buffers == 2 ? CQSA_MODE_HOST_ACC_KV2 : CQSA_MODE_HOST_ACC_KV1);
+}
+
 }  // namespace
 
 cqsa_status estimate_plan(int64_t n, int heads, int d, cqsa_dtype dtype, const int32_t* ls, int n_levels,
@@ -834,6 +872,32 @@ cqsa_status estimate_plan(int64_t n, int heads, int d, cqsa_dtype dtype, const i
   const double kv_serial = fp.kv_buffers == 1 ? 2.0 * V * N * H * D * e / (r.h2d_gbs * 1e9) : 0.0;
   out.t_est_s = std::max({out.t_attn_s + out.t_merge_s + kv_serial, out.t_h2d_s, out.t_d2h_s});
   out.materializable = materializable(p) ? 1 : 0;
+
+  // the streamed backward: at these levels, and with auto levels divided further (the
+  // innermost l repeated) until one of its layouts fits
+  {
+    std::vector<int> levels = p.ls;
+    for (;;) {
+      Plan pb;
+      std::string w;
+      if (plan_shape(n, heads, d, dtype, levels, budget, flags, pb, w) != CQSA_OK) break;
+      Footprint bf{};
+      bool hs = false, fits = false;
+      if (fit_bwd(pb, bf, hs, fits, w) != CQSA_OK) break;
+      if (fits) {
+        out.bwd_levels = static_cast<int32_t>(pb.ls.size());
+        out.bwd_stream_mode = mode_of(bf);
+        out.bwd_host_stats = hs ? 1 : 0;
+        out.bwd_task_tokens = pb.task_tokens();
+        out.bwd_stream_workspace_bytes = bf.bytes;
+        break;
+      }
+      if (n_levels > 0 || static_cast<int>(levels.size()) >= CQSA_MAX_LEVELS) break;
+      if (levels.size() == 1 && levels[0] == 1) levels.clear();
+      levels.push_back(ls[0]);
+    }
+    if (out.bwd_levels == 0) out.bwd_stream_workspace_bytes = -1;
+  }
   return CQSA_OK;
 }
 

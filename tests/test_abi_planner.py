@@ -426,3 +426,66 @@ def test_estimate_and_plan_agree_at_budget_edges(n, h, d, levels, n_levels):
             made = _create_or_none(n, h, d, levels, budget, n_levels)
             if made != "unbuildable":
                 assert _estimate_or_none(n, h, d, levels, budget, n_levels) == made, budget
+
+
+@pytest.mark.parametrize("n,h,d,dt,levels,flags", [
+    (7 * 2048, 4, 128, cqsa.CQSA_BF16, [3], 0),
+    (13 * 100 + 9, 2, 64, cqsa.CQSA_BF16, [4], cqsa.CQSA_FLAG_PAD),
+    (9 * 40, 2, 128, cqsa.CQSA_BF16, [2, 2], cqsa.CQSA_FLAG_CAUSAL),
+    (7 * 64, 1, 64, cqsa.CQSA_F32, [3], cqsa.CQSA_FLAG_KV_SINGLE),
+])
+def test_estimate_backward_matches_built_plan(n, h, d, dt, levels, flags):
+    """The dry run's backward figures (mode, L and Delta placement, workspace) equal those of
+    the plan cqsa_plan_create builds, at budgets around the backward's layouts: none
+    fitting, host statistics only, statistics on the device, unlimited."""
+    rates = {"attn_tflops": 1.0, "merge_gbs": 1.0, "h2d_gbs": 1.0, "d2h_gbs": 1.0}
+    with cqsa.Plan(n, h, d, dt, levels, flags=flags) as free:
+        big = free.info["bwd_stream_workspace_bytes"]
+    budgets = [0, big + (16 << 20)]
+    # the smallest budget with a backward layout, and the bytes just below it
+    lo, hi = 1, big + (16 << 20)
+    while hi - lo > 1:
+        mid = (lo + hi) // 2
+        try:
+            with cqsa.Plan(n, h, d, dt, levels, budget_bytes=mid, flags=flags) as p:
+                fits = p.info["bwd_stream_mode"] != 0
+        except cqsa.CqsaError:
+            fits = False
+        lo, hi = (lo, mid) if fits else (mid, hi)
+    budgets += [hi, hi - 1, hi + 4 * h * n]
+    seen_host_stats = set()
+    for b in budgets:
+        try:
+            p = cqsa.Plan(n, h, d, dt, levels, budget_bytes=b, flags=flags)
+        except cqsa.CqsaError:
+            continue  # the forward itself does not fit
+        with p:
+            info = p.info
+        e = cqsa.cqsa_plan_estimate(n, h, d, dt, levels, budget_bytes=b, flags=flags, rates=rates)
+        if info["bwd_stream_mode"] == 0:
+            assert e["bwd_levels"] == 0 and e["bwd_stream_workspace_bytes"] == -1, b
+            continue
+        assert e["bwd_levels"] == len(levels), b
+        assert e["bwd_stream_mode"] == info["bwd_stream_mode"], b
+        assert e["bwd_host_stats"] == info["bwd_host_stats"], b
+        assert e["bwd_stream_workspace_bytes"] == info["bwd_stream_workspace_bytes"], b
+        assert e["bwd_task_tokens"] == info["task_tokens"], b
+        seen_host_stats.add(info["bwd_host_stats"])
+    assert seen_host_stats == {0, 1}
+
+
+def test_estimate_backward_of_a_billion_tokens_divides_further():
+    """A billion tokens under 2 GiB: the forward fits at 7 levels of l = 3, the backward (four
+    staged tensors and three transposed copies per task) only at 9, with L and Delta (8 GiB
+    at this N) in pinned host memory; with the 7 levels fixed it has no layout."""
+    rates = {"attn_tflops": 1.0, "merge_gbs": 1.0, "h2d_gbs": 1.0, "d2h_gbs": 1.0}
+    GiB = 1 << 30
+    e = cqsa.cqsa_plan_estimate(1 << 30, 1, 128, cqsa.CQSA_BF16, [3], n_levels=0, budget_bytes=2 * GiB,
+                                flags=cqsa.CQSA_FLAG_PAD, rates=rates)
+    assert e["levels"] == 7 and e["bwd_levels"] == 9
+    assert e["bwd_host_stats"] == 1 and 0 < e["bwd_stream_workspace_bytes"] <= 2 * GiB
+    unit = -(-(1 << 30) // 7 ** 9)  # tokens per unit of the padded 9-level grid
+    assert e["bwd_task_tokens"] == unit * 3 ** 9
+    fixed = cqsa.cqsa_plan_estimate(1 << 30, 1, 128, cqsa.CQSA_BF16, [3] * 7, budget_bytes=2 * GiB,
+                                    flags=cqsa.CQSA_FLAG_PAD, rates=rates)
+    assert fixed["bwd_levels"] == 0 and fixed["bwd_stream_workspace_bytes"] == -1
